@@ -1,0 +1,8 @@
+"""Seeded synthetic inputs shared by the CPU reference and the GPU path.
+
+Holds workload shapes and input generators only; no step of the attention
+method lives here.
+"""
+
+from .configs import BY_INDEX, WORKLOADS, Workload  # noqa: F401
+from .fourier import generate, generate_head, kmeans_uniforms, token_coords  # noqa: F401

@@ -1,0 +1,86 @@
+"""Pins of the reference k-means and cluster order (no GPU)."""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle import kmeans as ok
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _seed_cases():
+    with open(os.path.join(GOLDEN, "kmeanspp_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                pts, us, seeds = (s.strip() for s in line.split("|"))
+                yield (np.array([[float(p)] for p in pts.split()]),
+                       np.array([float(u) for u in us.split()]),
+                       [int(s) for s in seeds.split()])
+
+
+@pytest.mark.parametrize("x,u,seeds", list(_seed_cases()))
+def test_seeding_golden(x, u, seeds):
+    assert ok.kmeanspp_seeds(x, len(u), u).tolist() == seeds
+
+
+def test_seeding_frequencies_follow_d2():
+    # Over a fine grid of uniforms, each point is chosen as the second seed in
+    # proportion to its squared distance from the first.
+    rng = np.random.default_rng(20)
+    x = rng.normal(size=(9, 3))
+    d2 = ((x - x[4]) ** 2).sum(1)
+    m = 20000
+    counts = np.zeros(9)
+    for j in range(m):
+        s = ok.kmeanspp_seeds(x, 2, np.array([4.5 / 9, (j + 0.5) / m]))
+        counts[s[1]] += 1
+    np.testing.assert_allclose(counts / m, d2 / d2.sum(), atol=2.0 / m)
+
+
+def test_separated_clusters_recovered():
+    rng = np.random.default_rng(21)
+    centers = np.array([[0.0, 0.0], [100.0, 0.0], [0.0, 100.0], [100.0, 100.0]])
+    lab = rng.integers(0, 4, 400)
+    x = centers[lab] + rng.normal(scale=1.0, size=(400, 2))
+    cent, a, sizes, seeds, hist = ok.kmeans(x, 4, 5, rng.random(4))
+    # same partition up to relabelling
+    mapping = {}
+    for i in range(400):
+        mapping.setdefault(lab[i], a[i])
+        assert mapping[lab[i]] == a[i]
+    assert len(set(mapping.values())) == 4
+    for c in range(4):
+        np.testing.assert_allclose(cent[c], x[a == c].mean(0), rtol=1e-12)
+
+
+def test_single_cluster_is_global_mean_and_invariants():
+    rng = np.random.default_rng(22)
+    x = rng.normal(size=(300, 8)) * rng.uniform(0.5, 3, size=8)
+    cent, a, sizes, seeds, hist = ok.kmeans(x, 1, 3, np.array([0.3]))
+    np.testing.assert_allclose(cent[0], x.mean(0), rtol=1e-12)
+    cent, a, sizes, seeds, hist = ok.kmeans(x, 12, 10, rng.random(12))
+    assert all(h2 <= h1 * (1 + 1e-12) for h1, h2 in zip(hist, hist[1:]))
+    assert sizes.sum() == 300 and (np.bincount(a, minlength=12) == sizes).all()
+    for c in range(12):
+        if sizes[c]:
+            np.testing.assert_allclose(cent[c], x[a == c].mean(0), rtol=1e-12)
+    # at a fixed point (enough rounds) every point is nearest to its own centroid
+    cent, a, sizes, seeds, hist = ok.kmeans(x, 12, 200, rng.random(12))
+    assert ok.assign(x, cent).tolist() == a.tolist()
+    d = ok.sq_dists(x, cent)
+    assert (d[np.arange(300), a] <= d.min(1) * (1 + 1e-12) + 1e-12).all()
+
+
+def test_cluster_order_is_stable_sort():
+    rng = np.random.default_rng(23)
+    a = rng.integers(0, 7, 100)
+    perm, start, size = ok.cluster_order(a, 9, N=104)
+    assert sorted(perm.tolist()) == list(range(104))
+    assert (perm[100:] == np.arange(100, 104)).all()
+    assert (size == np.bincount(a, minlength=9)).all()
+    for c in range(9):
+        seg = perm[start[c]:start[c] + size[c]]
+        assert (a[seg] == c).all() and (np.diff(seg) > 0).all()
