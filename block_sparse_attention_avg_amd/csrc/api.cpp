@@ -1,0 +1,309 @@
+// C ABI of libbsa: argument validation, workspace carving and kernel launch
+// (declarations and the contract of every entry point are in include/bsa.h).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSA_OK;
+  return fail(BSA_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Validates a descriptor and converts it for the kernels.
+int make_blocks(const bsa_blocks* in, int block, int n_valid, const char* what, bsa::Blocks& out) {
+  out.block = block;
+  out.n_valid = n_valid;
+  if (in == nullptr) {
+    if (block != 64) return fail(BSA_EUNSUPPORTED, "%s: uniform blocks must have 64 tokens (got %d)", what, block);
+    out.start = nullptr;
+    out.len = nullptr;
+    out.nblocks = (n_valid + block - 1) / block;
+    out.per_head = 0;
+    return BSA_OK;
+  }
+  if (in->nblocks < 0) return fail(BSA_EINVAL, "%s: nblocks < 0", what);
+  if (in->nblocks > 0 && (in->start == nullptr || in->len == nullptr))
+    return fail(BSA_EINVAL, "%s: null start/len array", what);
+  out.start = in->start;
+  out.len = in->len;
+  out.nblocks = in->nblocks;
+  out.per_head = in->per_head ? 1 : 0;
+  // A non-null descriptor with no blocks is valid (nothing to do).
+  if (out.start == nullptr) {
+    // keep the device view distinguishable from uniform blocks
+    static const int32_t dummy = 0;
+    out.start = &dummy;
+    out.len = &dummy;
+  }
+  return BSA_OK;
+}
+
+int check_shape(int B, int H, int N, int d, int n_valid) {
+  if (B <= 0 || H <= 0 || N <= 0) return fail(BSA_EINVAL, "B, H and N must be positive (B=%d H=%d N=%d)", B, H, N);
+  if ((long long)B * H > 65535) return fail(BSA_EUNSUPPORTED, "B*H must be <= 65535");
+  if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+  if (n_valid <= 0 || n_valid > N) return fail(BSA_EINVAL, "n_valid must be in [1, N] (got %d, N=%d)", n_valid, N);
+  return BSA_OK;
+}
+
+int make_window(const bsa_window* w, int nqb, int nkb, bsa::Window& out) {
+  memset(&out, 0, sizeof out);
+  if (w == nullptr) return BSA_OK;
+  if (w->nt <= 0 || w->ny <= 0 || w->nx <= 0) return fail(BSA_EINVAL, "window grid must be positive");
+  if (w->rt < 0 || w->ry < 0 || w->rx < 0) return fail(BSA_EINVAL, "window radii must be >= 0");
+  const long long cells = (long long)w->nt * w->ny * w->nx;
+  if (cells != nqb || cells != nkb)
+    return fail(BSA_EINVAL, "window grid %dx%dx%d does not match %d query / %d key blocks", w->nt, w->ny, w->nx, nqb, nkb);
+  out.nt = w->nt; out.ny = w->ny; out.nx = w->nx;
+  out.rt = w->rt; out.ry = w->ry; out.rx = w->rx;
+  out.enabled = 1;
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+const char* bsa_strerror(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_EINVAL: return "invalid argument";
+    case BSA_EUNSUPPORTED: return "unsupported argument";
+    case BSA_ENOSPC: return "workspace or capacity too small";
+    case BSA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error_message(void) { return g_msg; }
+
+int bsa_pool_blocks(const void* x, int B, int H, int N, int d, int n_valid, int block,
+                    const bsa_blocks* blocks, float* out, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (!x || !out) return fail(BSA_EINVAL, "pool: null pointer");
+  if (!aligned16(x)) return fail(BSA_EINVAL, "pool: x must be 16-byte aligned");
+  bsa::Blocks b;
+  if (int e = make_blocks(blocks, block, n_valid, "pool", b)) return e;
+  return hip_status(bsa::launch_pool(static_cast<const uint16_t*>(x), B * H, N, d, b, out, stream), "pool");
+}
+
+int bsa_select_blocks(const float* qbar, const float* kbar, int B, int H, int nqb, int nkb, int d,
+                      const int32_t* q_sizes, const int32_t* k_sizes, float thr, float scale,
+                      const bsa_window* win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
+                      hipStream_t stream) {
+  g_msg[0] = 0;
+  if (B <= 0 || H <= 0) return fail(BSA_EINVAL, "select: B and H must be positive");
+  if ((long long)B * H > 65535) return fail(BSA_EUNSUPPORTED, "B*H must be <= 65535");
+  if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "select: d must be 64 or 128");
+  if (nqb < 0 || nkb <= 0) return fail(BSA_EINVAL, "select: need nqb >= 0 and nkb >= 1");
+  if (nkb > 8192) return fail(BSA_EUNSUPPORTED, "select: at most 8192 key blocks (got %d)", nkb);
+  if (!qbar || !kbar || !kv_count || !kv_index) return fail(BSA_EINVAL, "select: null pointer");
+  if (!aligned16(qbar) || !aligned16(kbar)) return fail(BSA_EINVAL, "select: pooled inputs must be 16-byte aligned");
+  if (!(thr >= 0.f && thr <= 1.f)) return fail(BSA_EINVAL, "select: thr must be in [0, 1]");
+  if (kv_stride < nkb) return fail(BSA_ENOSPC, "select: kv_stride %d < nkb %d", kv_stride, nkb);
+  bsa::Window w;
+  if (int e = make_window(win, nqb, nkb, w)) return e;
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return hip_status(bsa::launch_select(qbar, kbar, B * H, nqb, nkb, d, q_sizes, k_sizes, thr, sc, w,
+                                       kv_count, kv_index, kv_stride, stream),
+                    "select");
+}
+
+size_t bsa_build_block_mask_workspace(int B, int H, int nqb, int nkb, int d) {
+  if (B <= 0 || H <= 0 || nqb < 0 || nkb < 0 || d <= 0) return 0;
+  return round256(sizeof(float) * (size_t)B * H * nqb * d) + round256(sizeof(float) * (size_t)B * H * nkb * d);
+}
+
+int bsa_build_block_mask(const void* q, const void* k, int B, int H, int N, int d, int n_valid, int block,
+                         const bsa_blocks* qb, const bsa_blocks* kb, float thr, const bsa_window* win,
+                         int32_t* kv_count, int32_t* kv_index, int kv_stride, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (!q || !k || !kv_count || !kv_index) return fail(BSA_EINVAL, "build_block_mask: null pointer");
+  if (!aligned16(q) || !aligned16(k)) return fail(BSA_EINVAL, "build_block_mask: q, k must be 16-byte aligned");
+  bsa::Blocks bq, bk;
+  if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
+  if (int e = make_blocks(kb, block, n_valid, "key blocks", bk)) return e;
+  if (bk.nblocks <= 0) return fail(BSA_EINVAL, "build_block_mask: no key blocks");
+  if (bk.nblocks > 8192) return fail(BSA_EUNSUPPORTED, "build_block_mask: at most 8192 key blocks");
+  if (!(thr >= 0.f && thr <= 1.f)) return fail(BSA_EINVAL, "build_block_mask: thr must be in [0, 1]");
+  if (kv_stride < bk.nblocks) return fail(BSA_ENOSPC, "build_block_mask: kv_stride %d < nkb %d", kv_stride, bk.nblocks);
+  bsa::Window w;
+  if (int e = make_window(win, bq.nblocks, bk.nblocks, w)) return e;
+  const size_t need = bsa_build_block_mask_workspace(B, H, bq.nblocks, bk.nblocks, d);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(BSA_ENOSPC, "build_block_mask: workspace %zu bytes < %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(BSA_EINVAL, "build_block_mask: workspace must be 16-byte aligned");
+  float* qbar = static_cast<float*>(ws);
+  float* kbar = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         round256(sizeof(float) * (size_t)B * H * bq.nblocks * d));
+  const int BH = B * H;
+  if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(q), BH, N, d, bq, qbar, stream), "pool q")) return e;
+  if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(k), BH, N, d, bk, kbar, stream), "pool k")) return e;
+  const float sc = 1.f / sqrtf((float)d);
+  return hip_status(bsa::launch_select(qbar, kbar, BH, bq.nblocks, bk.nblocks, d, nullptr, nullptr, thr, sc, w,
+                                       kv_count, kv_index, kv_stride, stream),
+                    "select");
+}
+
+int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes, const float* ck, const int32_t* k_sizes,
+                            int B, int H, int Cq, int Ck, int d, float top_p, float scale, int32_t* kv_count,
+                            int32_t* kv_index, int kv_stride, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (!q_sizes || !k_sizes) return fail(BSA_EINVAL, "centroid mask: cluster sizes are required");
+  if (!(top_p >= 0.f && top_p <= 1.f)) return fail(BSA_EINVAL, "centroid mask: top_p must be in [0, 1]");
+  return bsa_select_blocks(cq, ck, B, H, Cq, Ck, d, q_sizes, k_sizes, 1.f - top_p, scale, nullptr, kv_count,
+                           kv_index, kv_stride, stream);
+}
+
+size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb, const bsa_blocks* qb) {
+  if (qb == nullptr || B <= 0 || H <= 0 || nqb < 0) return 0;
+  return round256(sizeof(int32_t) * (size_t)B * H * (nqb + 1));
+}
+
+int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                              int n_valid, int block, const bsa_blocks* qb, const bsa_blocks* kb,
+                              const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (!q || !k || !v || !o || !kv_count || !kv_index) return fail(BSA_EINVAL, "attn_fwd: null pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_EINVAL, "attn_fwd: q, k, v, o must be 16-byte aligned");
+  bsa::Blocks bq, bk;
+  if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
+  if (int e = make_blocks(kb, block, n_valid, "key blocks", bk)) return e;
+  if (kv_stride < 0 || (bk.nblocks > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_fwd: bad kv_stride");
+  const size_t need = bsa_block_sparse_attn_fwd_workspace(B, H, bq.nblocks, qb);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(BSA_ENOSPC, "attn_fwd: workspace %zu bytes < %zu", ws_bytes, need);
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return hip_status(bsa::launch_attn_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), B * H, N, d,
+                                         n_valid, bq, bk, kv_count, kv_index, kv_stride, sc,
+                                         static_cast<int32_t*>(ws), stream),
+                    "attn_fwd");
+}
+
+static int permute_common(const void* x, void* y, const int32_t* perm, int B, int H, int N, int d,
+                          int per_head, bool inverse, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (B <= 0 || H <= 0 || N <= 0) return fail(BSA_EINVAL, "permute: B, H, N must be positive");
+  if ((long long)B * H > 65535) return fail(BSA_EUNSUPPORTED, "B*H must be <= 65535");
+  if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "permute: d must be 64 or 128");
+  if (!x || !y || !perm) return fail(BSA_EINVAL, "permute: null pointer");
+  if (x == y) return fail(BSA_EINVAL, "permute: x and y must not overlap");
+  if (!aligned16(x) || !aligned16(y)) return fail(BSA_EINVAL, "permute: x, y must be 16-byte aligned");
+  return hip_status(bsa::launch_permute(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), perm, B * H, N,
+                                        d, per_head, inverse, stream),
+                    "permute");
+}
+
+int bsa_permute_tokens(const void* x, void* y, const int32_t* perm, int B, int H, int N, int d, int perm_per_head,
+                       hipStream_t stream) {
+  return permute_common(x, y, perm, B, H, N, d, perm_per_head, false, stream);
+}
+
+int bsa_unpermute_tokens(const void* x, void* y, const int32_t* perm, int B, int H, int N, int d, int perm_per_head,
+                         hipStream_t stream) {
+  return permute_common(x, y, perm, B, H, N, d, perm_per_head, true, stream);
+}
+
+int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm, int32_t* blk_start, int32_t* blk_len,
+                      int32_t* blk_coords, int max_blocks, int* nblocks) {
+  g_msg[0] = 0;
+  if (T <= 0 || Hl <= 0 || Wl <= 0 || P <= 0) return fail(BSA_EINVAL, "fractal_order: sizes must be positive");
+  const long long n = (long long)T * Hl * Wl;
+  if (n > 0x7fffffffLL || N < n) return fail(BSA_EINVAL, "fractal_order: N must be >= T*Hl*Wl");
+  if (!perm || !blk_start || !blk_len || !nblocks) return fail(BSA_EINVAL, "fractal_order: null pointer");
+  const int npy = (Hl + P - 1) / P, npx = (Wl + P - 1) / P;
+  const long long nb = (long long)T * npy * npx;
+  *nblocks = (int)nb;
+  if (nb > max_blocks) return fail(BSA_ENOSPC, "fractal_order: %lld blocks > max_blocks %d", nb, max_blocks);
+  int pos = 0, b = 0;
+  for (int t = 0; t < T; ++t)
+    for (int py = 0; py < npy; ++py)
+      for (int px = 0; px < npx; ++px) {
+        blk_start[b] = pos;
+        const int y1 = py * P + P < Hl ? py * P + P : Hl;
+        const int x1 = px * P + P < Wl ? px * P + P : Wl;
+        for (int y = py * P; y < y1; ++y)
+          for (int x = px * P; x < x1; ++x) perm[pos++] = (t * Hl + y) * Wl + x;
+        blk_len[b] = pos - blk_start[b];
+        if (blk_coords) {
+          blk_coords[3 * b + 0] = t;
+          blk_coords[3 * b + 1] = py;
+          blk_coords[3 * b + 2] = px;
+        }
+        ++b;
+      }
+  for (int i = (int)n; i < N; ++i) perm[i] = i;
+  return BSA_OK;
+}
+
+size_t bsa_kmeans_workspace(int B, int H, int N, int C, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || C <= 0) return 0;
+  return bsa::kmeans_ws_bytes(B * H, N, C, d);
+}
+
+int bsa_kmeans(const void* x, int B, int H, int N, int d, int n_valid, int C, int iters, const float* uniforms,
+               float* centroids, int32_t* assign, int32_t* sizes, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (C < 1 || C > 1024) return fail(BSA_EUNSUPPORTED, "kmeans: C must be in [1, 1024] (got %d)", C);
+  if (C > n_valid) return fail(BSA_EINVAL, "kmeans: C=%d exceeds n_valid=%d", C, n_valid);
+  if (iters < 0) return fail(BSA_EINVAL, "kmeans: iters must be >= 0");
+  if (!x || !uniforms || !centroids || !assign || !sizes) return fail(BSA_EINVAL, "kmeans: null pointer");
+  if (!aligned16(x)) return fail(BSA_EINVAL, "kmeans: x must be 16-byte aligned");
+  const size_t need = bsa_kmeans_workspace(B, H, N, C, d);
+  if (ws == nullptr || ws_bytes < need) return fail(BSA_ENOSPC, "kmeans: workspace %zu bytes < %zu", ws_bytes, need);
+  return hip_status(bsa::launch_kmeans(static_cast<const uint16_t*>(x), B * H, N, d, n_valid, C, iters, uniforms,
+                                       centroids, assign, sizes, ws, stream),
+                    "kmeans");
+}
+
+size_t bsa_cluster_order_workspace(int B, int H, int N, int C) {
+  if (B <= 0 || H <= 0 || N <= 0 || C <= 0) return 0;
+  return bsa::cluster_order_ws_bytes(B * H, N, C);
+}
+
+int bsa_cluster_order(const int32_t* assign, int B, int H, int N, int n_valid, int C, int32_t* perm, int32_t* start,
+                      int32_t* len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (B <= 0 || H <= 0 || N <= 0) return fail(BSA_EINVAL, "cluster_order: B, H, N must be positive");
+  if ((long long)B * H > 65535) return fail(BSA_EUNSUPPORTED, "B*H must be <= 65535");
+  if (n_valid <= 0 || n_valid > N) return fail(BSA_EINVAL, "cluster_order: n_valid must be in [1, N]");
+  if (C < 1 || C > 1024) return fail(BSA_EUNSUPPORTED, "cluster_order: C must be in [1, 1024]");
+  if (!assign || !perm || !start || !len) return fail(BSA_EINVAL, "cluster_order: null pointer");
+  const size_t need = bsa_cluster_order_workspace(B, H, N, C);
+  if (ws == nullptr || ws_bytes < need) return fail(BSA_ENOSPC, "cluster_order: workspace %zu bytes < %zu", ws_bytes, need);
+  return hip_status(bsa::launch_cluster_order(assign, B * H, N, n_valid, C, perm, start, len, ws, stream),
+                    "cluster_order");
+}
+
+}  // extern "C"

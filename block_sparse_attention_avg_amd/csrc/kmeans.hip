@@ -1,0 +1,365 @@
+// k-means of query / key vectors and the cluster-contiguous order (Sparse
+// VideoGen2 summary, Metodologia A, "Clustering" and "Permutazione").
+//
+// Seeding is k-means++ (each new centre drawn with probability proportional
+// to D^2, by inverse CDF over token order with a caller-supplied uniform).
+// One launch per seeding round: every workgroup owns 256 tokens, keeps their
+// D^2 in a double buffer and publishes its partial sum; at the start of the
+// next round every workgroup re-derives the drawn index from those partials
+// in the same fixed order (no atomics, no grid barrier), the first workgroup
+// records the centre, and all update D^2 against it.
+//
+// Lloyd rounds: assignment computes exact fp32 squared distances (centroids
+// are wave-uniform, so they are read through scalar loads); the update is a
+// stable counting sort by cluster (per-chunk histograms, a per-head scan, an
+// in-chunk stable rank) followed by a per-cluster mean over the cluster's
+// tokens in ascending token order. Every reduction has a fixed order, so
+// results are bit-reproducible. The same sort produces the
+// cluster-contiguous permutation.
+#include "common.h"
+
+#include <math.h>
+
+namespace bsa {
+
+namespace {
+constexpr int kChunk = 256;   // tokens per workgroup
+
+struct KmWs {
+  float* d2;        // [2][BH][N]
+  float* part;      // [2][BH][nchunk]
+  int32_t* off;     // [BH][nchunk][C]
+  int32_t* order;   // [BH][N]   tokens sorted by cluster
+  int32_t* start;   // [BH][C]
+  int32_t* size;    // [BH][C]
+};
+
+__device__ __forceinline__ float load_x(const uint16_t* row, int dd) {
+  return __uint_as_float((uint32_t)row[dd] << 16);
+}
+
+// Fixed-order block sum over 256 threads (result valid in thread 0).
+__device__ float block_sum_256(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace
+
+// D^2 of the tokens of this chunk to centre `cidx`; min with the previous D^2
+// unless first. Writes the chunk's partial sum.
+template <int D>
+__device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_prev,
+                           float* d2_next, float* part_next, bool first, float* red) {
+  const int i = blockIdx.x * kChunk + threadIdx.x;
+  float v = 0.f;
+  if (i < n) {
+    const uint16_t* xr = xh + (size_t)i * D;
+    const uint16_t* cr = xh + (size_t)cidx * D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int dd = 0; dd < D; ++dd) {
+      const float t = load_x(xr, dd) - load_x(cr, dd);
+      acc = fmaf(t, t, acc);
+    }
+    v = first ? acc : fminf(acc, d2_prev[i]);
+    d2_next[i] = v;
+  }
+  const float s = block_sum_256(v, red);
+  if (threadIdx.x == 0) part_next[blockIdx.x] = s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restrict__ x, int N,
+                                                        int n, int C, int r,
+                                                        const float* __restrict__ uni,
+                                                        float* __restrict__ cent, KmWs ws,
+                                                        int BH) {
+  __shared__ float red[256];
+  __shared__ int chosen;
+  const int bh = blockIdx.y;
+  const int nchunk = gridDim.x;
+  const uint16_t* xh = x + (size_t)bh * N * D;
+  const float u = uni[(size_t)bh * C + r];
+  const int prev = (r + 1) & 1, next = r & 1;
+  const float* d2p = ws.d2 + ((size_t)prev * BH + bh) * N;
+  float* d2n = ws.d2 + ((size_t)next * BH + bh) * N;
+  const float* pp = ws.part + ((size_t)prev * BH + bh) * nchunk;
+  float* pn = ws.part + ((size_t)next * BH + bh) * nchunk;
+
+  if (threadIdx.x == 0) {
+    int idx;
+    if (r == 0) {
+      idx = (int)floor((double)u * (double)n);
+    } else {
+      float total = 0.f;
+      for (int c = 0; c < nchunk; ++c) total += pp[c];
+      if (!(total > 0.f)) {
+        idx = (int)floor((double)u * (double)n);
+      } else {
+        const float target = u * total;
+        float run = 0.f;
+        int ch = 0;
+        for (; ch < nchunk - 1; ++ch) {
+          if (run + pp[ch] > target) break;
+          run += pp[ch];
+        }
+        // Rounding can leave the in-chunk running sum just short of the
+        // target; then take the chunk's last token with positive D^2.
+        idx = -1;
+        int last_pos = min(n, (ch + 1) * kChunk) - 1;
+        for (int i = ch * kChunk; i < min(n, (ch + 1) * kChunk); ++i) {
+          const float v = d2p[i];
+          if (v > 0.f) last_pos = i;
+          run += v;
+          if (run > target) { idx = i; break; }
+        }
+        if (idx < 0) idx = last_pos;
+      }
+    }
+    chosen = min(max(idx, 0), n - 1);
+  }
+  __syncthreads();
+  const int cidx = chosen;
+  if (blockIdx.x == 0 && threadIdx.x < D)
+    cent[((size_t)bh * C + r) * D + threadIdx.x] = load_x(xh + (size_t)cidx * D, threadIdx.x);
+  kpp_update<D>(xh, n, cidx, d2p, d2n, pn, r == 0, red);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict__ x, int N, int n,
+                                                     int C, const float* __restrict__ cent,
+                                                     int32_t* __restrict__ assign) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * kChunk + threadIdx.x;
+  if (i >= N) return;
+  if (i >= n) {
+    assign[(size_t)bh * N + i] = -1;
+    return;
+  }
+  const uint16_t* xr = x + ((size_t)bh * N + i) * D;
+  float xv[D];
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(xr + 8 * c8);
+    xv[8 * c8 + 0] = bf16_lo(w.x); xv[8 * c8 + 1] = bf16_hi(w.x);
+    xv[8 * c8 + 2] = bf16_lo(w.y); xv[8 * c8 + 3] = bf16_hi(w.y);
+    xv[8 * c8 + 4] = bf16_lo(w.z); xv[8 * c8 + 5] = bf16_hi(w.z);
+    xv[8 * c8 + 6] = bf16_lo(w.w); xv[8 * c8 + 7] = bf16_hi(w.w);
+  }
+  const float* cb = cent + (size_t)bh * C * D;
+  float best = INFINITY;
+  int bi = 0;
+  for (int c = 0; c < C; ++c) {
+    const float* cr = cb + (size_t)c * D;
+    float acc = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) {
+      const float t = xv[dd] - cr[dd];
+      acc = fmaf(t, t, acc);
+    }
+    if (acc < best) {
+      best = acc;
+      bi = c;
+    }
+  }
+  assign[(size_t)bh * N + i] = bi;
+}
+
+// Per-chunk cluster histogram: cnt[bh][chunk][c].
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ assign, int N, int n,
+                                                   int C, int32_t* __restrict__ cnt) {
+  extern __shared__ int h[];
+  const int bh = blockIdx.y, ch = blockIdx.x, nchunk = gridDim.x;
+  for (int c = threadIdx.x; c < C; c += 256) h[c] = 0;
+  __syncthreads();
+  const int i = ch * kChunk + threadIdx.x;
+  if (i < n) atomicAdd(&h[assign[(size_t)bh * N + i]], 1);
+  __syncthreads();
+  int32_t* out = cnt + ((size_t)bh * nchunk + ch) * C;
+  for (int c = threadIdx.x; c < C; c += 256) out[c] = h[c];
+}
+
+// Per head: running offsets over chunks for every cluster, cluster sizes and
+// starts; off[bh][chunk][c] becomes the first output slot of chunk's members.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ off, int nchunk, int C,
+                                                    int32_t* __restrict__ start,
+                                                    int32_t* __restrict__ size) {
+  __shared__ int sz[1024];
+  const int bh = blockIdx.x;
+  const int c = threadIdx.x;
+  int32_t* o = off + (size_t)bh * nchunk * C;
+  int run = 0;
+  if (c < C) {
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const int t = o[(size_t)ch * C + c];
+      o[(size_t)ch * C + c] = run;
+      run += t;
+    }
+  }
+  sz[c] = c < C ? run : 0;
+  __syncthreads();
+  if (c == 0) {
+    int acc = 0;
+    for (int j = 0; j < C; ++j) {
+      const int v = sz[j];
+      sz[j] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  if (c < C) {
+    const int st = sz[c];
+    start[(size_t)bh * C + c] = st;
+    size[(size_t)bh * C + c] = run;
+    for (int ch = 0; ch < nchunk; ++ch) o[(size_t)ch * C + c] += st;
+  }
+}
+
+// Stable scatter: token i goes to off[chunk][a_i] + (# earlier tokens of the
+// chunk in the same cluster). Rows >= n map to themselves.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ assign, int N,
+                                                      int n, int C,
+                                                      const int32_t* __restrict__ off,
+                                                      int32_t* __restrict__ order) {
+  __shared__ int ids[kChunk];
+  const int bh = blockIdx.y, ch = blockIdx.x, nchunk = gridDim.x;
+  const int i = ch * kChunk + threadIdx.x;
+  ids[threadIdx.x] = i < n ? assign[(size_t)bh * N + i] : -1;
+  __syncthreads();
+  if (i < n) {
+    const int a = ids[threadIdx.x];
+    int rank = 0;
+    for (int j = 0; j < (int)threadIdx.x; ++j) rank += ids[j] == a;
+    order[(size_t)bh * N + off[((size_t)bh * nchunk + ch) * C + a] + rank] = i;
+  }
+  // padding rows (and the tail beyond the last chunk) map to themselves
+  for (int t = n + ch * kChunk + threadIdx.x; t < N; t += kChunk * nchunk)
+    order[(size_t)bh * N + t] = t;
+}
+
+// Cluster means: token p of a cluster (ascending token order) goes to group
+// p % G, groups are combined in a fixed order.
+template <int D>
+__global__ __launch_bounds__(256) void mean_kernel(const uint16_t* __restrict__ x, int N, int C,
+                                                   const int32_t* __restrict__ order,
+                                                   const int32_t* __restrict__ start,
+                                                   const int32_t* __restrict__ size,
+                                                   float* __restrict__ cent) {
+  constexpr int G = 256 / D;   // token groups
+  __shared__ float red[G][D];
+  const int bh = blockIdx.y, c = blockIdx.x;
+  const int sz = size[(size_t)bh * C + c];
+  if (sz == 0) return;   // empty cluster keeps its centroid
+  const int st = start[(size_t)bh * C + c];
+  const int dd = threadIdx.x % D, g = threadIdx.x / D;
+  const int32_t* ord = order + (size_t)bh * N + st;
+  const uint16_t* xh = x + (size_t)bh * N * D;
+  float acc = 0.f;
+  int p = g;
+  for (; p + 3 * G < sz; p += 4 * G) {
+    const int i0 = ord[p], i1 = ord[p + G], i2 = ord[p + 2 * G], i3 = ord[p + 3 * G];
+    const float a0 = load_x(xh + (size_t)i0 * D, dd), a1 = load_x(xh + (size_t)i1 * D, dd);
+    const float a2 = load_x(xh + (size_t)i2 * D, dd), a3 = load_x(xh + (size_t)i3 * D, dd);
+    acc += a0; acc += a1; acc += a2; acc += a3;
+  }
+  for (; p < sz; p += G) acc += load_x(xh + (size_t)ord[p] * D, dd);
+  red[g][dd] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float s = red[0][dd];
+    for (int k = 1; k < G; ++k) s += red[k][dd];
+    cent[((size_t)bh * C + c) * D + dd] = s / (float)sz;
+  }
+}
+
+static KmWs carve(void* ws, int BH, int N, int C) {
+  const int nchunk = (N + kChunk - 1) / kChunk;
+  char* p = reinterpret_cast<char*>(ws);
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return r;
+  };
+  KmWs w;
+  w.d2 = reinterpret_cast<float*>(take(sizeof(float) * 2 * (size_t)BH * N));
+  w.part = reinterpret_cast<float*>(take(sizeof(float) * 2 * (size_t)BH * nchunk));
+  w.off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nchunk * C));
+  w.order = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * N));
+  w.start = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * C));
+  w.size = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * C));
+  return w;
+}
+
+size_t kmeans_ws_bytes(int BH, int N, int C, int /*d*/) {
+  const int nchunk = (N + kChunk - 1) / kChunk;
+  auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return r(sizeof(float) * 2 * (size_t)BH * N) + r(sizeof(float) * 2 * (size_t)BH * nchunk) +
+         r(sizeof(int32_t) * (size_t)BH * nchunk * C) + r(sizeof(int32_t) * (size_t)BH * N) +
+         2 * r(sizeof(int32_t) * (size_t)BH * C);
+}
+
+size_t cluster_order_ws_bytes(int BH, int N, int C) {
+  const int nchunk = (N + kChunk - 1) / kChunk;
+  return ((sizeof(int32_t) * (size_t)BH * nchunk * C) + 255) & ~(size_t)255;
+}
+
+static hipError_t sort_by_cluster(const int32_t* assign, int BH, int N, int n, int C, int32_t* off,
+                                  int32_t* order, int32_t* start, int32_t* size, hipStream_t s) {
+  const int nchunk = (N + kChunk - 1) / kChunk;
+  hist_kernel<<<dim3(nchunk, BH), 256, C * sizeof(int), s>>>(assign, N, n, C, off);
+  scan_kernel<<<BH, 1024, 0, s>>>(off, nchunk, C, start, size);
+  scatter_kernel<<<dim3(nchunk, BH), 256, 0, s>>>(assign, N, n, C, off, order);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t kmeans_t(const uint16_t* x, int BH, int N, int n, int C, int iters,
+                           const float* uni, float* cent, int32_t* assign, int32_t* sizes,
+                           void* wsp, hipStream_t s) {
+  KmWs ws = carve(wsp, BH, N, C);
+  const int nchunk_n = (n + kChunk - 1) / kChunk;
+  for (int r = 0; r < C; ++r)
+    kpp_round_kernel<D><<<dim3(nchunk_n, BH), 256, 0, s>>>(x, N, n, C, r, uni, cent, ws, BH);
+  const int nchunk = (N + kChunk - 1) / kChunk;
+  for (int it = 0; it < iters; ++it) {
+    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign);
+    hipError_t e = sort_by_cluster(assign, BH, N, n, C, ws.off, ws.order, ws.start, ws.size, s);
+    if (e != hipSuccess) return e;
+    mean_kernel<D><<<dim3(C, BH), 256, 0, s>>>(x, N, C, ws.order, ws.start, ws.size, cent);
+  }
+  if (iters == 0) {
+    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign);
+    hipError_t e = sort_by_cluster(assign, BH, N, n, C, ws.off, ws.order, ws.start, ws.size, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipMemcpyAsync(sizes, ws.size, sizeof(int32_t) * (size_t)BH * C,
+                                hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,
+                         const float* uniforms, float* centroids, int32_t* assign,
+                         int32_t* sizes, void* ws, hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  if (d == 128) return kmeans_t<128>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, ws, s);
+  return kmeans_t<64>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, ws, s);
+}
+
+hipError_t launch_cluster_order(const int32_t* assign, int BH, int N, int n_valid, int C,
+                                int32_t* perm, int32_t* start, int32_t* len, void* ws,
+                                hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  return sort_by_cluster(assign, BH, N, n_valid, C, reinterpret_cast<int32_t*>(ws), perm, start,
+                         len, s);
+}
+
+}  // namespace bsa

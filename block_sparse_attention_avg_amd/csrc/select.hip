@@ -1,0 +1,232 @@
+// Reduced attention + CDF selection of key blocks (NABLA summary, Metodologia
+// section 2, "Attenzione Ridotta" and "CDF Thresholding"; section 3 for the
+// window union; Sparse VideoGen2 summary, Metodologia B for the
+// size-weighted centroid variant).
+//
+// One workgroup (4 waves) owns R consecutive rows of one head's reduced map.
+//
+// Phase 1 -- scores. s[r][J] = scale * qbar_r . kbar_J (+ log n_J) for all
+// key blocks, on fp32 MFMA 16x16x4 (A = 16 pooled query rows, B = 16 pooled
+// key rows, the 4-wide k slot of the MFMA split over the four 16-lane groups
+// so each lane streams a contiguous quarter of the channel vector). The R x nkb
+// fp32 score rows stay in LDS; the reduced map never touches HBM.
+//
+// Phase 2 -- selection, one wave per row. p_J = exp(s_J - max) in fp32.
+// Masses are converted to 2^-40 fixed point (m_J = floor(p_J * 2^40)) so that
+// every sum is exact and order-independent. The cut is found by an MSB-first
+// radix select over the 43-bit key (bits(p_J) << 13 | (8191 - J)): keys order
+// blocks lightest first with ties broken toward the higher index. Each 8-bit
+// digit pass builds a 256-bin mass histogram of the keys still matching the
+// prefix (LDS 64-bit integer atomics, order-independent), scans it and
+// descends into the first bin where the cumulative mass reaches
+// T = ceil(thr * Z). After 6 passes k* is the smallest key whose inclusive
+// cumulative mass reaches T: exactly the blocks with key < k* are dropped.
+// The kept ids are written in ascending order with wave ballots; the window
+// test, if any, is OR'd in at that point.
+#include "common.h"
+
+#include <math.h>
+
+namespace bsa {
+
+namespace {
+constexpr int kIdxBits = 13;          // supports nkb <= 8192
+constexpr int kKeyBits = 30 + kIdxBits;
+constexpr int kDigit = 8;
+constexpr int kPasses = (kKeyBits + kDigit - 1) / kDigit;   // 6
+constexpr int kBins = 1 << kDigit;
+}  // namespace
+
+template <int D, int R>
+__global__ __launch_bounds__(256) void select_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
+    const int32_t* __restrict__ q_sizes, const int32_t* __restrict__ k_sizes, float thr,
+    float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+    int kv_stride) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
+  unsigned long long* hist =
+      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [4][kBins]
+
+  constexpr int KQ = D / 4;
+  const int bh = blockIdx.y;
+  const int row0 = blockIdx.x * R;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, i16 = lane & 15;
+
+  // ---------------- phase 1: score rows into LDS
+  float a[KQ];
+  {
+    const int row = row0 + i16;
+    const bool ok = i16 < R && row < nqb;
+    const float4* src =
+        reinterpret_cast<const float4*>(qbar + ((size_t)bh * nqb + (ok ? row : 0)) * D + g * KQ);
+#pragma unroll
+    for (int s = 0; s < KQ / 4; ++s) {
+      const float4 v = ok ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+      a[4 * s + 0] = v.x; a[4 * s + 1] = v.y; a[4 * s + 2] = v.z; a[4 * s + 3] = v.w;
+    }
+  }
+  const float* kbh = kbar + (size_t)bh * nkb * D;
+  const int ntiles = (nkb + 15) >> 4;
+  for (int t = wave; t < ntiles; t += 4) {
+    const int key = t * 16 + i16;
+    const bool kok = key < nkb;
+    const float4* src = reinterpret_cast<const float4*>(kbh + (size_t)(kok ? key : 0) * D + g * KQ);
+    float b[KQ];
+#pragma unroll
+    for (int s = 0; s < KQ / 4; ++s) {
+      const float4 v = kok ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+      b[4 * s + 0] = v.x; b[4 * s + 1] = v.y; b[4 * s + 2] = v.z; b[4 * s + 3] = v.w;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    if (kok) {
+      float bias = 0.f;
+      bool excluded = false;
+      if (k_sizes) {
+        const int n = k_sizes[(size_t)bh * nkb + key];
+        excluded = n <= 0;
+        bias = excluded ? 0.f : logf((float)n);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 4 * g + v;   // MFMA output row held in register v
+        if (rr < R) sc[rr * nkb_pad + key] = excluded ? -INFINITY : acc[v] * scale + bias;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- phase 2: per-row CDF selection
+  unsigned long long* h = hist + wave * kBins;
+  for (int rr = wave; rr < R; rr += 4) {
+    const int row = row0 + rr;
+    if (row >= nqb) break;
+    const size_t orow = (size_t)bh * nqb + row;
+    int32_t* out = kv_index + orow * kv_stride;
+    if (q_sizes && q_sizes[orow] <= 0) {
+      if (lane == 0) kv_count[orow] = 0;
+      continue;
+    }
+    float* sr = sc + rr * nkb_pad;
+    float mx = -INFINITY;
+    for (int j = lane; j < nkb; j += kWave) mx = fmaxf(mx, sr[j]);
+    mx = wave_max(mx);
+    unsigned long long z = 0;
+    for (int j = lane; j < nkb; j += kWave) {
+      const float p = expf(sr[j] - mx);     // in [0, 1]; exp(-inf) = 0
+      sr[j] = p;
+      z += (unsigned long long)(p * 0x1p40f);
+    }
+    z = wave_sum_u64(z);
+    const double tt = ceil((double)thr * (double)z);
+    const unsigned long long tint = tt >= (double)z ? z : (unsigned long long)tt;
+    wave_lds_sync();
+
+    unsigned long long prefix = 0, below = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int shift = kDigit * (kPasses - 1 - pass);
+#pragma unroll
+      for (int e = 0; e < kBins / kWave; ++e) h[lane * (kBins / kWave) + e] = 0;
+      wave_lds_sync();
+      for (int j = lane; j < nkb; j += kWave) {
+        const float p = sr[j];
+        const unsigned long long key =
+            ((unsigned long long)__float_as_uint(p) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
+        if ((key >> (shift + kDigit)) == prefix) {
+          const unsigned long long m = (unsigned long long)(p * 0x1p40f);
+          if (m) atomicAdd(&h[(key >> shift) & (kBins - 1)], m);
+        }
+      }
+      wave_lds_sync();
+      // lane owns bins [4*lane, 4*lane+4)
+      unsigned long long hv[kBins / kWave];
+      unsigned long long loc = 0;
+#pragma unroll
+      for (int e = 0; e < kBins / kWave; ++e) {
+        hv[e] = h[lane * (kBins / kWave) + e];
+        loc += hv[e];
+      }
+      const unsigned long long incl = wave_incl_scan_u64(loc, lane);
+      unsigned long long run = incl - loc;
+      const unsigned long long need = tint > below ? tint - below : 0ull;
+      int cand = 1 << 30;
+      unsigned long long before = 0;
+#pragma unroll
+      for (int e = kBins / kWave - 1; e >= 0; --e) {
+        // cumulative mass through bin (4*lane + e)
+        unsigned long long through = run;
+#pragma unroll
+        for (int f = 0; f <= e; ++f) through += hv[f];
+        if (through >= need) {
+          cand = lane * (kBins / kWave) + e;
+          before = through - hv[e];
+        }
+      }
+      int b = wave_min_i32(cand);
+      if (b >= kBins) b = kBins - 1;   // unreachable for finite inputs
+      before = __shfl(before, b / (kBins / kWave));
+      below += before;
+      prefix = (prefix << kDigit) | (unsigned)b;
+      wave_lds_sync();
+    }
+    const unsigned long long kstar = prefix;
+
+    int base = 0;
+    for (int j0 = 0; j0 < nkb; j0 += kWave) {
+      const int j = j0 + lane;
+      bool keep = false;
+      if (j < nkb) {
+        const unsigned long long key =
+            ((unsigned long long)__float_as_uint(sr[j]) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
+        keep = key >= kstar;
+        if (k_sizes && k_sizes[(size_t)bh * nkb + j] <= 0) keep = false;
+        if (win.enabled && win.inside(row, j)) keep = true;
+      }
+      const unsigned long long bal = __ballot(keep);
+      if (keep) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+      base += __popcll(bal);
+    }
+    if (lane == 0) kv_count[orow] = base;
+  }
+}
+
+template <int D, int R>
+static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
+                                  const int32_t* q_sizes, const int32_t* k_sizes, float thr,
+                                  float scale, const Window& win, int32_t* kv_count,
+                                  int32_t* kv_index, int kv_stride, hipStream_t s) {
+  const int nkb_pad = (nkb + 3) & ~3;
+  const size_t lds = (size_t)R * nkb_pad * sizeof(float) + 4 * kBins * sizeof(unsigned long long);
+  auto kern = select_kernel<D, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((nqb + R - 1) / R, BH);
+  kern<<<grid, 256, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, q_sizes, k_sizes, thr, scale, win,
+                              kv_count, kv_index, kv_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, int nkb, int d,
+                         const int32_t* q_sizes, const int32_t* k_sizes, float thr, float scale,
+                         const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
+                         hipStream_t s) {
+  if (BH == 0 || nqb == 0) return hipSuccess;
+#define BSA_SEL(DD, RR) \
+  launch_select_t<DD, RR>(qbar, kbar, BH, nqb, nkb, q_sizes, k_sizes, thr, scale, win, kv_count, kv_index, kv_stride, s)
+  if (d == 128) {
+    if (nkb <= 2048) return BSA_SEL(128, 16);
+    if (nkb <= 4096) return BSA_SEL(128, 8);
+    return BSA_SEL(128, 4);
+  }
+  if (nkb <= 2048) return BSA_SEL(64, 16);
+  if (nkb <= 4096) return BSA_SEL(64, 8);
+  return BSA_SEL(64, 4);
+#undef BSA_SEL
+}
+
+}  // namespace bsa

@@ -1,0 +1,302 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) content-adaptive block-sparse
+ * attention library (libbsa.so).
+ *
+ * The library implements, as hand-written HIP kernels, the two-stage hot path
+ * described for video diffusion transformers:
+ *
+ *   1. a dynamic block mask (NABLA summary "Riepilogo Tecnico: NABLA -
+ *      Neighborhood Adaptive Block-Level Attention ...", Metodologia section
+ *      2): Q and K are average-pooled into blocks, a reduced attention map is
+ *      computed over the pooled blocks, each row is binarised by its CDF
+ *      against 1 - thr, optionally OR'd with a static sliding-tile window
+ *      (section 3, M = M_nabla OR M_STA);
+ *   2. block-sparse attention that computes only the kept query x key tiles
+ *      (section 2, "Espansione"), with an online softmax.
+ *
+ * plus the token reorder helpers and the semantic-clustering variant of the
+ * Sparse VideoGen2 summary (Metodologia A-C): fractal flattening (NABLA
+ * section 1), k-means of Q and K, cluster-contiguous permutation and its
+ * inverse, centroid top-p selection and attention over variable-size blocks.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensors are dense and row-major. Q, K, V, O are bf16 (raw 16-bit
+ *    storage) with shape [B, H, N, d]: batch, head, token, channel.
+ *  - Device pointers are HIP device memory owned by the caller. The library
+ *    never allocates or frees memory and keeps no pointer after return.
+ *  - All device work is enqueued asynchronously on the caller's stream
+ *    `stream` (0 = the null stream); the library never synchronises. Buffers
+ *    must stay valid until the stream has passed the work.
+ *  - The first `n_valid` tokens of each sequence are real; rows
+ *    n_valid..N-1 are padding. Padding is never read as a key or value, and
+ *    output padding rows are written as zero.
+ *  - Return value: BSA_OK (0) or an error code. Argument checks are done on
+ *    the host before any launch; on error nothing is enqueued and
+ *    bsa_last_error_message() describes the problem. BSA_EHIP reports a HIP
+ *    launch/runtime error. No C++ exception crosses the ABI.
+ *  - The library is thread-safe; its only mutable global state is a
+ *    thread-local error message.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+enum bsa_status {
+  BSA_OK = 0,
+  BSA_EINVAL = 1,        /* invalid argument (null pointer, bad size, ...)   */
+  BSA_EUNSUPPORTED = 2,  /* valid but unsupported (head dim, block size ...) */
+  BSA_ENOSPC = 3,        /* workspace or output capacity too small           */
+  BSA_EHIP = 4           /* HIP launch or runtime error                      */
+};
+
+/*
+ * Block descriptors: block i covers tokens [start[i], start[i] + len[i]) of
+ * the (possibly reordered) token axis. `start` and `len` are int32 device
+ * arrays of shape [nblocks], or [B*H*nblocks] (row-major over b, h, i) when
+ * `per_head` is non-zero. Blocks may have any length >= 0; blocks of one
+ * side must not overlap. Passing NULL for a bsa_blocks* means uniform
+ * blocks: block i = [block*i, min(block*(i+1), n_valid)),
+ * nblocks = ceil(n_valid / block).
+ */
+typedef struct bsa_blocks {
+  int32_t nblocks;
+  int32_t per_head;
+  const int32_t* start;
+  const int32_t* len;
+} bsa_blocks;
+
+/*
+ * Static sliding-tile window (NABLA summary, Metodologia section 3). Blocks
+ * lie on an nt x ny x nx grid with block index (t*ny + y)*nx + x; key block
+ * J is inside query block I's window when |t_I - t_J| <= rt,
+ * |y_I - y_J| <= ry and |x_I - x_J| <= rx (clipped at the grid edges, no
+ * wrap-around). nt*ny*nx must equal the number of query and of key blocks.
+ */
+typedef struct bsa_window {
+  int32_t nt, ny, nx;
+  int32_t rt, ry, rx;
+} bsa_window;
+
+int bsa_abi_version(void);
+const char* bsa_strerror(int status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* bsa_last_error_message(void);
+
+/* ------------------------------------------------------------------------
+ * Mask stage
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Block mean pooling (NABLA summary, Metodologia section 2,
+ * "Sottocampionamento"): out[b,h,i,:] = mean of x[b,h,t,:] over the tokens t
+ * of block i, accumulated in fp32 in a fixed order (bit-reproducible).
+ *   x    bf16 [B,H,N,d] (device), d in {64, 128}
+ *   out  fp32 [B,H,nblocks,d] (device)
+ *   blocks  NULL = uniform blocks of `block` tokens (block = 64)
+ * Blocks of length 0 produce zeros.
+ */
+int bsa_pool_blocks(const void* x, int B, int H, int N, int d, int n_valid,
+                    int block, const bsa_blocks* blocks, float* out,
+                    hipStream_t stream);
+
+/*
+ * Reduced attention and CDF selection (NABLA summary, Metodologia section 2,
+ * "Attenzione Ridotta" and "CDF Thresholding"; section 3 window union;
+ * Sparse VideoGen2 summary, Metodologia B, for the size-weighted variant).
+ *
+ * For every row (b,h,I): s_J = scale * qbar_I . kbar_J in fp32 (+ log n_J
+ * when k_sizes is given), p_J = exp(s_J - max s), and the kept set is
+ * computed exactly on the fp32 values p_J: order the blocks lightest first
+ * (equal p: higher J lighter), drop J exactly when the inclusive cumulative
+ * mass up to J is below thr times the row total. Masses are summed in
+ * 2^-40 fixed point, so the result does not depend on summation order and
+ * is bit-reproducible. thr = 0 keeps every block; the heaviest block is
+ * always kept. The window, if any, is OR'd in afterwards.
+ *
+ *   qbar     fp32 [B,H,nqb,d], kbar fp32 [B,H,nkb,d] (device), d in {64,128}
+ *   q_sizes  int32 [B,H,nqb] or NULL: rows with size 0 keep nothing
+ *   k_sizes  int32 [B,H,nkb] or NULL: NULL = equal weights; otherwise key J
+ *            is weighted by k_sizes[J] (log-weight added to s_J) and never
+ *            kept when its size is 0
+ *   thr      in [0, 1]; scale > 0, or <= 0 for 1/sqrt(d)
+ *   win      NULL or a window on the block grid (nqb == nkb required)
+ *   kv_count int32 [B,H,nqb] (device): number of kept key blocks per row
+ *   kv_index int32 [B,H,nqb,kv_stride] (device): the first kv_count entries
+ *            of each row are the kept key-block ids in ascending order; the
+ *            rest of the row is left untouched. kv_stride >= nkb.
+ * Supports nkb <= 8192.
+ */
+int bsa_select_blocks(const float* qbar, const float* kbar, int B, int H,
+                      int nqb, int nkb, int d, const int32_t* q_sizes,
+                      const int32_t* k_sizes, float thr, float scale,
+                      const bsa_window* win, int32_t* kv_count,
+                      int32_t* kv_index, int kv_stride, hipStream_t stream);
+
+/* Workspace bytes needed by bsa_build_block_mask (pooled Q and K). */
+size_t bsa_build_block_mask_workspace(int B, int H, int nqb, int nkb, int d);
+
+/*
+ * Whole mask stage: bsa_pool_blocks on q and k, then bsa_select_blocks with
+ * equal weights. q, k bf16 [B,H,N,d]; qb/kb block descriptors (NULL =
+ * uniform `block`-token blocks); ws of at least
+ * bsa_build_block_mask_workspace(...) bytes (device, 256-byte aligned).
+ * Outputs as in bsa_select_blocks.
+ */
+int bsa_build_block_mask(const void* q, const void* k, int B, int H, int N,
+                         int d, int n_valid, int block, const bsa_blocks* qb,
+                         const bsa_blocks* kb, float thr, const bsa_window* win,
+                         int32_t* kv_count, int32_t* kv_index, int kv_stride,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Centroid top-p mask (Sparse VideoGen2 summary, Metodologia B): weights
+ * w_ab proportional to k_sizes[b] * exp(scale * cq_a . ck_b); key clusters
+ * are kept heaviest first until the mass reaches top_p (the CDF rule above
+ * with thr = 1 - top_p). Empty key clusters are never kept; empty query
+ * clusters keep nothing.
+ *   cq fp32 [B,H,Cq,d], ck fp32 [B,H,Ck,d], q_sizes int32 [B,H,Cq],
+ *   k_sizes int32 [B,H,Ck] (device); top_p in [0,1].
+ */
+int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes,
+                            const float* ck, const int32_t* k_sizes, int B,
+                            int H, int Cq, int Ck, int d, float top_p,
+                            float scale, int32_t* kv_count, int32_t* kv_index,
+                            int kv_stride, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Block-sparse attention
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes needed by bsa_block_sparse_attn_fwd (0 for uniform
+ * 64-token query blocks). */
+size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
+                                           const bsa_blocks* qb);
+
+/*
+ * Block-sparse attention forward (NABLA summary, Metodologia section 2,
+ * "Espansione"; Sparse VideoGen2 summary, Metodologia C.2 for variable-size
+ * blocks). For every query block I and query token i in it:
+ *   o_i = sum_j softmax_j(scale * q_i . k_j) v_j
+ * over exactly the key tokens j of the key blocks listed in
+ * kv_index[b,h,I,0..kv_count-1]; every other score is -inf. QK^T and PV run
+ * on bf16 MFMA with fp32 accumulation; the softmax is an fp32 online
+ * softmax. A query block with no kept key block gets zero rows.
+ *
+ *   q, k, v   bf16 [B,H,N,d] (device), d in {64, 128}
+ *   o         bf16 [B,H,N,d] (device); every row of every query block is
+ *             written, rows n_valid..N-1 are zeroed, other rows untouched
+ *   qb, kb    block descriptors (NULL = uniform `block`-token blocks,
+ *             block = 64). Query blocks of any length are tiled by 64 rows;
+ *             key blocks of any length are gathered into 64-key tiles.
+ *   kv_count, kv_index, kv_stride   as produced by the mask stage; ids must
+ *             be valid key blocks (the caller's contract)
+ *   scale     > 0, or <= 0 for 1/sqrt(d)
+ *   ws        workspace of bsa_block_sparse_attn_fwd_workspace(...) bytes
+ */
+int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                              void* o, int B, int H, int N, int d, int n_valid,
+                              int block, const bsa_blocks* qb,
+                              const bsa_blocks* kb, const int32_t* kv_count,
+                              const int32_t* kv_index, int kv_stride,
+                              float scale, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Token reorder helpers
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Gather rows: y[b,h,i,:] = x[b,h,perm[i],:] (NABLA summary, Metodologia
+ * section 1; Sparse VideoGen2 summary, Metodologia A "Permutazione").
+ *   x, y  bf16 [B,H,N,d] (device, must not overlap); d a multiple of 8
+ *   perm  int32 [N], or [B,H,N] when perm_per_head != 0 (device); must be a
+ *         permutation of 0..N-1 (the caller's contract)
+ */
+int bsa_permute_tokens(const void* x, void* y, const int32_t* perm, int B,
+                       int H, int N, int d, int perm_per_head,
+                       hipStream_t stream);
+
+/*
+ * Inverse of bsa_permute_tokens, a scatter: y[b,h,perm[i],:] = x[b,h,i,:]
+ * (Sparse VideoGen2 summary, Metodologia A "Equivalenza Matematica": the
+ * output is permuted back to the original token order).
+ */
+int bsa_unpermute_tokens(const void* x, void* y, const int32_t* perm, int B,
+                         int H, int N, int d, int perm_per_head,
+                         hipStream_t stream);
+
+/*
+ * Fractal flattening order (NABLA summary, Metodologia section 1), a pure
+ * host function on caller-owned HOST arrays. The T x Hl x Wl latent video
+ * (raster order, t slowest) is reordered so that every P x P spatial patch
+ * of a frame is contiguous (patches row-major on a ceil(Hl/P) x ceil(Wl/P)
+ * grid, tokens row-major inside a patch, time order kept; edge patches are
+ * smaller, no tokens are inserted).
+ *   perm        int32 [N] out: perm[new] = old raster index; positions
+ *               >= T*Hl*Wl map to themselves (N >= T*Hl*Wl)
+ *   blk_start, blk_len  int32 [max_blocks] out: one block per patch
+ *   blk_coords  int32 [max_blocks*3] out or NULL: (t, patch_row, patch_col)
+ *   nblocks     out: T * ceil(Hl/P) * ceil(Wl/P); BSA_ENOSPC if larger than
+ *               max_blocks
+ */
+int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm,
+                      int32_t* blk_start, int32_t* blk_len,
+                      int32_t* blk_coords, int max_blocks, int* nblocks);
+
+/* ------------------------------------------------------------------------
+ * Semantic clustering (Sparse VideoGen2 summary, Metodologia A)
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes needed by bsa_kmeans. */
+size_t bsa_kmeans_workspace(int B, int H, int N, int C, int d);
+
+/*
+ * k-means of the first n_valid token vectors of every (b,h): k-means++
+ * seeding (D^2 inverse-CDF draws over token order driven by the given
+ * uniforms), then `iters` rounds of (assign to the nearest centroid by
+ * squared Euclidean distance, ties to the lower index; update to the cluster
+ * means, an empty cluster keeps its centroid). The outputs are the last
+ * assignment and its cluster means. Deterministic (fixed reduction orders).
+ *   x         bf16 [B,H,N,d] (device), d in {64, 128}
+ *   uniforms  fp32 [B,H,C] in [0,1) (device)
+ *   centroids fp32 [B,H,C,d] out; assign int32 [B,H,N] out (-1 for padding
+ *             rows); sizes int32 [B,H,C] out
+ *   1 <= C <= 1024, C <= n_valid
+ */
+int bsa_kmeans(const void* x, int B, int H, int N, int d, int n_valid, int C,
+               int iters, const float* uniforms, float* centroids,
+               int32_t* assign, int32_t* sizes, void* ws, size_t ws_bytes,
+               hipStream_t stream);
+
+/* Workspace bytes needed by bsa_cluster_order. */
+size_t bsa_cluster_order_workspace(int B, int H, int N, int C);
+
+/*
+ * Cluster-contiguous token order (Sparse VideoGen2 summary, Metodologia A,
+ * "Permutazione"): a stable counting sort of the first n_valid tokens of
+ * every (b,h) by cluster id.
+ *   assign  int32 [B,H,N] (device), ids in [0, C) for the first n_valid rows
+ *   perm    int32 [B,H,N] out: perm[new] = old; rows >= n_valid map to
+ *           themselves
+ *   start, len  int32 [B,H,C] out: cluster c occupies
+ *           [start[c], start[c] + len[c]) of the new order
+ */
+int bsa_cluster_order(const int32_t* assign, int B, int H, int N, int n_valid,
+                      int C, int32_t* perm, int32_t* start, int32_t* len,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -1,0 +1,52 @@
+"""Mask comparison with a tolerance band around the CDF threshold.
+
+A GPU bit may differ from the reference only where the reference's own
+numbers leave the decision open: the block's cumulative mass lies within
+``delta`` of thr, counting blocks whose probabilities are within relative
+``rho`` of it as possibly lighter or heavier (ties under rounding).
+"""
+
+import numpy as np
+
+
+def sure_bits(p: np.ndarray, thr: float, rho: float = 1e-4, delta: float = 1e-4):
+    """(sure_keep, sure_drop) bool arrays for one row of probabilities."""
+    p = np.asarray(p, np.float64)
+    p = p / p.sum()
+    s = np.sort(p)
+    c = np.concatenate([[0.0], np.cumsum(s)])
+    lo = np.searchsorted(s, p * (1 - rho), side="left")     # count of p_K < p_J(1-rho)
+    hi = np.searchsorted(s, p * (1 + rho), side="right")    # count of p_K <= p_J(1+rho)
+    L = c[lo]
+    U = c[hi]
+    sure_drop = U < thr - delta
+    sure_keep = (L + p) >= thr + delta
+    return sure_keep, sure_drop
+
+
+def mask_mismatches(P: np.ndarray, thr: float, gpu_keep: np.ndarray, window=None,
+                    rho: float = 1e-4, delta: float = 1e-4, valid_cols=None):
+    """Number of sure bits where gpu_keep disagrees, over all rows of P."""
+    bad = 0
+    for i in range(P.shape[0]):
+        cols = slice(None) if valid_cols is None else valid_cols
+        k, d = sure_bits(P[i][cols], thr, rho, delta)
+        g = gpu_keep[i][cols]
+        if window is not None:
+            w = window[i][cols]
+            k = k | w
+            d = d & ~w
+        bad += int(((k & ~g) | (d & g)).sum())
+    return bad
+
+
+def keep_from_lists(kv_count: np.ndarray, kv_index: np.ndarray, nkb: int) -> np.ndarray:
+    """bool [rows, nkb] from (count, ascending index) lists; checks the lists."""
+    rows = kv_count.shape[0]
+    keep = np.zeros((rows, nkb), dtype=bool)
+    for r in range(rows):
+        ids = kv_index[r, :kv_count[r]]
+        assert (ids >= 0).all() and (ids < nkb).all(), r
+        assert (np.diff(ids) > 0).all(), r
+        keep[r, ids] = True
+    return keep

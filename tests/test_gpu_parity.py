@@ -1,0 +1,279 @@
+"""GPU parity of the HIP path against the CPU reference (needs an MI355X).
+
+Every case feeds the same seeded bf16 tensors to the library (through the C
+ABI binding) and to the float64 reference, then compares:
+  * pooled means: |gpu - ref| <= 1e-5 * mean|x| of the block (fp32 summation
+    error bound for 64 terms is ~4e-6 of that);
+  * masks: every bit the reference decides with margin (band.py: cumulative
+    mass farther than 1e-4 from thr, near-ties within relative 1e-4 counted
+    both ways) must match exactly, window bits must be set, lists ascending;
+  * outputs: with the GPU's own mask, max-abs <= 2e-2 and mean-abs <= 2e-3
+    against the float64 reference over valid rows;
+  * integer work (permutations, counts): bit-exact.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gen import BY_INDEX, WORKLOADS, generate
+from oracle import attention as oa
+from oracle import layout as ol
+from oracle import mask as om
+from tests.band import keep_from_lists, mask_mismatches
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=3)
+def _inputs(key):
+    w = WORKLOADS[key]
+    q, k, v = generate(w)
+    return w, q, k, v
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_out(o_gpu, o_ref, rows, what):
+    d = np.abs(o_gpu[rows] - o_ref[rows])
+    say(f"  {what}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+    assert np.isfinite(o_gpu[rows]).all(), what
+    assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, what
+
+
+def _rows_of(st, ln, blocks):
+    return np.concatenate([np.arange(st[b], st[b] + ln[b]) for b in blocks])
+
+
+# --------------------------------------------------------------------- pooling
+
+@pytest.mark.parametrize("key", ["tiny", "wan480"])
+def test_pool_parity(gpu_lib, key):
+    bsa = gpu_lib
+    w, q, k, v = _inputs(key)
+    say(f"pool parity {key}")
+    qd = q.cuda()
+    g = bsa.pool_blocks(qd, n_valid=w.n_valid).cpu().numpy()
+    st, ln = ol.raster_blocks(w.n_valid)
+    for h in range(min(w.H, 3)):
+        x = _np(q[0, h])
+        ref = om.pool(x, st, ln)
+        scale = np.stack([np.abs(x[s:s + n]).mean(0) for s, n in zip(st, ln)])
+        assert (np.abs(g[0, h] - ref) <= 1e-5 * scale + 1e-30).all(), h
+
+
+def test_pool_descriptors_and_empty_blocks(gpu_lib):
+    bsa = gpu_lib
+    rng = np.random.default_rng(0)
+    x = torch.from_numpy(rng.normal(size=(1, 2, 300, 64)).astype(np.float32)).to(torch.bfloat16)
+    st = np.array([0, 10, 10, 77, 200], np.int32)
+    ln = np.array([10, 0, 67, 100, 99], np.int32)
+    blocks = bsa.Blocks(torch.from_numpy(st).cuda(), torch.from_numpy(ln).cuda())
+    g = bsa.pool_blocks(x.cuda(), blocks=blocks).cpu().numpy()
+    for h in range(2):
+        ref = np.zeros((5, 64))
+        for i in range(5):
+            if ln[i]:
+                ref[i] = om.pool(_np(x[0, h]), st[i:i + 1], ln[i:i + 1])[0]
+        np.testing.assert_allclose(g[0, h], ref, rtol=1e-5, atol=1e-6)
+        assert (g[0, h, 1] == 0).all()
+
+
+# ------------------------------------------------------------------ mask stage
+
+def _mask_case(bsa, w, q, k, heads, thr=None):
+    thr = w.thr if thr is None else thr
+    cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), thr, n_valid=w.n_valid)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    st, ln = ol.raster_blocks(w.n_valid)
+    nb = len(st)
+    total_bad = 0
+    for h in heads:
+        keep = keep_from_lists(cnt[0, h], idx[0, h], nb)
+        ref_keep, P = om.block_mask(_np(q[0, h]), _np(k[0, h]), st, ln, st, ln, thr)
+        bad = mask_mismatches(P, thr, keep)
+        diff = int((keep != ref_keep).sum())
+        say(f"  head {h}: kept {keep.sum()} / {keep.size}, differing bits {diff}, sure-bit mismatches {bad}")
+        total_bad += bad
+    return cnt, idx, total_bad
+
+
+@pytest.mark.parametrize("key", ["tiny", "wan480"])
+def test_mask_parity(gpu_lib, key):
+    w, q, k, v = _inputs(key)
+    say(f"mask parity {key}")
+    heads = range(w.H) if key == "tiny" else [0, 3, 7, 11]
+    _, _, bad = _mask_case(gpu_lib, w, q, k, heads)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("thr", [0.0, 1.0, 0.5])
+def test_mask_special_thresholds(gpu_lib, thr):
+    w, q, k, v = _inputs("wan480")
+    say(f"mask thr={thr}")
+    cnt, idx, bad = _mask_case(gpu_lib, w, q, k, [1], thr=thr)
+    assert bad == 0
+    if thr == 0.0:
+        assert (cnt == w.nb).all()
+    if thr == 1.0:
+        assert (cnt >= 1).all() and (cnt <= 2).all()
+
+
+def test_mask_ragged_and_d64(gpu_lib):
+    bsa = gpu_lib
+    rng = np.random.default_rng(1)
+    for (H, N, nv, d, g) in [(3, 640, 600, 64, 4.0), (2, 1280, 1250, 128, 3.0)]:
+        say(f"mask ragged H={H} N={N} n_valid={nv} d={d}")
+        x = rng.normal(size=(2, 1, H, N, d)).astype(np.float32) * g
+        x[:, :, :, nv:] = 0
+        q = torch.from_numpy(x[0]).to(torch.bfloat16)
+        k = torch.from_numpy(x[1]).to(torch.bfloat16)
+        cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), 0.15, n_valid=nv)
+        cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+        st, ln = ol.raster_blocks(nv)
+        for h in range(H):
+            keep = keep_from_lists(cnt[0, h], idx[0, h], len(st))
+            _, P = om.block_mask(_np(q[0, h]), _np(k[0, h]), st, ln, st, ln, 0.15)
+            assert mask_mismatches(P, 0.15, keep) == 0
+
+
+def test_mask_deterministic(gpu_lib):
+    w, q, k, v = _inputs("wan480")
+    qd, kd = q.cuda(), k.cuda()
+    a = gpu_lib.build_block_mask(qd, kd, w.thr, n_valid=w.n_valid)
+    b = gpu_lib.build_block_mask(qd, kd, w.thr, n_valid=w.n_valid)
+    assert torch.equal(a[0], b[0])
+    for r in range(0, a[0].numel(), 97):
+        c = int(a[0].view(-1)[r])
+        assert torch.equal(a[1].view(-1, a[1].shape[-1])[r, :c], b[1].view(-1, b[1].shape[-1])[r, :c])
+
+
+# ------------------------------------------------------------------- attention
+
+def _attn_case(bsa, w, q, k, v, heads, nsample, seed=0, thr=None):
+    thr = w.thr if thr is None else thr
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cnt, idx = bsa.build_block_mask(qd, kd, thr, n_valid=w.n_valid)
+    o = bsa.block_sparse_attn_fwd(qd, kd, vd, cnt, idx, n_valid=w.n_valid)
+    torch.cuda.synchronize()
+    o = _np(o)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    st, ln = ol.raster_blocks(w.n_valid)
+    nb = len(st)
+    rng = np.random.default_rng(seed)
+    for h in heads:
+        keep = keep_from_lists(cnt[0, h], idx[0, h], nb)
+        blocks = list(range(nb)) if nsample is None else sorted(
+            set(rng.choice(nb, size=min(nsample, nb), replace=False).tolist()) | {0, nb - 1})
+        ref = oa.masked_attention(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), st, ln, st, ln, keep,
+                                  blocks=blocks)
+        rows = _rows_of(st, ln, blocks)
+        _check_out(o[0, h], ref, rows, f"head {h} ({len(blocks)} query blocks)")
+    assert (o[:, :, w.n_valid:] == 0).all()
+    return o
+
+
+def test_attn_parity_tiny(gpu_lib):
+    w, q, k, v = _inputs("tiny")
+    say("attention parity tiny (every block)")
+    _attn_case(gpu_lib, w, q, k, v, range(w.H), None)
+
+
+def test_attn_parity_wan480(gpu_lib):
+    w, q, k, v = _inputs("wan480")
+    say("attention parity wan480 (sampled query blocks)")
+    _attn_case(gpu_lib, w, q, k, v, [0, 5, 11], 10)
+
+
+def test_attn_dense_equivalence(gpu_lib):
+    # thr = 0 keeps every block: the result is dense softmax attention.
+    w, q, k, v = _inputs("tiny")
+    say("attention thr=0 == dense")
+    o = _attn_case(gpu_lib, w, q, k, v, range(w.H), None, thr=0.0)
+    for h in range(w.H):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[0, h].double()[None], k[0, h].double()[None], v[0, h].double()[None])[0].numpy()
+        _check_out(o[0, h], ref, np.arange(w.n_valid), f"dense head {h}")
+
+
+@pytest.mark.parametrize("H,N,nv,d", [(2, 256, 256, 64), (3, 704, 650, 128), (1, 1088, 1030, 64)])
+def test_attn_ragged_random_masks(gpu_lib, H, N, nv, d):
+    # random kept lists (including long and single-block rows) on ragged sizes
+    bsa = gpu_lib
+    say(f"attention random masks H={H} N={N} n_valid={nv} d={d}")
+    rng = np.random.default_rng(N)
+    x = rng.normal(size=(3, 1, H, N, d)).astype(np.float32)
+    x[:, :, :, nv:] = 0
+    q, k, v = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(3))
+    st, ln = ol.raster_blocks(nv)
+    nb = len(st)
+    keep = rng.random((H, nb, nb)) < 0.3
+    keep[:, :, 0] |= ~keep.any(2)
+    keep[:, 0, :] = True
+    cnt = keep.sum(2).astype(np.int32)
+    idx = np.full((H, nb, nb), -1, np.int32)
+    for h in range(H):
+        for i in range(nb):
+            ids = np.nonzero(keep[h, i])[0]
+            idx[h, i, :len(ids)] = ids
+    o = bsa.block_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(cnt[None]).cuda(),
+                                  torch.from_numpy(idx[None]).cuda(), n_valid=nv)
+    o = _np(o)
+    for h in range(H):
+        ref = oa.masked_attention(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), st, ln, st, ln, keep[h])
+        _check_out(o[0, h], ref, np.arange(nv), f"head {h}")
+    assert (o[:, :, nv:] == 0).all()
+
+
+def test_attn_empty_rows_give_zero(gpu_lib):
+    bsa = gpu_lib
+    q = torch.randn(1, 1, 128, 64, dtype=torch.bfloat16)
+    cnt = torch.tensor([[[0, 1]]], dtype=torch.int32)
+    idx = torch.tensor([[[[0, -1], [1, -1]]]], dtype=torch.int32)
+    o = bsa.block_sparse_attn_fwd(q.cuda(), q.cuda(), q.cuda(), cnt.cuda(), idx.cuda()).cpu()
+    assert (o[0, 0, :64] == 0).all() and o[0, 0, 64:].abs().sum() > 0
+
+
+def test_attn_pad_poisoning_and_determinism(gpu_lib):
+    bsa = gpu_lib
+    w, q, k, v = _inputs("wan480")
+    say("pad poisoning + determinism wan480")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cnt, idx = bsa.build_block_mask(qd, kd, w.thr, n_valid=w.n_valid)
+    o1 = bsa.block_sparse_attn_fwd(qd, kd, vd, cnt, idx, n_valid=w.n_valid)
+    o2 = bsa.block_sparse_attn_fwd(qd, kd, vd, cnt, idx, n_valid=w.n_valid)
+    assert torch.equal(o1, o2)
+    for val in (float("nan"), 1e4):
+        qp, kp, vp = qd.clone(), kd.clone(), vd.clone()
+        for t in (qp, kp, vp):
+            t[:, :, w.n_valid:] = val
+        c2, i2 = bsa.build_block_mask(qp, kp, w.thr, n_valid=w.n_valid)
+        assert torch.equal(c2, cnt)
+        o3 = bsa.block_sparse_attn_fwd(qp, kp, vp, c2, i2, n_valid=w.n_valid)
+        assert torch.equal(o3, o1), val
+
+
+# ---------------------------------------------------------------- full-size 720p
+
+@pytest.mark.parametrize("part", ["mask", "attn"])
+def test_hunyuan720_sampled(gpu_lib, part):
+    w, q, k, v = _inputs("hunyuan720")
+    say(f"hunyuan720 {part} (sampled heads / blocks)")
+    if part == "mask":
+        _, _, bad = _mask_case(gpu_lib, w, q, k, [0, 23])
+        assert bad == 0
+    else:
+        _attn_case(gpu_lib, w, q, k, v, [4, 19], 5)
