@@ -1,0 +1,268 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config wan480]
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: block mean pooling of Q and K, reduced attention + CDF selection (the
+mask stage), then the block-sparse attention forward. Prints ONE JSON line.
+
+  value      effective TFLOP/s of the whole step: F_eff / step time, where
+             F_eff = 4 * d * sum over kept (query block I, key block J) of
+             len_I * len_J (QK^T and PV of kept tiles only, padding excluded)
+  roofline   the attention kernel (the dominant one) against the bf16 dense
+             MFMA peak of MI355X (2516.6 TFLOP/s), timed with HIP events on
+             the stream the library launches on
+  cpu_baseline  the float64 CPU reference timed on a bounded sample of the
+             same workload and extrapolated to one step
+
+A second workload (the 118,800-token 720p layer) is measured after the main
+one and reported under "also", with its mask-stage / attention time ratio.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_attention_avg_amd as bsa  # noqa: E402
+from gen import WORKLOADS, generate  # noqa: E402
+
+METRIC = "block-sparse attn effective TFLOP/s & % bf16 MFMA peak at ~90% sparsity"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def describe(w) -> str:
+    return (f"{w.key}: B{w.B} H{w.H} d{w.d} N{w.N} ({w.T}x{w.Hl}x{w.Wl} latent, "
+            f"{w.n_valid} tokens), block {w.block}, thr {w.thr}")
+
+
+def block_lengths(w):
+    nb = -(-w.n_valid // w.block)
+    ln = np.full(nb, w.block, dtype=np.int64)
+    ln[-1] = w.n_valid - w.block * (nb - 1)
+    return ln
+
+
+def effective_flops(w, cnt: np.ndarray, idx: np.ndarray):
+    """F_eff and block / token-pair sparsity from the kept lists."""
+    ln = block_lengths(w)
+    nb = len(ln)
+    rows_c = cnt.reshape(-1, nb)
+    rows_i = idx.reshape(-1, nb, idx.shape[-1])
+    stride = idx.shape[-1]
+    col = np.arange(stride)[None, None, :]
+    valid = col < rows_c[:, :, None]
+    klen = np.where(valid, ln[np.clip(rows_i, 0, nb - 1)], 0).sum(-1)     # [BH, nqb]
+    flops = 4.0 * w.d * float((klen * ln[None, :]).sum())
+    kept = float(rows_c.sum())
+    total = rows_c.shape[0] * nb * nb
+    pair_total = rows_c.shape[0] * float(ln.sum()) ** 2
+    return flops, 1.0 - kept / total, 1.0 - float((klen * ln[None, :]).sum()) / pair_total
+
+
+class Runner:
+    """Holds device inputs and preallocated outputs for one workload."""
+
+    def __init__(self, w, dev):
+        self.w = w
+        q, k, v = generate(w)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.q_cpu, self.k_cpu, self.v_cpu = q, k, v
+        nb = -(-w.n_valid // w.block)
+        self.nb = nb
+        self.cnt = torch.empty((w.B, w.H, nb), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((w.B, w.H, nb, nb), dtype=torch.int32, device=dev)
+        self.o = torch.empty_like(self.q)
+        lib = bsa.load()
+        self.ws = torch.empty(lib.bsa_build_block_mask_workspace(w.B, w.H, nb, nb, w.d),
+                              dtype=torch.uint8, device=dev)
+
+    def mask(self):
+        bsa.build_block_mask(self.q, self.k, self.w.thr, n_valid=self.w.n_valid,
+                             out=(self.cnt, self.idx), workspace=self.ws)
+
+    def attn(self):
+        bsa.block_sparse_attn_fwd(self.q, self.k, self.v, self.cnt, self.idx,
+                                  n_valid=self.w.n_valid, out=self.o)
+
+    def step(self):
+        self.mask()
+        self.attn()
+
+    def timed(self, steps: int, warmup: int):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e in evs:
+            e[0].record()
+            self.mask()
+            e[1].record()
+            self.attn()
+            e[2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_mask = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        t_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        return wall / steps * 1e3, t_mask, t_attn
+
+    def summary(self, ms_step, t_mask, t_attn):
+        w = self.w
+        cnt = self.cnt.cpu().numpy()
+        idx = self.idx.cpu().numpy()
+        flops, sp_block, sp_pair = effective_flops(w, cnt, idx)
+        attn_tflops = flops / (t_attn * 1e-3) / 1e12
+        qk_bytes = 2.0 * w.B * w.H * w.N * w.d * 2
+        mask_bytes = qk_bytes + cnt.nbytes + 4.0 * float(cnt.sum())
+        return {
+            "flops_eff": flops,
+            "step_tflops": flops / (ms_step * 1e-3) / 1e12,
+            "attn_tflops": attn_tflops,
+            "attn_frac_of_peak": attn_tflops / PEAK_BF16_TFLOPS,
+            "t_mask_ms": t_mask,
+            "t_attn_ms": t_attn,
+            "mask_over_attn": t_mask / t_attn,
+            "mask_gbs": mask_bytes / (t_mask * 1e-3) / 1e9,
+            "mask_frac_of_hbm": mask_bytes / (t_mask * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "sparsity_blocks": sp_block,
+            "sparsity_token_pairs": sp_pair,
+            "kept_per_row_mean": float(cnt.mean()),
+            "kept_per_row_max": int(cnt.max()),
+        }
+
+
+def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
+    """Times the float64 CPU reference on a bounded sample, extrapolated to a step."""
+    from oracle import attention as oa, layout as ol, mask as om  # CPU reference (baseline leg only)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = r.w
+    st, ln = ol.raster_blocks(w.n_valid, w.block)
+    t0 = time.perf_counter()
+    keeps = []
+    for h in range(mask_heads):
+        kp, _ = om.block_mask(r.q_cpu[0, h].double().numpy(), r.k_cpu[0, h].double().numpy(),
+                              st, ln, st, ln, w.thr)
+        keeps.append(kp)
+    t_mask = (time.perf_counter() - t0) / mask_heads * w.H * w.B
+    rng = np.random.default_rng(0)
+    blocks = sorted(rng.choice(len(st), size=min(attn_blocks, len(st)), replace=False).tolist())
+    qh, kh, vh = (t[0, 0].double().numpy() for t in (r.q_cpu, r.k_cpu, r.v_cpu))
+    t0 = time.perf_counter()
+    oa.masked_attention(qh, kh, vh, st, ln, st, ln, keeps[0], blocks=blocks)
+    t_att = (time.perf_counter() - t0) / len(blocks) * len(st) * w.H * w.B
+    t_step = t_mask + t_att
+    return {
+        "value": flops_total / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy reference: mask stage of {mask_heads} of {w.H} heads and "
+                   f"attention of {len(blocks)} of {len(st)} query blocks of head 0, "
+                   f"extrapolated to one step (est. {t_step:.1f} s/step)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan480", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", default="hunyuan720", help="second workload to report, or 'none'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the hot path shards by head with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    bsa.load()
+
+    w = WORKLOADS[a.config]
+    if w.order != "raster":
+        print("bench.py times the raster-order workloads (tiny, wan480, hunyuan720)", file=sys.stderr)
+        sys.exit(1)
+    r = Runner(w, dev)
+    ms_step, t_mask, t_attn = r.timed(a.steps, a.warmup)
+    s = r.summary(ms_step, t_mask, t_attn)
+
+    line = {
+        "metric": METRIC,
+        "value": round(s["step_tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Fourier-feature Q/K, Gaussian V)",
+        "config": {"workload": describe(w), "global_batch": w.B, "seq_len": w.N,
+                   "heads": w.H, "head_dim": w.d, "block": w.block, "thr": w.thr,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel",
+            "achieved": round(s["attn_tflops"], 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(s["attn_frac_of_peak"], 4),
+            "traffic": None,
+        },
+        "pct_bf16_peak_attn": round(100 * s["attn_frac_of_peak"], 2),
+        "sparsity": {"blocks": round(s["sparsity_blocks"], 4),
+                     "token_pairs": round(s["sparsity_token_pairs"], 4),
+                     "kept_per_row_mean": round(s["kept_per_row_mean"], 2),
+                     "kept_per_row_max": s["kept_per_row_max"]},
+        "stages_ms": {"mask": round(t_mask, 4), "attention": round(t_attn, 4),
+                      "mask_over_attention": round(s["mask_over_attn"], 4),
+                      "mask_gbs": round(s["mask_gbs"], 1)},
+        "flops_eff_per_step": s["flops_eff"],
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r, s["flops_eff"])
+    if a.also and a.also != "none" and a.also != a.config:
+        del r
+        torch.cuda.empty_cache()
+        w2 = WORKLOADS[a.also]
+        r2 = Runner(w2, dev)
+        m2, tm2, ta2 = r2.timed(max(3, a.steps // 2), max(1, a.warmup // 2))
+        s2 = r2.summary(m2, tm2, ta2)
+        line["also"] = {w2.key: {
+            "workload": describe(w2),
+            "ms_per_step": round(m2, 4),
+            "step_tflops": round(s2["step_tflops"], 3),
+            "attn_tflops": round(s2["attn_tflops"], 3),
+            "pct_bf16_peak_attn": round(100 * s2["attn_frac_of_peak"], 2),
+            "mask_ms": round(tm2, 4),
+            "attention_ms": round(ta2, 4),
+            "mask_over_attention": round(s2["mask_over_attn"], 4),
+            "mask_gbs": round(s2["mask_gbs"], 1),
+            "sparsity_blocks": round(s2["sparsity_blocks"], 4),
+        }}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

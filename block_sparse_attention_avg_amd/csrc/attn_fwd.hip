@@ -9,21 +9,28 @@
 // in ascending order as a stream of key rows cut into 64-row chunks; with
 // uniform 64-token blocks a chunk is exactly one key block.
 //
-// Per chunk, K (row-major) and V (transposed to [d][key]) are staged in LDS by
-// all 128 threads; the next chunk's global loads are issued before the
-// current chunk's math so they overlap it. Each wave then computes
-//   S^T = K Q^T           bf16 MFMA 32x32x16, Q^T held in registers as the
-//                         B operand for the whole tile,
-// which leaves every lane holding 32 key scores of a single query, so the
-// online-softmax max/sum are lane-local except for one exchange with the lane
-// holding that query's other 32 keys. P^T is rounded to bf16 in registers and
-// fed straight back as the B operand of
-//   O^T += V^T P^T        bf16 MFMA 32x32x16,
-// which works because the transposed V tile is written to LDS with its key
-// order permuted to match the accumulator layout of S^T (no shuffles of P).
-// The softmax runs in the log2 domain in fp32 (running max m, running sum l);
-// O is divided by l once at the end, staged through LDS and stored as bf16
-// rows.
+// Data movement: K and V chunks go HBM -> LDS with direct-to-LDS loads (no
+// staging registers), row-major, each row's 16-byte pieces XOR-swizzled so
+// that both the K operand reads and the transposed V reads below are free of
+// bank conflicts. The pipeline is split by phase: the next chunk's K is in
+// flight while this chunk's softmax and PV run, the next V while the next S
+// runs. Waits are explicit vmcnt counts; barriers carry no memory fence (a
+// fence would drain every in-flight load).
+//
+// Math per wave and chunk:
+//   S^T = K Q^T        bf16 MFMA 32x32x16; Q^T stays in registers as the B
+//                      operand for the whole tile, so each lane ends up with
+//                      32 key scores of ONE query: max/sum are lane-local plus
+//                      one permlane32 swap with the lane holding the other 32.
+//   online softmax     fp32, log2 domain (scale*log2e folded into one FMA),
+//                      O rescaled only when some row max moved.
+//   O^T += V^T P^T     bf16 MFMA 32x32x16; P^T is the S^T accumulator
+//                      rounded to bf16 in registers (hardware convert), and
+//                      V^T comes straight from the row-major V tile through the
+//                      LDS transpose read (ds_read_b64_tr_b16), addressed so
+//                      its key order matches the accumulator layout of S^T.
+// O is divided by the row sum once at the end, staged through LDS and
+// written as bf16 rows.
 #include "common.h"
 
 #include <math.h>
@@ -47,40 +54,363 @@ struct AttnArgs {
 
 namespace {
 
-__device__ __forceinline__ uint32_t bf16_of(const uint4& w, int e) {
-  const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
-  return (e & 1) ? (x >> 16) : (x & 0xffffu);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Swizzle of the 16-byte piece index inside a K/V tile row.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  else return (r >> 1) & 7;
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt unconstrained).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
+// Workgroup barrier for the LDS pipeline: this wave's LDS accesses complete
+// before it arrives (so no other wave can refill a tile under a read still in
+// the LDS queue), compiler-level ordering of memory accesses on both sides,
+// but no wait on in-flight direct-to-LDS loads (those are waited explicitly).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
-  uint4 u;
-  u.x = pack_bf16x2(p[0], p[1]);
-  u.y = pack_bf16x2(p[2], p[3]);
-  u.z = pack_bf16x2(p[4], p[5]);
-  u.w = pack_bf16x2(p[6], p[7]);
-  return __builtin_bit_cast(bf16x8, u);
+  const bf16x2 a = __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2);
+  const bf16x2 b = __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2);
+  const bf16x2 c = __builtin_convertvector((f32x2){p[4], p[5]}, bf16x2);
+  const bf16x2 d = __builtin_convertvector((f32x2){p[6], p[7]}, bf16x2);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Position of key offset o (0..63) inside a transposed V row: within each group
-// of 16 keys, offsets (a, g, b) = (bit 3, bit 2, bits 1:0) are stored at
-// (g, a, b), which is the order in which a lane of the S^T accumulator holds
-// its keys when the accumulator is reused as the PV B operand.
-__device__ __forceinline__ int vpos(int o) {
-  return (o & ~0xC) | ((o & 4) << 1) | ((o & 8) >> 1);
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
+// max over lanes l and l^32 (the two wave halves hold the same query)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 }  // namespace
 
+// One query tile. The K and V tiles are passed as distinct __restrict__ LDS
+// pointers: after inlining, the compiler can then tell the two direct-to-LDS
+// load streams apart and leaves the waits to the explicit vmcnt counts below
+// instead of draining every load before each LDS read.
+template <int D, bool KVAR>
+__device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
+                                          lds_u8* Kp, lds_u8* Vp,
+                                          int* tok, int* chunk_rows) {
+  constexpr int ROWB = D * 2;                  // bytes per K/V row
+  constexpr int TILE = 64 * ROWB;              // bytes per K or V tile
+  constexpr int NI = TILE / 1024 / 2;          // direct-to-LDS loads per wave per tile
+  constexpr int RPI = 1024 / ROWB;             // rows per load instruction
+  constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const size_t head_off = (size_t)bh * a.N * D;
+  const uint16_t* qh = a.q + head_off;
+  const unsigned char* kh = reinterpret_cast<const unsigned char*>(a.k + head_off);
+  const unsigned char* vh = reinterpret_cast<const unsigned char*>(a.v + head_off);
+
+  // Q^T as MFMA B operand: lane supplies Q[row][16c + 8*half .. +7].
+  bf16x8 qf[D / 16];
+  {
+    const int qr = 32 * wave + l32;
+    const bool ok = qr < ql;
+    const uint16_t* src = qh + (size_t)(qs + (ok ? qr : 0)) * D + 8 * half;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      uint4 w = ok ? *reinterpret_cast<const uint4*>(src + 16 * c) : make_uint4(0, 0, 0, 0);
+      qf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const size_t qrow = (size_t)bh * a.nqb + I;
+  const int cnt = __builtin_amdgcn_readfirstlane(a.kv_count[qrow]);
+  const int32_t* list = a.kv_index + qrow * a.kv_stride;
+
+  // ---- per-lane LDS offsets (loop invariant)
+  // K operand of S^T: row 32kb + l32, piece 2c + half.
+  const int fk = swz<D>(l32 & 15);
+  // V^T operand via the transpose read: lane (16-lane group g, slot 4j+q)
+  // addresses key row 32kb + 16hh + 8t + 4*half + j, channels
+  // 32dg + 16(g&1) + 4q .. +3, so the lane receives channel 32dg + l32 of
+  // keys 32kb + 16hh + 8t + 4*half + 0..3 -- the P^T slot order.
+  const int g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
+  int voff[D / 32][2];
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * t + 4 * half + sj;               // + 32kb + 16hh (multiple of 16)
+      const int piece = 4 * dg + 2 * g16 + (sq >> 1);
+      voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
+    }
+
+  // ---- direct-to-LDS issue of one K or V tile. Row r comes from token
+  // ks + r (uniform) or tk[r] (gathered); rows >= kl re-load row 0 (finite
+  // data whose keys are masked to -inf).
+  auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
+    const unsigned char* src = isv ? vh : kh;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ins = wave * NI + i;
+      const int r = ins * RPI + lane / PPR;
+      const int p = lane % PPR;
+      const int rr = r < kl ? r : 0;
+      const int t = KVAR ? tk[rr] : ks + rr;
+      const unsigned char* g = src + (size_t)t * ROWB + ((p ^ swz<D>(r & 15)) << 4);
+      // separate call sites: each DMA names its own destination tile
+      if (isv)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Vp + ins * 1024, 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Kp + ins * 1024, 16, 0, 0);
+    }
+  };
+
+  // ---- chunk walk.
+  // Uniform blocks: chunk c is key block list[c]; the list is read 64
+  // entries at a time into a register window (one vector load per 64
+  // chunks), each entry taken with readlane.
+  int lst = 0;
+  auto chunk_uniform = [&](int c, int& ks, int& kl) {
+    if (c >= cnt) { ks = 0; kl = 0; return; }
+    if ((c & 63) == 0) lst = list[min(c + lane, cnt - 1)];
+    const int J = __builtin_amdgcn_readlane(lst, c & 63);
+    ks = J * 64;                       // uniform 64-token key blocks
+    kl = min(64, a.n_valid - ks);
+  };
+  // Gathered blocks: wave 0 writes the token indices of the next chunk to
+  // tok[buf] with a cursor (list entry e_cur, offset off_cur).
+  int e_cur = 0, off_cur = 0;
+  auto next_chunk = [&](int buf) {   // wave 0 only
+    int rows = 0;
+    while (rows == 0 && e_cur < cnt) {
+      const int ent = e_cur + lane;
+      int ks = 0, n = 0;
+      if (ent < cnt) a.kb.get(bh, list[ent], ks, n);
+      int incl = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int total = __shfl(incl, 63);
+      rows = max(0, min(64, total - off_cur));
+      const int pos = off_cur + lane;
+      int lo = 0, hi = 64;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (__shfl(incl, mid & 63) > pos) hi = mid; else lo = mid + 1;
+      }
+      const int src = lo & 63;
+      const int excl_src = __shfl(incl, src) - __shfl(n, src);
+      const int ks_src = __shfl(ks, src);
+      if (lane < rows) tok[buf * 64 + lane] = ks_src + (pos - excl_src);
+      const int pend = off_cur + rows;
+      int lo2 = 0, hi2 = 64;
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2) >> 1;
+        if (__shfl(incl, mid & 63) > pend) hi2 = mid; else lo2 = mid + 1;
+      }
+      if (lo2 >= 64) {
+        e_cur += 64;
+        off_cur = pend - total;
+      } else {
+        off_cur = pend - (__shfl(incl, lo2) - __shfl(n, lo2));
+        e_cur += lo2;
+      }
+    }
+    if (lane == 0) chunk_rows[buf] = rows;
+  };
+  auto chunk_info = [&](int c, int& ks, int& kl) {
+    if (KVAR) {
+      ks = 0;
+      kl = __builtin_amdgcn_readfirstlane(chunk_rows[c & 1]);
+    } else {
+      chunk_uniform(c, ks, kl);
+    }
+  };
+
+  if (KVAR) {
+    if (wave == 0) next_chunk(0);
+    wait_lgkm0();
+    wg_barrier();
+  }
+  int ks, kl;
+  chunk_info(0, ks, kl);
+  if (kl > 0) {
+    issue_tile(false, ks, kl, tok);
+    issue_tile(true, ks, kl, tok);
+  }
+  for (int c = 0; kl > 0; ++c) {
+    if (KVAR && wave == 0) next_chunk((c + 1) & 1);
+    wait_vm<NI>();                 // own K(c) loads landed (V(c) may be in flight)
+    wait_lgkm0();
+    wg_barrier();                  // ... and every other wave's
+
+    // S^T = K Q^T
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
+        const bf16x8 ka = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], sacc[kb], 0, 0, 0);
+      }
+    wg_barrier();                  // every wave is done reading K(c)
+    int ks_n, kl_n;
+    chunk_info(c + 1, ks_n, kl_n);
+    // The next chunk's loads are issued unconditionally (after the last chunk
+    // they re-load the current rows into the free buffer): a load issued on
+    // one path only makes the compiler drain every load before LDS reads.
+    const bool more = kl_n > 0;
+    const int ks_i = more ? ks_n : ks, kl_i = more ? kl_n : kl;
+    const int* tk_i = tok + (((more ? c + 1 : c)) & 1) * 64;
+    issue_tile(false, ks_i, kl_i, tk_i);
+
+    // online softmax; sacc[kb][r] is key 32kb + 8(r/4) + 4*half + r%4
+    if (kl < 64) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kl) sacc[kb][r] = -INFINITY;
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+    mloc = halves_max(mloc);
+    const float m_new = fmaxf(m_run, mloc * a.sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.sl2, -m_new));
+        sacc[kb][r] = p;
+        rs += p;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = sacc[kb][8 * hh + e];
+        pf[kb][hh] = pack8(tmp);
+      }
+
+    wait_vm<NI>();                 // own V(c) loads landed (next K in flight)
+    wg_barrier();
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int dg = 0; dg < D / 32; ++dg) {
+          const int base = (32 * kb + 16 * hh) * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][0]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][hh], oacc[dg], 0, 0, 0);
+        }
+    wg_barrier();                  // every wave is done reading V(c)
+    issue_tile(true, ks_i, kl_i, tk_i);
+    ks = ks_n;
+    kl = kl_n;
+  }
+  wait_vm<0>();                    // no load may still target LDS
+
+  // ---- epilogue: O = O^T / l, staged through the K tile (swizzled rows),
+  // stored as bf16 rows. No load is in flight here.
+  const float lt = halves_sum(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int orow = 32 * wave + l32;
+  const int fo = swz<D>(orow & 15);
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      // channels 32dg + 8*j4 + 4*half .. +3 = piece 4dg + j4, byte 8*half
+      const u32x2 w = {pack2(oacc[dg][4 * j4 + 0] * inv, oacc[dg][4 * j4 + 1] * inv),
+                       pack2(oacc[dg][4 * j4 + 2] * inv, oacc[dg][4 * j4 + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          Kp + orow * ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
+    }
+  wait_lgkm0();
+  wg_barrier();
+  uint16_t* oh = a.o + head_off;
+#pragma unroll
+  for (int r = 0; r < TILE / 16 / 128; ++r) {
+    const int u = tid + 128 * r;            // 16-byte piece of the 64 x D tile
+    const int row = u / PPR, p = u % PPR;
+    if (row < ql)
+      *reinterpret_cast<u32x4*>(oh + (size_t)(qs + row) * D + p * 8) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              Kp + row * ROWB + ((p ^ swz<D>(row & 15)) << 4));
+  }
+}
+
 template <int D, bool QVAR, bool KVAR>
-__global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KS = D + 8;        // K tile row stride (elements)
-  constexpr int VS = 64 + 8;       // V^T tile row stride (elements)
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int NK = 64 * CPR / 128;   // K chunks per thread
-  constexpr int NV = 16 * CPR / 128;   // V key-quad units per thread
-  __shared__ __align__(16) uint16_t Ks[64 * KS];
-  __shared__ __align__(16) uint16_t Vt[D * VS];
-  __shared__ int tok[2][64];
+__global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int TILE = 64 * D * 2;
+  __shared__ __align__(16) unsigned char Ks[TILE];
+  __shared__ __align__(16) unsigned char Vs[TILE];
+  __shared__ int tok[2 * 64];
   __shared__ int chunk_rows[2];
 
   // Flat id -> (head, tile): consecutive workgroups are dealt round-robin to
@@ -115,265 +445,7 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
     ql = min(64, n0 - 64 * sub);
   }
   if (ql <= 0) return;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, l32 = lane & 31;
-  const size_t head_off = (size_t)bh * a.N * D;
-  const uint16_t* qh = a.q + head_off;
-  const uint16_t* kh = a.k + head_off;
-  const uint16_t* vh = a.v + head_off;
-
-  // Q^T as MFMA B operand: lane supplies Q[row][16c + 8*half .. +7].
-  bf16x8 qf[D / 16];
-  {
-    const int qr = 32 * wave + l32;
-    const bool ok = qr < ql;
-    const uint16_t* src = qh + (size_t)(qs + (ok ? qr : 0)) * D + 8 * half;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      uint4 w = ok ? *reinterpret_cast<const uint4*>(src + 16 * c) : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const size_t qrow = (size_t)bh * a.nqb + I;
-  const int cnt = a.kv_count[qrow];
-  const int32_t* list = a.kv_index + qrow * a.kv_stride;
-
-  uint4 kreg[NK];
-  uint4 vreg[NV][4];
-
-  // ---- chunk addressing
-  // Uniform: chunk c = key block list[c], rows [64*J, 64*J + kl).
-  // Variable: rows come from tok[buf][r] (token index), r < chunk_rows[buf].
-  auto load_chunk = [&](int row_base, int kl, const int* tk) {
-#pragma unroll
-    for (int r = 0; r < NK; ++r) {
-      const int u = tid + 128 * r;
-      const int row = u / CPR, col = u % CPR;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (row < kl) {
-        const int t = KVAR ? tk[row] : row_base + row;
-        w = *reinterpret_cast<const uint4*>(kh + (size_t)t * D + col * 8);
-      }
-      kreg[r] = w;
-    }
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int u = tid + 128 * r;
-      const int kq = u / CPR, col = u % CPR;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (row < kl) {
-          const int t = KVAR ? tk[row] : row_base + row;
-          w = *reinterpret_cast<const uint4*>(vh + (size_t)t * D + col * 8);
-        }
-        vreg[r][e] = w;
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int r = 0; r < NK; ++r) {
-      const int u = tid + 128 * r;
-      const int row = u / CPR, col = u % CPR;
-      *reinterpret_cast<uint4*>(&Ks[row * KS + col * 8]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int u = tid + 128 * r;
-      const int kq = u / CPR, col = u % CPR;
-      const int pos = vpos(4 * kq);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w;
-        w.x = bf16_of(vreg[r][0], e) | (bf16_of(vreg[r][1], e) << 16);
-        w.y = bf16_of(vreg[r][2], e) | (bf16_of(vreg[r][3], e) << 16);
-        *reinterpret_cast<uint2*>(&Vt[(col * 8 + e) * VS + pos]) = w;
-      }
-    }
-  };
-
-  auto compute_chunk = [&](int kl) {
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&Ks[(32 * kb + l32) * KS + 16 * c + 8 * half]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], sacc[kb], 0, 0, 0);
-      }
-    }
-    // sacc[kb][r] = S[query 32*wave + l32][key 32kb + 8(r/4) + 4*half + r%4]
-    if (kl < 64) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kl) sacc[kb][r] = -INFINITY;
-        }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * a.sl2);
-    const float alpha = exp2f(m_run - m_new);
-    float p[2][16];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[kb][r] = exp2f(fmaf(sacc[kb][r], a.sl2, -m_new));
-        rs += p[kb][r];
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pf[kb][hh] = pack8(&p[kb][8 * hh]);
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              &Vt[(32 * dg + l32) * VS + 32 * kb + 16 * hh + 8 * half]);
-          oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][hh], oacc[dg], 0, 0, 0);
-        }
-  };
-
-  if (!KVAR) {
-    int kl_next = 0;
-    if (cnt > 0) {
-      int ks;
-      a.kb.get(bh, list[0], ks, kl_next);
-      load_chunk(ks, kl_next, nullptr);
-    }
-    for (int c = 0; c < cnt; ++c) {
-      const int kl = kl_next;
-      __syncthreads();
-      store_chunk();
-      __syncthreads();
-      if (c + 1 < cnt) {
-        int ks;
-        a.kb.get(bh, list[c + 1], ks, kl_next);
-        load_chunk(ks, kl_next, nullptr);
-      }
-      compute_chunk(kl);
-    }
-  } else {
-    // Cursor over the stream of kept key rows: list entry e, offset off.
-    // Wave 0 produces the token indices of the next chunk into tok[buf].
-    int e = 0, off = 0;
-    auto next_chunk = [&](int buf) {
-      // wave 0 only; skips entries until at least one row is available
-      int rows = 0;
-      while (rows == 0 && e < cnt) {
-        const int ent = e + lane;
-        int ks = 0, n = 0;
-        if (ent < cnt) a.kb.get(bh, list[ent], ks, n);
-        int incl = n;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o);
-          if (lane >= o) incl += t;
-        }
-        const int total = __shfl(incl, 63);
-        rows = min(64, total - off);
-        // row `lane` sits at stream position off + lane: first entry with incl > pos
-        const int pos = off + lane;
-        int lo = 0, hi = 64;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (__shfl(incl, mid & 63) > pos) hi = mid; else lo = mid + 1;
-        }
-        const int src = lo & 63;
-        const int excl_src = __shfl(incl, src) - __shfl(n, src);
-        const int ks_src = __shfl(ks, src);
-        if (lane < rows) tok[buf][lane] = ks_src + (pos - excl_src);
-        // advance the cursor past the rows consumed
-        const int pend = off + rows;
-        int lo2 = 0, hi2 = 64;
-        while (lo2 < hi2) {
-          const int mid = (lo2 + hi2) >> 1;
-          if (__shfl(incl, mid & 63) > pend) hi2 = mid; else lo2 = mid + 1;
-        }
-        if (lo2 >= 64) {
-          e += 64;
-          off = pend - total;
-        } else {
-          off = pend - (__shfl(incl, lo2) - __shfl(n, lo2));
-          e += lo2;
-        }
-      }
-      if (lane == 0) chunk_rows[buf] = rows;
-    };
-    if (wave == 0) next_chunk(0);
-    __syncthreads();
-    int buf = 0;
-    int kl = chunk_rows[0];
-    if (kl > 0) load_chunk(0, kl, tok[0]);
-    while (kl > 0) {
-      __syncthreads();
-      store_chunk();
-      if (wave == 0) next_chunk(buf ^ 1);
-      __syncthreads();
-      const int kl_next = chunk_rows[buf ^ 1];
-      if (kl_next > 0) load_chunk(0, kl_next, tok[buf ^ 1]);
-      compute_chunk(kl);
-      kl = kl_next;
-      buf ^= 1;
-    }
-  }
-
-  // ---- epilogue: O = O^T / l, staged through LDS, stored as bf16 rows
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __syncthreads();
-#pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      uint2 w;
-      w.x = pack_bf16x2(oacc[dg][4 * j4 + 0] * inv, oacc[dg][4 * j4 + 1] * inv);
-      w.y = pack_bf16x2(oacc[dg][4 * j4 + 2] * inv, oacc[dg][4 * j4 + 3] * inv);
-      *reinterpret_cast<uint2*>(&Ks[(32 * wave + l32) * KS + 32 * dg + 8 * j4 + 4 * half]) = w;
-    }
-  __syncthreads();
-  uint16_t* oh = a.o + head_off;
-#pragma unroll
-  for (int r = 0; r < NK; ++r) {
-    const int u = tid + 128 * r;
-    const int row = u / CPR, col = u % CPR;
-    if (row < ql)
-      *reinterpret_cast<uint4*>(oh + (size_t)(qs + row) * D + col * 8) =
-          *reinterpret_cast<const uint4*>(&Ks[row * KS + col * 8]);
-  }
+  attn_tile<D, KVAR>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
 }
 
 // Tile prefix over query blocks of any length: tb[bh][I] = sum_{I'<I} ceil(len/64).
