@@ -86,6 +86,8 @@ class Runner:
         lib = bsa.load()
         self.ws = torch.empty(lib.bsa_build_block_mask_workspace(w.B, w.H, nb, nb, w.d),
                               dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(lib.bsa_block_sparse_attn_fwd_workspace(w.B, w.H, nb, None),
+                                   dtype=torch.uint8, device=dev)
 
     def mask(self):
         bsa.build_block_mask(self.q, self.k, self.w.thr, n_valid=self.w.n_valid,
@@ -93,7 +95,7 @@ class Runner:
 
     def attn(self):
         bsa.block_sparse_attn_fwd(self.q, self.k, self.v, self.cnt, self.idx,
-                                  n_valid=self.w.n_valid, out=self.o)
+                                  n_valid=self.w.n_valid, out=self.o, workspace=self.ws_attn)
 
     def step(self):
         self.mask()
@@ -177,6 +179,20 @@ def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
     }
 
 
+def copy_calibration(dev, steps: int):
+    """Identity permutation: reads and writes exactly 1 GiB per launch."""
+    B, H, N, d = 1, 16, 262144, 128        # 16 * 262144 * 128 * 2 bytes = 1 GiB
+    x = torch.randn((B, H, N, d), device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    perm = torch.arange(N, dtype=torch.int32, device=dev)
+    for _ in range(steps):
+        bsa.permute_tokens(x, perm, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    print(json.dumps({"copy_calibration": {"bytes_read": x.numel() * 2, "bytes_written": y.numel() * 2,
+                                           "launches": steps}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +201,9 @@ def main():
     ap.add_argument("--config", default="wan480", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="hunyuan720", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (identity token permutation of "
+                         "1 GiB of bf16 rows) to calibrate hardware byte counters")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -196,6 +215,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     bsa.load()
+    if a.copy_calibration:
+        copy_calibration(dev, a.steps)
+        return
 
     w = WORKLOADS[a.config]
     if w.order != "raster":

@@ -182,7 +182,8 @@ int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes, const float
 }
 
 size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb, const bsa_blocks* qb) {
-  if (qb == nullptr || B <= 0 || H <= 0 || nqb < 0) return 0;
+  (void)qb;
+  if (B <= 0 || H <= 0 || nqb < 0) return 0;
   return round256(sizeof(int32_t) * (size_t)B * H * (nqb + 1));
 }
 
@@ -200,7 +201,7 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void*
   if (int e = make_blocks(kb, block, n_valid, "key blocks", bk)) return e;
   if (kv_stride < 0 || (bk.nblocks > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_fwd: bad kv_stride");
   const size_t need = bsa_block_sparse_attn_fwd_workspace(B, H, bq.nblocks, qb);
-  if (need > 0 && (ws == nullptr || ws_bytes < need))
+  if (ws == nullptr || ws_bytes < need)
     return fail(BSA_ENOSPC, "attn_fwd: workspace %zu bytes < %zu", ws_bytes, need);
   const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return hip_status(bsa::launch_attn_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -45,6 +45,7 @@ struct AttnArgs {
   int N, n_valid, nqb, nkb;
   Blocks qb, kb;
   const int32_t* tile_base;   // variable query blocks: [BH][nqb + 1] tile prefix
+  const int32_t* order;       // uniform query blocks: [BH][nqb] processing order
   int tiles;                  // grid tiles per (b, h)
   const int32_t* kv_count;
   const int32_t* kv_index;
@@ -183,8 +184,29 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   // ---- direct-to-LDS issue of one K or V tile. Row r comes from token
   // ks + r (uniform) or tk[r] (gathered); rows >= kl re-load row 0 (finite
   // data whose keys are masked to -inf).
+  // Lane byte offsets of the loads of a full 64-row chunk of consecutive
+  // tokens (loop invariant): row r = ins*RPI + lane/PPR, swizzled piece.
+  int loff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wave * NI + i) * RPI + lane / PPR;
+    loff[i] = r * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4);
+  }
   auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
     const unsigned char* src = isv ? vh : kh;
+    if (!KVAR && kl == 64) {
+      const unsigned char* base = src + (size_t)ks * ROWB;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ins = wave * NI + i;
+        const unsigned char* g = base + loff[i];
+        if (isv)
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Vp + ins * 1024, 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Kp + ins * 1024, 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int ins = wave * NI + i;
@@ -193,7 +215,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       const int rr = r < kl ? r : 0;
       const int t = KVAR ? tk[rr] : ks + rr;
       const unsigned char* g = src + (size_t)t * ROWB + ((p ^ swz<D>(r & 15)) << 4);
-      // separate call sites: each DMA names its own destination tile
+      // separate call sites: each load names its own destination tile
       if (isv)
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Vp + ins * 1024, 16, 0, 0);
       else
@@ -415,7 +437,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
 
   // Flat id -> (head, tile): consecutive workgroups are dealt round-robin to
   // the 8 XCDs; remap so each XCD works on a contiguous range of tiles (one or
-  // two heads), which keeps a head's K/V hot in that XCD's L2.
+  // two heads), so the tiles sharing an XCD's L2 are neighbours in the
+  // processing order and tend to keep the same key blocks.
   int L = blockIdx.x;
   {
     const int total = gridDim.x, per = total >> 3, rem = total & 7;
@@ -427,7 +450,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
 
   int I, qs, ql;
   if (!QVAR) {
-    I = tile;
+    if (tile >= a.nqb) return;
+    I = a.order ? a.order[(size_t)bh * a.nqb + tile] : tile;
     a.qb.get(bh, I, qs, ql);
   } else {
     const int32_t* tb = a.tile_base + (size_t)bh * (a.nqb + 1);
@@ -446,6 +470,58 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   if (ql <= 0) return;
   attn_tile<D, KVAR>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
+}
+
+// Processing order of uniform query blocks: query blocks of one head are
+// sorted (counting sort) by the mean index of their kept key blocks, so that
+// the workgroups running at the same time on an XCD walk overlapping key
+// blocks and find them in that XCD's L2. Affects scheduling only.
+__global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__ kv_count,
+                                                     const int32_t* __restrict__ kv_index,
+                                                     int kv_stride, int nqb, int nkb,
+                                                     int32_t* __restrict__ order) {
+  extern __shared__ int sm[];
+  int* cnt = sm;              // [nkb + 1] bucket counts, then cursors
+  int* key = sm + nkb + 1;    // [nqb]
+  __shared__ int part[257];
+  const int bh = blockIdx.x;
+  for (int b = threadIdx.x; b <= nkb; b += 256) cnt[b] = 0;
+  __syncthreads();
+  for (int I = threadIdx.x; I < nqb; I += 256) {
+    const size_t row = (size_t)bh * nqb + I;
+    const int c = kv_count[row];
+    const int32_t* ids = kv_index + row * kv_stride;
+    long long sum = 0;
+    for (int j = 0; j < c; ++j) sum += ids[j];
+    const int k = c > 0 ? (int)(sum / c) : 0;
+    key[I] = k;
+    atomicAdd(&cnt[k], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the bucket counts
+  const int per = (nkb + 1 + 255) / 256;
+  const int b0 = threadIdx.x * per, b1 = min(nkb + 1, b0 + per);
+  int loc = 0;
+  for (int b = b0; b < b1; ++b) loc += cnt[b];
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int run = part[threadIdx.x];
+  for (int b = b0; b < b1; ++b) {
+    const int v = cnt[b];
+    cnt[b] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int I = threadIdx.x; I < nqb; I += 256) order[(size_t)bh * nqb + atomicAdd(&cnt[key[I]], 1)] = I;
 }
 
 // Tile prefix over query blocks of any length: tb[bh][I] = sum_{I'<I} ceil(len/64).
@@ -516,11 +592,18 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const bool qvar = qb.start != nullptr;
   const bool kvar = kb.start != nullptr;
   a.tile_base = tile_ws;
+  a.order = nullptr;
   if (qvar) {
     tile_base_kernel<<<BH, 256, 0, s>>>(qb, tile_ws);
     a.tiles = (N + 63) / 64 + qb.nblocks;
   } else {
     a.tiles = qb.nblocks;
+    const size_t lds = sizeof(int) * ((size_t)kb.nblocks + 1 + qb.nblocks);
+    if (lds <= 64 * 1024) {
+      int32_t* order = tile_ws;
+      qorder_kernel<<<BH, 256, lds, s>>>(kv_count, kv_index, kv_stride, qb.nblocks, kb.nblocks, order);
+      a.order = order;
+    }
   }
   const long long grid = (long long)BH * a.tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;

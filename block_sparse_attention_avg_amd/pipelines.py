@@ -1,0 +1,93 @@
+"""Composed hot paths built from the C-ABI calls (argument marshalling only).
+
+``fractal_sta_attention`` -- NABLA summary, Metodologia sections 1-3: tokens
+are reordered by fractal flattening, the content-adaptive CDF mask is built
+on the patch blocks and OR'd with the static sliding-tile window, attention
+runs over the kept patch tiles and the output is put back in raster order.
+
+``semantic_attention`` -- Sparse VideoGen2 summary, Metodologia A-C: Q and K
+are clustered with k-means, tokens are permuted cluster-contiguously, the
+centroid top-p rule selects key clusters per query cluster, attention runs
+over the variable-size cluster blocks and the output is inverse-permuted.
+
+Every arithmetic step runs in libbsa's HIP kernels; this module only chains
+the calls and keeps the intermediate tensors.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import torch
+
+from . import (Blocks, block_sparse_attn_fwd, build_block_mask, build_centroid_mask,
+               cluster_order, fractal_order, kmeans, permute_tokens, unpermute_tokens)
+
+
+@dataclasses.dataclass
+class FractalLayout:
+    """Fractal order of a T x Hl x Wl latent video with P x P patches, on the device."""
+    perm: torch.Tensor          # int32 [N]
+    blocks: Blocks              # one block per patch
+    grid: Tuple[int, int, int]  # (T, ceil(Hl/P), ceil(Wl/P)) block grid
+    coords: torch.Tensor        # int32 [nblocks, 3] (host)
+
+
+def fractal_layout(T: int, Hl: int, Wl: int, P: int, N: int, device) -> FractalLayout:
+    perm, st, ln, co = fractal_order(T, Hl, Wl, P, N)
+    grid = (T, -(-Hl // P), -(-Wl // P))
+    return FractalLayout(perm.to(device), Blocks(st.to(device), ln.to(device)), grid, co)
+
+
+def fractal_sta_attention(q, k, v, layout: FractalLayout, thr: float,
+                          radius: Optional[Tuple[int, int, int]] = (1, 2, 2),
+                          n_valid: Optional[int] = None, return_mask: bool = False):
+    """Reorder -> CDF mask (OR window) -> block-sparse attention -> inverse reorder."""
+    qp = permute_tokens(q, layout.perm)
+    kp = permute_tokens(k, layout.perm)
+    vp = permute_tokens(v, layout.perm)
+    window = None if radius is None else (*layout.grid, *radius)
+    cnt, idx = build_block_mask(qp, kp, thr, window=window, n_valid=n_valid,
+                                qb=layout.blocks, kb=layout.blocks)
+    op = block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=n_valid,
+                               qb=layout.blocks, kb=layout.blocks)
+    o = unpermute_tokens(op, layout.perm)
+    return (o, cnt, idx) if return_mask else o
+
+
+@dataclasses.dataclass
+class SemanticState:
+    """Intermediate results of the semantic path (all on the device)."""
+    cq: torch.Tensor
+    nq: torch.Tensor
+    ck: torch.Tensor
+    nk: torch.Tensor
+    perm_q: torch.Tensor
+    perm_k: torch.Tensor
+    qblocks: Blocks
+    kblocks: Blocks
+    kv_count: torch.Tensor
+    kv_index: torch.Tensor
+
+
+def semantic_attention(q, k, v, Cq: int, Ck: int, iters: int, top_p: float,
+                       uq: torch.Tensor, uk: torch.Tensor, n_valid: Optional[int] = None,
+                       return_state: bool = False):
+    """k-means(Q), k-means(K) -> cluster order -> centroid top-p -> attention -> inverse."""
+    N = q.shape[2]
+    n_valid = N if n_valid is None else n_valid
+    cq, aq, nq = kmeans(q, Cq, iters, uq, n_valid)
+    ck, ak, nk = kmeans(k, Ck, iters, uk, n_valid)
+    pq, sq, lq = cluster_order(aq, Cq, n_valid)
+    pk, sk, lk = cluster_order(ak, Ck, n_valid)
+    qp = permute_tokens(q, pq)
+    kp = permute_tokens(k, pk)
+    vp = permute_tokens(v, pk)
+    cnt, idx = build_centroid_mask(cq, nq, ck, nk, top_p)
+    qb, kb = Blocks(sq, lq), Blocks(sk, lk)
+    op = block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=n_valid, qb=qb, kb=kb)
+    o = unpermute_tokens(op, pq)
+    if return_state:
+        return o, SemanticState(cq, nq, ck, nk, pq, pk, qb, kb, cnt, idx)
+    return o

@@ -177,8 +177,9 @@ int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes,
  * Block-sparse attention
  * ------------------------------------------------------------------------ */
 
-/* Workspace bytes needed by bsa_block_sparse_attn_fwd (0 for uniform
- * 64-token query blocks). */
+/* Workspace bytes needed by bsa_block_sparse_attn_fwd: int32 scratch of
+ * B*H*(nqb+1) entries (the processing order of the query blocks, or the tile
+ * table of variable-size query blocks). */
 size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
                                            const bsa_blocks* qb);
 
@@ -202,6 +203,10 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
  *             be valid key blocks (the caller's contract)
  *   scale     > 0, or <= 0 for 1/sqrt(d)
  *   ws        workspace of bsa_block_sparse_attn_fwd_workspace(...) bytes
+ *             (device, 4-byte aligned; contents are overwritten)
+ * Query blocks are scheduled grouped by the key blocks they keep (uniform
+ * blocks) so that concurrently running tiles share K/V in cache; the order
+ * does not change any output bit.
  */
 int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                               void* o, int B, int H, int N, int d, int n_valid,

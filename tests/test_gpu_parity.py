@@ -284,3 +284,68 @@ def test_hunyuan720_sampled(gpu_lib, part):
         assert bad == 0
     else:
         _attn_case(gpu_lib, w, q, k, v, [4, 19], 5)
+
+
+def _random_partition(rng, n, lens=(0, 1, 7, 17, 33, 64, 65, 100, 150, 230)):
+    st, ln, pos = [], [], 0
+    while pos < n:
+        L = int(min(rng.choice(lens), n - pos))
+        st.append(pos)
+        ln.append(L)
+        pos += L
+    return np.array(st, np.int32), np.array(ln, np.int32)
+
+
+@pytest.mark.parametrize("d,per_head", [(128, False), (64, True), (128, True)])
+def test_attn_variable_blocks_random(gpu_lib, d, per_head):
+    # query blocks of any length (tiled by 64 rows) and key blocks of any
+    # length (gathered into 64-row chunks), shared or per head
+    bsa = gpu_lib
+    H, N, nv = 3, 1100, 1037
+    rng = np.random.default_rng(d + per_head)
+    say(f"attention variable blocks d={d} per_head={per_head}")
+    x = rng.normal(size=(3, 1, H, N, d)).astype(np.float32)
+    x[:, :, :, nv:] = 0
+    q, k, v = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(3))
+    heads = range(H) if per_head else [0]
+    parts_q = [_random_partition(rng, nv) for _ in heads]
+    parts_k = [_random_partition(rng, nv) for _ in heads]
+    nqb = max(len(p[0]) for p in parts_q)
+    nkb = max(len(p[0]) for p in parts_k)
+
+    def pad(parts, nb):
+        st = np.zeros((len(parts), nb), np.int32)
+        ln = np.zeros((len(parts), nb), np.int32)
+        for i, (s, l) in enumerate(parts):
+            st[i, :len(s)], ln[i, :len(l)] = s, l
+            st[i, len(s):] = nv
+        return st, ln
+
+    qst, qln = pad(parts_q, nqb)
+    kst, kln = pad(parts_k, nkb)
+    keep = rng.random((H, nqb, nkb)) < 0.25
+    keep[:, :, 0] = True
+    keep[:, 3, :] = False           # a query block with nothing kept -> zero rows
+    cnt = keep.sum(2).astype(np.int32)
+    idx = np.full((H, nqb, nkb), -1, np.int32)
+    for h in range(H):
+        for i in range(nqb):
+            ids = np.nonzero(keep[h, i])[0]
+            idx[h, i, :len(ids)] = ids
+    if per_head:
+        qb = bsa.Blocks(torch.from_numpy(qst[None]).cuda(), torch.from_numpy(qln[None]).cuda())
+        kb = bsa.Blocks(torch.from_numpy(kst[None]).cuda(), torch.from_numpy(kln[None]).cuda())
+    else:
+        qb = bsa.Blocks(torch.from_numpy(qst[0]).cuda(), torch.from_numpy(qln[0]).cuda())
+        kb = bsa.Blocks(torch.from_numpy(kst[0]).cuda(), torch.from_numpy(kln[0]).cuda())
+    o = bsa.block_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(cnt[None]).cuda(),
+                                  torch.from_numpy(idx[None]).cuda(), n_valid=nv, qb=qb, kb=kb)
+    o = _np(o)
+    assert (o[:, :, nv:] == 0).all()
+    for h in range(H):
+        hi = h if per_head else 0
+        ref = oa.masked_attention(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), qst[hi], qln[hi],
+                                  kst[hi], kln[hi], keep[h])
+        _check_out(o[0, h], ref, np.arange(nv), f"head {h}")
+        s3, l3 = qst[hi][3], qln[hi][3]
+        assert (o[0, h, s3:s3 + l3] == 0).all()

@@ -1,0 +1,252 @@
+"""GPU parity of the reorder-based paths against the CPU reference (MI355X).
+
+  * fractal flattening + CDF mask OR sliding-tile window + attention over
+    variable-length patch blocks + inverse reorder (480p layer, 588 patches);
+  * k-means of Q and K, cluster-contiguous order, centroid top-p mask,
+    attention over variable-size cluster blocks, inverse permutation.
+
+Integer work (permutations, cluster order, sizes) is compared bit-exactly.
+Clusterings can differ from the reference's where distances nearly tie, so
+k-means is checked by what must hold for any correct run (nearest-centroid
+assignment w.r.t. the previous round's centroids, centroids equal to member
+means, seeds drawn by the D^2 rule) and the later stages run on the GPU's own
+clustering on both sides.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_avg_amd.pipelines as pl
+from gen import WORKLOADS, generate, kmeans_uniforms, token_coords
+from oracle import attention as oa
+from oracle import kmeans as ok
+from oracle import layout as ol
+from oracle import mask as om
+from tests.band import keep_from_lists, mask_mismatches
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=1)
+def _wan480():
+    w = WORKLOADS["wan480"]
+    return generate(w)
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_out(o_gpu, o_ref, rows, what):
+    d = np.abs(o_gpu[rows] - o_ref[rows])
+    say(f"  {what}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+    assert np.isfinite(o_gpu[rows]).all(), what
+    assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, what
+
+
+# ------------------------------------------------------------------ fractal + STA
+
+def test_permute_roundtrip_bit_exact(gpu_lib):
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_fractal_sta"]
+    q, _, _ = _wan480()
+    perm, st, ln, co = bsa.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
+    rp, _, _, _ = ol.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
+    assert np.array_equal(perm.numpy(), rp)
+    qd = q.cuda()
+    pd = perm.cuda()
+    y = bsa.permute_tokens(qd, pd)
+    assert torch.equal(y.cpu(), q[:, :, torch.from_numpy(rp)])
+    assert torch.equal(bsa.unpermute_tokens(y, pd), qd)
+    # per-head permutations
+    rng = np.random.default_rng(3)
+    ph = np.stack([rng.permutation(w.N) for _ in range(w.H)]).astype(np.int32)[None]
+    y2 = bsa.permute_tokens(qd, torch.from_numpy(ph).cuda()).cpu()
+    for h in (0, 7):
+        assert torch.equal(y2[0, h], q[0, h][torch.from_numpy(ph[0, h]).long()])
+
+
+def test_fractal_sta_path(gpu_lib):
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_fractal_sta"]
+    q, k, v = _wan480()
+    say("fractal + STA path, 480p layer")
+    lay = pl.fractal_layout(w.T, w.Hl, w.Wl, w.patch, w.N, "cuda")
+    o, cnt, idx = pl.fractal_sta_attention(q.cuda(), k.cuda(), v.cuda(), lay, w.thr,
+                                           radius=w.window, n_valid=w.n_valid, return_mask=True)
+    torch.cuda.synchronize()
+    o, cnt, idx = _np(o), cnt.cpu().numpy(), idx.cpu().numpy()
+    perm, st, ln, coords = ol.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
+    derived = ol.block_coords_from_tokens(token_coords(w.T, w.Hl, w.Wl), perm, st, ln, w.patch)
+    win = ol.window_blocks(derived, derived, *w.window)
+    nb = len(st)
+    assert (o[:, :, w.n_valid:] == 0).all()
+    rng = np.random.default_rng(0)
+    for h in (0, 5, 11):
+        keep = keep_from_lists(cnt[0, h], idx[0, h], nb)
+        qh, kh, vh = _np(q[0, h]), _np(k[0, h]), _np(v[0, h])
+        ref_keep, P = om.block_mask(qh[perm], kh[perm], st, ln, st, ln, w.thr, window=win)
+        assert (keep >= win).all(), "window bits must be set"
+        bad = mask_mismatches(P, w.thr, keep, window=win)
+        say(f"  head {h}: kept {keep.sum()}/{keep.size} (window alone {win.sum()}), "
+            f"differing bits {(keep != ref_keep).sum()}, sure-bit mismatches {bad}")
+        assert bad == 0
+        blocks = sorted(set(rng.choice(nb, 12, replace=False).tolist()) | {0, nb - 1})
+        ref = oa.permuted_attention(qh, kh, vh, perm, perm, st, ln, st, ln, keep, blocks=blocks)
+        rows = perm[np.concatenate([np.arange(st[b], st[b] + ln[b]) for b in blocks])]
+        _check_out(o[0, h], ref, rows, f"head {h} ({len(blocks)} patch blocks)")
+
+
+def test_window_only_mask_is_static_sta(gpu_lib):
+    # thr = 0 with the window keeps everything; with thr = 1 the kept set is
+    # the window plus each row's heaviest block.
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_fractal_sta"]
+    q, k, v = _wan480()
+    lay = pl.fractal_layout(w.T, w.Hl, w.Wl, w.patch, w.N, "cuda")
+    qp = bsa.permute_tokens(q.cuda(), lay.perm)
+    kp = bsa.permute_tokens(k.cuda(), lay.perm)
+    cnt, idx = bsa.build_block_mask(qp, kp, 1.0, window=(*lay.grid, *w.window), n_valid=w.n_valid,
+                                    qb=lay.blocks, kb=lay.blocks)
+    cnt = cnt.cpu().numpy()
+    perm, st, ln, coords = ol.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
+    win = ol.window_blocks(coords, coords, *w.window)
+    wc = win.sum(1)
+    assert ((cnt[0] == wc[None]) | (cnt[0] == wc[None] + 1)).all()
+
+
+# ------------------------------------------------------------------ semantic clustering
+
+@functools.lru_cache(maxsize=1)
+def _semantic():
+    w = WORKLOADS["wan480_semantic"]
+    q, k, v = _wan480()
+    uq = torch.from_numpy(kmeans_uniforms(w.B, w.H, w.Cq, stream=0))
+    uk = torch.from_numpy(kmeans_uniforms(w.B, w.H, w.Ck, stream=1))
+    return w, q, k, v, uq, uk
+
+
+def _d2(x, c):
+    return ok.sq_dists(x, c)
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_kmeans_seeding_rule(gpu_lib, which):
+    bsa = gpu_lib
+    w, q, k, v, uq, uk = _semantic()
+    x, C, u = (q, w.Cq, uq) if which == "q" else (k, w.Ck, uk)
+    say(f"k-means++ seeding on {which}, C={C}")
+    cent, a, sizes = bsa.kmeans(x.cuda(), C, 0, u.cuda(), n_valid=w.n_valid)
+    cent = cent.cpu().numpy().astype(np.float64)
+    for h in (0, 9):
+        xh = _np(x[0, h])[:w.n_valid]
+        uh = u[0, h].numpy().astype(np.float64)
+        # every seed is a token vector; recover it and check the D^2 draw
+        d2 = None
+        for r in range(C):
+            hits = np.nonzero((xh == cent[0, h, r]).all(1))[0]
+            assert len(hits) >= 1, (h, r)
+            if r == 0:
+                assert min(int(np.floor(uh[0] * w.n_valid)), w.n_valid - 1) in hits
+                d2 = ((xh - cent[0, h, 0]) ** 2).sum(1)
+                continue
+            cs = np.cumsum(d2)
+            target = uh[r] * cs[-1]
+            tol = 1e-5 * cs[-1]
+            ok_idx = [i for i in hits if cs[i] - d2[i] <= target + tol and cs[i] >= target - tol]
+            assert ok_idx, (h, r)
+            d2 = np.minimum(d2, ((xh - cent[0, h, r]) ** 2).sum(1))
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_kmeans_lloyd_invariants(gpu_lib, which):
+    bsa = gpu_lib
+    w, q, k, v, uq, uk = _semantic()
+    x, C, u = (q, w.Cq, uq) if which == "q" else (k, w.Ck, uk)
+    say(f"k-means Lloyd invariants on {which}, C={C}")
+    xd, ud = x.cuda(), u.cuda()
+    c9, a9, _ = bsa.kmeans(xd, C, w.kmeans_iters - 1, ud, n_valid=w.n_valid)
+    c10, a10, s10 = bsa.kmeans(xd, C, w.kmeans_iters, ud, n_valid=w.n_valid)
+    c10b, a10b, s10b = bsa.kmeans(xd, C, w.kmeans_iters, ud, n_valid=w.n_valid)
+    assert torch.equal(c10, c10b) and torch.equal(a10, a10b), "k-means must be deterministic"
+    c9, c10 = c9.cpu().numpy().astype(np.float64), c10.cpu().numpy().astype(np.float64)
+    a10, s10 = a10.cpu().numpy(), s10.cpu().numpy()
+    assert (a10[:, :, w.n_valid:] == -1).all()
+    for h in (0, 4, 11):
+        xh = _np(x[0, h])[:w.n_valid]
+        ah = a10[0, h, :w.n_valid]
+        assert np.array_equal(np.bincount(ah, minlength=C), s10[0, h])
+        # the last assignment is nearest w.r.t. the previous centroids (fp32 ties allowed)
+        D = _d2(xh, c9[0, h])
+        mine = D[np.arange(len(ah)), ah]
+        assert (mine <= D.min(1) * (1 + 2e-5) + 1e-3).all(), h
+        # centroids are the means of their members (empty clusters keep their value)
+        for c in range(C):
+            if s10[0, h, c]:
+                ref = xh[ah == c].mean(0)
+                np.testing.assert_allclose(c10[0, h, c], ref, rtol=1e-5, atol=1e-4 * np.abs(ref).max())
+        say(f"  head {h}: sizes min {s10[0, h].min()} max {s10[0, h].max()}, "
+            f"inertia {((xh - c10[0, h][ah]) ** 2).sum():.6e}")
+
+
+def test_semantic_path(gpu_lib):
+    bsa = gpu_lib
+    w, q, k, v, uq, uk = _semantic()
+    say("semantic permutation path, 480p layer")
+    o, st = pl.semantic_attention(q.cuda(), k.cuda(), v.cuda(), w.Cq, w.Ck, w.kmeans_iters, w.top_p,
+                                  uq.cuda(), uk.cuda(), n_valid=w.n_valid, return_state=True)
+    torch.cuda.synchronize()
+    o = _np(o)
+    assert (o[:, :, w.n_valid:] == 0).all()
+    cnt, idx = st.kv_count.cpu().numpy(), st.kv_index.cpu().numpy()
+    cq, ck = st.cq.cpu().numpy(), st.ck.cpu().numpy()
+    nq, nk = st.nq.cpu().numpy(), st.nk.cpu().numpy()
+    pq, pk = st.perm_q.cpu().numpy(), st.perm_k.cpu().numpy()
+    qs, ql = st.qblocks.start.cpu().numpy(), st.qblocks.length.cpu().numpy()
+    ks, kl = st.kblocks.start.cpu().numpy(), st.kblocks.length.cpu().numpy()
+    rng = np.random.default_rng(1)
+    eff = tot = 0.0
+    for h in (0, 6, 11):
+        # cluster order: bit-exact stable sort of the GPU's own assignment
+        aq = np.empty(w.n_valid, np.int64)
+        ak = np.empty(w.n_valid, np.int64)
+        for c in range(w.Cq):
+            aq[pq[0, h, qs[0, h, c]:qs[0, h, c] + ql[0, h, c]]] = c
+        for c in range(w.Ck):
+            ak[pk[0, h, ks[0, h, c]:ks[0, h, c] + kl[0, h, c]]] = c
+        rq, rqs, rql = ok.cluster_order(aq, w.Cq, w.N)
+        rk, rks, rkl = ok.cluster_order(ak, w.Ck, w.N)
+        assert np.array_equal(rq, pq[0, h]) and np.array_equal(rqs, qs[0, h]) and np.array_equal(rql, ql[0, h])
+        assert np.array_equal(rk, pk[0, h]) and np.array_equal(rks, ks[0, h]) and np.array_equal(rkl, kl[0, h])
+        assert np.array_equal(rql, nq[0, h]) and np.array_equal(rkl, nk[0, h])
+        # centroid mask against the reference rule on the GPU's centroids
+        keep = keep_from_lists(cnt[0, h], idx[0, h], w.Ck)
+        ref_keep, W = om.centroid_mask(cq[0, h], nq[0, h], ck[0, h], nk[0, h], w.top_p)
+        valid = nk[0, h] > 0
+        rows = nq[0, h] > 0
+        bad = mask_mismatches(W[rows][:, valid], 1.0 - w.top_p, keep[rows][:, valid])
+        assert not keep[:, ~valid].any() and not keep[~rows].any()
+        say(f"  head {h}: kept {keep.sum()}/{keep.size} cluster pairs, differing {(keep != ref_keep).sum()}, "
+            f"sure-bit mismatches {bad}")
+        assert bad == 0
+        # attention over variable-size clusters, inverse-permuted
+        qh, kh, vh = _np(q[0, h]), _np(k[0, h]), _np(v[0, h])
+        blocks = sorted(rng.choice(np.nonzero(rows)[0], 6, replace=False).tolist())
+        ref = oa.permuted_attention(qh, kh, vh, rq, rk, rqs, rql, rks, rkl, keep, blocks=blocks)
+        rows_tok = rq[np.concatenate([np.arange(rqs[b], rqs[b] + rql[b]) for b in blocks])]
+        _check_out(o[0, h], ref, rows_tok, f"head {h} ({len(blocks)} query clusters)")
+        eff += float((rql[:, None] * rkl[None, :] * keep).sum())
+        tot += float(w.n_valid) ** 2
+    say(f"  kept token-pair density {eff / tot:.4f}")
