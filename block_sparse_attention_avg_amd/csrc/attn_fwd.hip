@@ -117,19 +117,29 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 }  // namespace
 
-// One query tile. The K and V tiles are passed as distinct __restrict__ LDS
-// pointers: after inlining, the compiler can then tell the two direct-to-LDS
-// load streams apart and leaves the waits to the explicit vmcnt counts below
-// instead of draining every load before each LDS read.
+// One query tile. K and V tiles are separate LDS arrays so the compiler can
+// tell the two direct-to-LDS load streams apart; all waits on those loads are
+// explicit vmcnt counts.
+//
+// Software pipeline (per iteration c, every wave):
+//   region A:  S(c+1) = K(c+1) Q^T on MFMA, interleaved with the VALU softmax
+//              of S(c) (independent work: the MFMA pipe and the VALU overlap
+//              inside the wave);
+//   region B:  O^T += V(c)^T P(c)^T on MFMA.
+// Loads: K(c+2) is issued as soon as every wave has finished region A, V(c+1)
+// as soon as every wave has finished region B. Each iteration issues exactly
+// one K and one V tile load (after the last chunk they re-load rows of the
+// current chunk into the free buffer, and the extra S is discarded), so the
+// outstanding-load accounting is the same on every path.
 template <int D, bool KVAR>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
-                                          lds_u8* Kp, lds_u8* Vp,
-                                          int* tok, int* chunk_rows) {
+                                          lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
   constexpr int ROWB = D * 2;                  // bytes per K/V row
   constexpr int TILE = 64 * ROWB;              // bytes per K or V tile
   constexpr int NI = TILE / 1024 / 2;          // direct-to-LDS loads per wave per tile
   constexpr int RPI = 1024 / ROWB;             // rows per load instruction
   constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
+  constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -181,17 +191,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
     }
 
-  // ---- direct-to-LDS issue of one K or V tile. Row r comes from token
-  // ks + r (uniform) or tk[r] (gathered); rows >= kl re-load row 0 (finite
-  // data whose keys are masked to -inf).
-  // Lane byte offsets of the loads of a full 64-row chunk of consecutive
-  // tokens (loop invariant): row r = ins*RPI + lane/PPR, swizzled piece.
+  // Lane byte offsets of the loads of a full chunk of 64 consecutive tokens.
   int loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * RPI + lane / PPR;
     loff[i] = r * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4);
   }
+  // Direct-to-LDS issue of one K or V tile. Row r comes from token ks + r
+  // (uniform blocks) or tk[r] (gathered); rows >= kl re-load row 0 (finite
+  // data whose keys are masked to -inf).
   auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
     const unsigned char* src = isv ? vh : kh;
     if (!KVAR && kl == 64) {
@@ -213,7 +222,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       const int r = ins * RPI + lane / PPR;
       const int p = lane % PPR;
       const int rr = r < kl ? r : 0;
-      const int t = KVAR ? tk[rr] : ks + rr;
+      int t = KVAR ? tk[rr] : ks + rr;
+      if (KVAR) t = (unsigned)t < (unsigned)a.N ? t : 0;   // never leave the head's rows
       const unsigned char* g = src + (size_t)t * ROWB + ((p ^ swz<D>(r & 15)) << 4);
       // separate call sites: each load names its own destination tile
       if (isv)
@@ -223,27 +233,31 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     }
   };
 
-  // ---- chunk walk.
+  // ---- chunk descriptors
   // Uniform blocks: chunk c is key block list[c]; the list is read 64
-  // entries at a time into a register window (one vector load per 64
-  // chunks), each entry taken with readlane.
+  // entries at a time into a register window, each entry taken by readlane.
   int lst = 0;
   auto chunk_uniform = [&](int c, int& ks, int& kl) {
     if (c >= cnt) { ks = 0; kl = 0; return; }
     if ((c & 63) == 0) lst = list[min(c + lane, cnt - 1)];
-    const int J = __builtin_amdgcn_readlane(lst, c & 63);
+    int J = __builtin_amdgcn_readlane(lst, c & 63);
+    J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;   // invalid ids stay in bounds
     ks = J * 64;                       // uniform 64-token key blocks
     kl = min(64, a.n_valid - ks);
   };
-  // Gathered blocks: wave 0 writes the token indices of the next chunk to
-  // tok[buf] with a cursor (list entry e_cur, offset off_cur).
+  // Gathered blocks: wave 0 writes the token indices of chunk c to the ring
+  // slot tok[c & 3] with a cursor (list entry e_cur, offset off_cur).
   int e_cur = 0, off_cur = 0;
-  auto next_chunk = [&](int buf) {   // wave 0 only
+  auto next_chunk = [&](int slot) {   // wave 0 only
     int rows = 0;
     while (rows == 0 && e_cur < cnt) {
       const int ent = e_cur + lane;
       int ks = 0, n = 0;
-      if (ent < cnt) a.kb.get(bh, list[ent], ks, n);
+      if (ent < cnt) {
+        const int J = list[ent];
+        if ((unsigned)J < (unsigned)a.nkb) a.kb.get(bh, J, ks, n);   // invalid ids: empty
+        n = max(n, 0);
+      }
       int incl = n;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -261,7 +275,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       const int src = lo & 63;
       const int excl_src = __shfl(incl, src) - __shfl(n, src);
       const int ks_src = __shfl(ks, src);
-      if (lane < rows) tok[buf * 64 + lane] = ks_src + (pos - excl_src);
+      if (lane < rows) tok[slot * 64 + lane] = ks_src + (pos - excl_src);
       const int pend = off_cur + rows;
       int lo2 = 0, hi2 = 64;
       while (lo2 < hi2) {
@@ -276,94 +290,105 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
         e_cur += lo2;
       }
     }
-    if (lane == 0) chunk_rows[buf] = rows;
+    if (lane == 0) chunk_rows[slot] = rows;
   };
   auto chunk_info = [&](int c, int& ks, int& kl) {
     if (KVAR) {
       ks = 0;
-      kl = __builtin_amdgcn_readfirstlane(chunk_rows[c & 1]);
+      kl = __builtin_amdgcn_readfirstlane(chunk_rows[c & 3]);
     } else {
       chunk_uniform(c, ks, kl);
     }
   };
 
-  if (KVAR) {
-    if (wave == 0) next_chunk(0);
-    wait_lgkm0();
-    wg_barrier();
-  }
-  int ks, kl;
-  chunk_info(0, ks, kl);
-  if (kl > 0) {
-    issue_tile(false, ks, kl, tok);
-    issue_tile(true, ks, kl, tok);
-  }
-  for (int c = 0; kl > 0; ++c) {
-    if (KVAR && wave == 0) next_chunk((c + 1) & 1);
-    wait_vm<NI>();                 // own K(c) loads landed (V(c) may be in flight)
-    wait_lgkm0();
-    wg_barrier();                  // ... and every other wave's
-
-    // S^T = K Q^T
-    f32x16 sacc[2];
+  // S^T = K Q^T from the K tile into s
+  auto compute_s = [&](f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
         const bf16x8 ka = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], sacc[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], s[kb], 0, 0, 0);
       }
-    wg_barrier();                  // every wave is done reading K(c)
-    int ks_n, kl_n;
-    chunk_info(c + 1, ks_n, kl_n);
-    // The next chunk's loads are issued unconditionally (after the last chunk
-    // they re-load the current rows into the free buffer): a load issued on
-    // one path only makes the compiler drain every load before LDS reads.
-    const bool more = kl_n > 0;
-    const int ks_i = more ? ks_n : ks, kl_i = more ? kl_n : kl;
-    const int* tk_i = tok + (((more ? c + 1 : c)) & 1) * 64;
-    issue_tile(false, ks_i, kl_i, tk_i);
+  };
 
-    // online softmax; sacc[kb][r] is key 32kb + 8(r/4) + 4*half + r%4
+  // ---- prologue: descriptors of chunks 0 and 1, loads K0 V0, S(0), load K1
+  if (KVAR) {
+    if (wave == 0) {
+      next_chunk(0);
+      next_chunk(1);
+    }
+    wait_lgkm0();
+    wg_barrier();
+  }
+  int ks0, kl0, ks1, kl1;
+  chunk_info(0, ks0, kl0);
+  if (kl0 == 0) {                      // nothing kept: zero rows
+    ks1 = ks0; kl1 = kl0;
+  } else {
+    chunk_info(1, ks1, kl1);
+  }
+  f32x16 s_cur[2], s_nxt[2];
+  int kl = kl0;                        // rows of chunk c
+  int ks_c = ks0;
+  if (kl0 > 0) {
+    issue_tile(false, ks0, kl0, tok);
+    wait_vm<0>();                      // K0 landed
+    wg_barrier();
+    compute_s(s_cur);
+    wg_barrier();
+    {
+      const bool more = kl1 > 0;
+      issue_tile(false, more ? ks1 : ks0, more ? kl1 : kl0, tok + (more ? 1 : 0) * 64);
+    }
+    // V0 after K1: the loop relies on loads being outstanding in the order
+    // [K(c+1)] [V(c)] when an iteration starts
+    issue_tile(true, ks0, kl0, tok);
+  }
+  int ks_n = ks1, kl_n = kl1;          // chunk c+1
+
+  for (int c = 0; kl > 0; ++c) {
+    // descriptor of chunk c+2 (gathered: wave 0 fills ring slot (c+2)&3)
+    if (KVAR && wave == 0) next_chunk((c + 2) & 3);
+    // outstanding loads, oldest first: [K(c+1)] [V(c)]
+    wait_vm<NI>();                     // K(c+1) landed
+    wait_lgkm0();
+    wg_barrier();
+
+    // ---- region A: S(c+1) on MFMA || softmax(c) on VALU
+    compute_s(s_nxt);
     if (kl < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kl) sacc[kb][r] = -INFINITY;
+          if (key >= kl) s_cur[kb][r] = -INFINITY;
         }
     }
     float mloc = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
-    mloc = halves_max(mloc);
-    const float m_new = fmaxf(m_run, mloc * a.sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.sl2, -m_new));
-        sacc[kb][r] = p;
-        rs += p;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s_cur[kb][r]);
+    mloc = halves_max(mloc) * a.sl2;
+    const bool grow = mloc > m_run + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow)) {   // rare: move the reference max
+      const float m_new = grow ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
+      m_run = m_new;
     }
+    float rs = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -371,13 +396,30 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       for (int hh = 0; hh < 2; ++hh) {
         float tmp[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = sacc[kb][8 * hh + e];
+        for (int e = 0; e < 8; ++e) {
+          tmp[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][8 * hh + e], a.sl2, -m_run));
+          rs += tmp[e];
+        }
         pf[kb][hh] = pack8(tmp);
       }
+    l_run += rs;
 
-    wait_vm<NI>();                 // own V(c) loads landed (next K in flight)
+    wg_barrier();                      // every wave is done reading K(c+1)
+    int ks_2, kl_2;
+    chunk_info(c + 2, ks_2, kl_2);
+    {
+      // K(c+2); without a chunk c+2 a re-load of a chunk that has rows
+      // (c+1 if it exists, else c itself) into the free buffer
+      const int kc = kl_2 > 0 ? c + 2 : (kl_n > 0 ? c + 1 : c);
+      const int ks_k = kl_2 > 0 ? ks_2 : (kl_n > 0 ? ks_n : ks_c);
+      const int kl_k = kl_2 > 0 ? kl_2 : (kl_n > 0 ? kl_n : kl);
+      issue_tile(false, ks_k, kl_k, tok + (kc & 3) * 64);
+    }
+
+    // ---- region B: O^T += V(c)^T P(c)^T
+    // outstanding loads, oldest first: [V(c)] [K(c+2)]
+    wait_vm<NI>();                     // V(c) landed
     wg_barrier();
-    // O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -390,15 +432,23 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][hh], oacc[dg], 0, 0, 0);
         }
-    wg_barrier();                  // every wave is done reading V(c)
-    issue_tile(true, ks_i, kl_i, tk_i);
-    ks = ks_n;
-    kl = kl_n;
+    wg_barrier();                      // every wave is done reading V(c)
+    {
+      // V(c+1), or a re-load of chunk c's rows when there is no chunk c+1
+      const bool more = kl_n > 0;
+      const int vc = more ? c + 1 : c;
+      issue_tile(true, more ? ks_n : ks_c, more ? kl_n : kl, tok + (vc & 3) * 64);
+    }
+    // advance: chunk c+1 becomes current
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    ks_c = ks_n; kl = kl_n;
+    ks_n = ks_2; kl_n = kl_2;
   }
-  wait_vm<0>();                    // no load may still target LDS
+  wait_vm<0>();                        // no load may still target LDS
 
   // ---- epilogue: O = O^T / l, staged through the K tile (swizzled rows),
-  // stored as bf16 rows. No load is in flight here.
+  // stored as bf16 rows.
   const float lt = halves_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int orow = 32 * wave + l32;
@@ -432,8 +482,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = 64 * D * 2;
   __shared__ __align__(16) unsigned char Ks[TILE];
   __shared__ __align__(16) unsigned char Vs[TILE];
-  __shared__ int tok[2 * 64];
-  __shared__ int chunk_rows[2];
+  __shared__ int tok[4 * 64];
+  __shared__ int chunk_rows[4];
 
   // Flat id -> (head, tile): consecutive workgroups are dealt round-robin to
   // the 8 XCDs; remap so each XCD works on a contiguous range of tiles (one or
@@ -493,7 +543,8 @@ __global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__
     const int32_t* ids = kv_index + row * kv_stride;
     long long sum = 0;
     for (int j = 0; j < c; ++j) sum += ids[j];
-    const int k = c > 0 ? (int)(sum / c) : 0;
+    int k = c > 0 ? (int)(sum / c) : 0;
+    k = k < 0 ? 0 : (k > nkb ? nkb : k);   // invalid ids cannot leave the table
     key[I] = k;
     atomicAdd(&cnt[k], 1);
   }
