@@ -196,6 +196,8 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void*
   if (!q || !k || !v || !o || !kv_count || !kv_index) return fail(BSA_EINVAL, "attn_fwd: null pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BSA_EINVAL, "attn_fwd: q, k, v, o must be 16-byte aligned");
+  if ((long long)N * d * 2 > 0xFFFFFFFFLL)
+    return fail(BSA_EUNSUPPORTED, "attn_fwd: one head (N*d*2 bytes) must be below 4 GiB");
   bsa::Blocks bq, bk;
   if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
   if (int e = make_blocks(kb, block, n_valid, "key blocks", bk)) return e;

@@ -46,7 +46,8 @@ struct AttnArgs {
   Blocks qb, kb;
   const int32_t* tile_base;   // variable query blocks: [BH][nqb + 1] tile prefix
   const int32_t* order;       // uniform query blocks: [BH][nqb] processing order
-  int tiles;                  // grid tiles per (b, h)
+  int tiles;                  // tiles per (b, h)
+  int bh;                     // B * H
   const int32_t* kv_count;
   const int32_t* kv_index;
   int kv_stride;
@@ -63,12 +64,25 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+// Read-only for the whole kernel: uniform loads through it become scalar loads.
+typedef __attribute__((address_space(4))) const int32_t cint;
 
 // Swizzle of the 16-byte piece index inside a K/V tile row.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
   else return (r >> 1) & 7;
+}
+
+// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 word 3: 32-bit
+// data format); loads at lane offsets >= bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS (dst is the wave's
+// 1 KiB destination; lane l lands at dst + 16 l).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
 // s_waitcnt lgkmcnt(0) (vmcnt, expcnt unconstrained).
@@ -121,16 +135,22 @@ __device__ __forceinline__ float halves_sum(float x) {
 // tell the two direct-to-LDS load streams apart; all waits on those loads are
 // explicit vmcnt counts.
 //
-// Software pipeline (per iteration c, every wave):
-//   region A:  S(c+1) = K(c+1) Q^T on MFMA, interleaved with the VALU softmax
-//              of S(c) (independent work: the MFMA pipe and the VALU overlap
-//              inside the wave);
+// Software pipeline (iteration c, every wave):
+//   prep:      mask and row max of S(c); rare rescale of O;
+//   region A:  S(c+1) = K(c+1) Q^T on MFMA, interleaved instruction by
+//              instruction with exp2 / row sum / bf16 pack of S(c) on the
+//              VALU (independent work, so the two pipes overlap in one wave);
 //   region B:  O^T += V(c)^T P(c)^T on MFMA.
-// Loads: K(c+2) is issued as soon as every wave has finished region A, V(c+1)
-// as soon as every wave has finished region B. Each iteration issues exactly
-// one K and one V tile load (after the last chunk they re-load rows of the
-// current chunk into the free buffer, and the extra S is discarded), so the
-// outstanding-load accounting is the same on every path.
+// Loads: K(c+2) is issued once every wave has finished region A, V(c+1) once
+// every wave has finished region B. Each iteration issues exactly one K and
+// one V tile load (after the last chunk they re-load rows of a chunk that
+// exists into the free buffer, and the extra S is discarded), so the number
+// of loads in flight is the same on every path. The loop body is unrolled
+// twice so S(c) and S(c+1) swap registers instead of being copied.
+//
+// Loads go through buffer descriptors that end at the chunk's last row:
+// rows past it (a partial last block, gathered rows past the chunk) read as
+// zeros, so no clamping is needed and padding never reaches P V.
 template <int D, bool KVAR>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
                                           lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
@@ -140,9 +160,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   constexpr int RPI = 1024 / ROWB;             // rows per load instruction
   constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
   constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
+  constexpr uint32_t OOB = 0xFFFFFFF0u;        // lane offset past every descriptor: loads zeros
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const size_t head_off = (size_t)bh * a.N * D;
   const uint16_t* qh = a.q + head_off;
@@ -170,8 +192,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   float m_run = -INFINITY, l_run = 0.f;
 
   const size_t qrow = (size_t)bh * a.nqb + I;
-  const int cnt = __builtin_amdgcn_readfirstlane(a.kv_count[qrow]);
+  const int cnt = ((const cint*)a.kv_count)[qrow];
   const int32_t* list = a.kv_index + qrow * a.kv_stride;
+  const cint* slist = (const cint*)list;
 
   // ---- per-lane LDS offsets (loop invariant)
   // K operand of S^T: row 32kb + l32, piece 2c + half.
@@ -191,56 +214,51 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
     }
 
-  // Lane byte offsets of the loads of a full chunk of 64 consecutive tokens.
-  int loff[NI];
+  // Lane byte offsets of the loads of a full chunk of 64 consecutive rows.
+  uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * RPI + lane / PPR;
     loff[i] = r * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4);
   }
+  // Buffer descriptor over `rows` rows starting at row `ks` of a head.
+  auto desc = [&](const unsigned char* base, int ks, int rows) -> __amdgpu_buffer_rsrc_t {
+    return make_rsrc(base + (size_t)ks * ROWB, (uint32_t)rows * (uint32_t)ROWB);
+  };
   // Direct-to-LDS issue of one K or V tile. Row r comes from token ks + r
-  // (uniform blocks) or tk[r] (gathered); rows >= kl re-load row 0 (finite
-  // data whose keys are masked to -inf).
+  // (uniform blocks) or tk[r] (gathered); rows >= kl load zeros.
   auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
-    const unsigned char* src = isv ? vh : kh;
-    if (!KVAR && kl == 64) {
-      const unsigned char* base = src + (size_t)ks * ROWB;
+    uint32_t off[NI];
+    const __amdgpu_buffer_rsrc_t rs = KVAR ? desc(isv ? vh : kh, 0, a.N) : desc(isv ? vh : kh, ks, kl);
+    if constexpr (KVAR) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int ins = wave * NI + i;
-        const unsigned char* g = base + loff[i];
-        if (isv)
-          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Vp + ins * 1024, 16, 0, 0);
-        else
-          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Kp + ins * 1024, 16, 0, 0);
+        const int r = (wave * NI + i) * RPI + lane / PPR;
+        const int t = tk[r < kl ? r : 0];
+        off[i] = (r < kl && (unsigned)t < (unsigned)a.N)
+                     ? (uint32_t)t * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4)
+                     : OOB;
       }
-      return;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) off[i] = loff[i];
     }
+    // separate call sites: each load names its own destination tile
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int ins = wave * NI + i;
-      const int r = ins * RPI + lane / PPR;
-      const int p = lane % PPR;
-      const int rr = r < kl ? r : 0;
-      int t = KVAR ? tk[rr] : ks + rr;
-      if (KVAR) t = (unsigned)t < (unsigned)a.N ? t : 0;   // never leave the head's rows
-      const unsigned char* g = src + (size_t)t * ROWB + ((p ^ swz<D>(r & 15)) << 4);
-      // separate call sites: each load names its own destination tile
       if (isv)
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Vp + ins * 1024, 16, 0, 0);
+        dma16(rs, Vp + ins * 1024, off[i]);
       else
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, Kp + ins * 1024, 16, 0, 0);
+        dma16(rs, Kp + ins * 1024, off[i]);
     }
   };
 
   // ---- chunk descriptors
-  // Uniform blocks: chunk c is key block list[c]; the list is read 64
-  // entries at a time into a register window, each entry taken by readlane.
-  int lst = 0;
+  // Uniform blocks: chunk c is key block list[c] (scalar loads).
   auto chunk_uniform = [&](int c, int& ks, int& kl) {
     if (c >= cnt) { ks = 0; kl = 0; return; }
-    if ((c & 63) == 0) lst = list[min(c + lane, cnt - 1)];
-    int J = __builtin_amdgcn_readlane(lst, c & 63);
+    int J = slist[c];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;   // invalid ids stay in bounds
     ks = J * 64;                       // uniform 64-token key blocks
     kl = min(64, a.n_valid - ks);
@@ -293,7 +311,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     if (lane == 0) chunk_rows[slot] = rows;
   };
   auto chunk_info = [&](int c, int& ks, int& kl) {
-    if (KVAR) {
+    if constexpr (KVAR) {
       ks = 0;
       kl = __builtin_amdgcn_readfirstlane(chunk_rows[c & 3]);
     } else {
@@ -301,24 +319,63 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     }
   };
 
-  // S^T = K Q^T from the K tile into s
+  // ---- LDS operand reads
+  // K operand of S^T step j (k-step cc = j / 2, key half kb = j % 2)
+  auto k_read = [&](int j) -> bf16x8 {
+    const int cc = j >> 1, kb = j & 1;
+    const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
+  };
+  // V^T operand of PV step j (key half kb, 16-key group hh, channel group dg)
+  auto v_read = [&](int j) -> bf16x8 {
+    const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
+    const int base = (32 * kb + 16 * hh) * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int NS = D / 8;            // MFMA steps of S^T (and of PV)
+  constexpr int EPS = 32 / NS;         // softmax elements per step
+
+  // S^T = K Q^T from the K tile into s (prologue only)
   auto compute_s = [&](f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
+    for (int j = 0; j < NS; ++j) s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(j), qf[j >> 1], s[j & 1], 0, 0, 0);
+  };
+  // keys >= kl of a chunk get -inf
+  auto mask_tail = [&](f32x16* s, int kl_s) {
+    if (kl_s < 64) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
-        const bf16x8 ka = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kl_s) s[kb][r] = -INFINITY;
+        }
+    }
+  };
+  // row max in log2 units -> move the reference max when it grew by > TAU
+  auto settle_max = [&](float mx) {
+    const float mloc = halves_max(mx) * a.sl2;
+    const bool grow = mloc > m_run + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow)) {   // rare: rescale O and l
+      const float m_new = grow ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
+      m_run = m_new;
+    }
   };
 
-  // ---- prologue: descriptors of chunks 0 and 1, loads K0 V0, S(0), load K1
-  if (KVAR) {
+  // ---- prologue: descriptors of chunks 0 and 1, load K0, S(0), loads K1 V0
+  if constexpr (KVAR) {
     if (wave == 0) {
       next_chunk(0);
       next_chunk(1);
@@ -333,80 +390,72 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   } else {
     chunk_info(1, ks1, kl1);
   }
-  f32x16 s_cur[2], s_nxt[2];
-  int kl = kl0;                        // rows of chunk c
-  int ks_c = ks0;
-  if (kl0 > 0) {
-    issue_tile(false, ks0, kl0, tok);
-    wait_vm<0>();                      // K0 landed
-    wg_barrier();
-    compute_s(s_cur);
-    wg_barrier();
-    {
-      const bool more = kl1 > 0;
-      issue_tile(false, more ? ks1 : ks0, more ? kl1 : kl0, tok + (more ? 1 : 0) * 64);
-    }
-    // V0 after K1: the loop relies on loads being outstanding in the order
-    // [K(c+1)] [V(c)] when an iteration starts
-    issue_tile(true, ks0, kl0, tok);
-  }
+  f32x16 sA[2], sB[2];
+  int c = 0;
+  int kl = kl0, ks_c = ks0;            // chunk c
   int ks_n = ks1, kl_n = kl1;          // chunk c+1
 
-  for (int c = 0; kl > 0; ++c) {
-    // descriptor of chunk c+2 (gathered: wave 0 fills ring slot (c+2)&3)
-    if (KVAR && wave == 0) next_chunk((c + 2) & 3);
+  // One pipeline iteration; sc holds S(c) (masked, reference max settled),
+  // sn receives S(c+1).
+  auto iter = [&](f32x16* sc, f32x16* sn) -> bool {
+    int ks_2 = 0, kl_2 = 0;
+    if constexpr (KVAR) {
+      if (wave == 0) next_chunk((c + 2) & 3);   // ring slot of chunk c+2
+    } else {
+      chunk_uniform(c + 2, ks_2, kl_2);         // scalar load, lands by the barrier
+    }
     // outstanding loads, oldest first: [K(c+1)] [V(c)]
     wait_vm<NI>();                     // K(c+1) landed
     wait_lgkm0();
     wg_barrier();
+    if constexpr (KVAR) chunk_info(c + 2, ks_2, kl_2);
 
-    // ---- region A: S(c+1) on MFMA || softmax(c) on VALU
-    compute_s(s_nxt);
-    if (kl < 64) {
+    // ---- region A: S(c+1) on MFMA || P(c) = exp2(S(c) - m) on VALU.
+    // Step j: K read for step j+3, MFMA j, softmax elements of step j.
+    uint32_t pw[2][2][4];
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kl) s_cur[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
+      bf16x8 kr[4];
+      kr[0] = k_read(0);
+      kr[1] = k_read(1);
+      kr[2] = k_read(2);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if (j + 3 < NS) kr[(j + 3) & 3] = k_read(j + 3);
+        sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j & 3], qf[j >> 1], sn[j & 1], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < EPS; e += 2) {
+          const int el = j * EPS + e;            // element 0..31 of this lane
+          const int kb = el >> 4, r = el & 15;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], a.sl2, -m_run));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r + 1], a.sl2, -m_run));
+          rsum[el & 3] += x0;
+          rsum[(el + 1) & 3] += x1;
+          pw[kb][r >> 3][(r & 7) >> 1] = pack2(x0, x1);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s_cur[kb][r]);
-    mloc = halves_max(mloc) * a.sl2;
-    const bool grow = mloc > m_run + TAU;
-    if (__builtin_amdgcn_ballot_w64(grow)) {   // rare: move the reference max
-      const float m_new = grow ? mloc : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
-      m_run = m_new;
-    }
-    float rs = 0.f;
+    // keep the softmax in region A: without a use here the compiler sinks it
+    // past the barriers to its consumer, region B
+    asm volatile("" ::"v"(pw[0][0][0]), "v"(pw[0][0][1]), "v"(pw[0][0][2]), "v"(pw[0][0][3]),
+                 "v"(pw[0][1][0]), "v"(pw[0][1][1]), "v"(pw[0][1][2]), "v"(pw[0][1][3]),
+                 "v"(pw[1][0][0]), "v"(pw[1][0][1]), "v"(pw[1][0][2]), "v"(pw[1][0][3]),
+                 "v"(pw[1][1][0]), "v"(pw[1][1][1]), "v"(pw[1][1][2]), "v"(pw[1][1][3]),
+                 "v"(rsum[0]), "v"(rsum[1]), "v"(rsum[2]), "v"(rsum[3]));
+    l_run += (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float tmp[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          tmp[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][8 * hh + e], a.sl2, -m_run));
-          rs += tmp[e];
-        }
-        pf[kb][hh] = pack8(tmp);
-      }
-    l_run += rs;
+      for (int hh = 0; hh < 2; ++hh)
+        pf[kb][hh] = __builtin_bit_cast(bf16x8, (u32x4){pw[kb][hh][0], pw[kb][hh][1], pw[kb][hh][2], pw[kb][hh][3]});
 
     wg_barrier();                      // every wave is done reading K(c+1)
-    int ks_2, kl_2;
-    chunk_info(c + 2, ks_2, kl_2);
     {
       // K(c+2); without a chunk c+2 a re-load of a chunk that has rows
       // (c+1 if it exists, else c itself) into the free buffer
@@ -416,22 +465,30 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       issue_tile(false, ks_k, kl_k, tok + (kc & 3) * 64);
     }
 
-    // ---- region B: O^T += V(c)^T P(c)^T
+    // ---- region B: O^T += V(c)^T P(c)^T on MFMA || row max of S(c+1)
     // outstanding loads, oldest first: [V(c)] [K(c+2)]
     wait_vm<NI>();                     // V(c) landed
     wg_barrier();
+    mask_tail(sn, kl_n);
+    float mx = -INFINITY;
+    {
+      bf16x8 vr[4];
+      vr[0] = v_read(0);
+      vr[1] = v_read(1);
+      vr[2] = v_read(2);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < NS; ++j) {
+        if (j + 3 < NS) vr[(j + 3) & 3] = v_read(j + 3);
+        const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
+        oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j & 3], pf[kb][hh], oacc[dg], 0, 0, 0);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg) {
-          const int base = (32 * kb + 16 * hh) * ROWB;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][0]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][hh], oacc[dg], 0, 0, 0);
+        for (int e = 0; e < EPS; e += 2) {
+          const int el = j * EPS + e;
+          mx = fmaxf(mx, fmaxf(sn[el >> 4][el & 15], sn[el >> 4][(el & 15) + 1]));
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     wg_barrier();                      // every wave is done reading V(c)
     {
       // V(c+1), or a re-load of chunk c's rows when there is no chunk c+1
@@ -439,11 +496,40 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       const int vc = more ? c + 1 : c;
       issue_tile(true, more ? ks_n : ks_c, more ? kl_n : kl, tok + (vc & 3) * 64);
     }
+    settle_max(mx);                    // reference max for S(c+1)
     // advance: chunk c+1 becomes current
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     ks_c = ks_n; kl = kl_n;
     ks_n = ks_2; kl_n = kl_2;
+    ++c;
+    return kl > 0;
+  };
+
+  if (kl0 > 0) {
+    issue_tile(false, ks0, kl0, tok);
+    wait_vm<0>();                      // K0 landed
+    wg_barrier();
+    compute_s(sA);
+    wg_barrier();
+    {
+      const bool more = kl1 > 0;
+      issue_tile(false, more ? ks1 : ks0, more ? kl1 : kl0, tok + (more ? 1 : 0) * 64);
+    }
+    // V0 after K1: an iteration starts with loads outstanding in the order
+    // [K(c+1)] [V(c)]
+    issue_tile(true, ks0, kl0, tok);
+    mask_tail(sA, kl0);
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sA[kb][r]);
+      settle_max(mx);
+    }
+    for (;;) {
+      if (!iter(sA, sB)) break;
+      if (!iter(sB, sA)) break;
+    }
   }
   wait_vm<0>();                        // no load may still target LDS
 
@@ -485,14 +571,16 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ int tok[4 * 64];
   __shared__ int chunk_rows[4];
 
-  // Flat id -> (head, tile): consecutive workgroups are dealt round-robin to
-  // the 8 XCDs; remap so each XCD works on a contiguous range of tiles (one or
-  // two heads), so the tiles sharing an XCD's L2 are neighbours in the
-  // processing order and tend to keep the same key blocks.
+  // Flat id -> (head, tile). Consecutive workgroups are dealt round-robin to
+  // the 8 XCDs, so workgroup 8i + x is the i-th one XCD x runs; XCD x takes a
+  // contiguous range of the flattened (head, tile) order. A head's tiles then
+  // share one XCD's L2 (the same K/V block is not fetched into all eight L2s)
+  // and the tiles running together on an XCD come from one or two heads.
   int L = blockIdx.x;
   {
-    const int total = gridDim.x, per = total >> 3, rem = total & 7;
+    const int total = a.bh * a.tiles, per = total >> 3, rem = total & 7;
     const int x = L & 7, i = L >> 3;
+    if (i >= per + (x < rem ? 1 : 0)) return;
     L = x * per + min(x, rem) + i;
   }
   const int bh = L / a.tiles;
@@ -501,10 +589,10 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   int I, qs, ql;
   if (!QVAR) {
     if (tile >= a.nqb) return;
-    I = a.order ? a.order[(size_t)bh * a.nqb + tile] : tile;
+    I = a.order ? ((const cint*)a.order)[(size_t)bh * a.nqb + tile] : tile;
     a.qb.get(bh, I, qs, ql);
   } else {
-    const int32_t* tb = a.tile_base + (size_t)bh * (a.nqb + 1);
+    const cint* tb = (const cint*)a.tile_base + (size_t)bh * (a.nqb + 1);
     if (tile >= tb[a.nqb]) return;
     int lo = 0, hi = a.nqb - 1;
     while (lo < hi) {
@@ -522,13 +610,12 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   attn_tile<D, KVAR>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
 }
 
-// Processing order of uniform query blocks: query blocks of one head are
-// sorted (counting sort) by the mean index of their kept key blocks, so that
-// the workgroups running at the same time on an XCD walk overlapping key
-// blocks and find them in that XCD's L2. Affects scheduling only.
-__global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__ kv_count,
-                                                     const int32_t* __restrict__ kv_index,
-                                                     int kv_stride, int nqb, int nkb,
+// Processing order of uniform query blocks: longest first. The query blocks
+// of one head are sorted (counting sort) by descending number of kept key
+// blocks, so the long tiles start early and do not finish last; together with
+// the contiguous per-XCD ranges this keeps the XCDs busy until the end.
+// Affects scheduling only: every tile computes the same bits in any order.
+__global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__ kv_count, int nqb, int nkb,
                                                      int32_t* __restrict__ order) {
   extern __shared__ int sm[];
   int* cnt = sm;              // [nkb + 1] bucket counts, then cursors
@@ -538,13 +625,8 @@ __global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__
   for (int b = threadIdx.x; b <= nkb; b += 256) cnt[b] = 0;
   __syncthreads();
   for (int I = threadIdx.x; I < nqb; I += 256) {
-    const size_t row = (size_t)bh * nqb + I;
-    const int c = kv_count[row];
-    const int32_t* ids = kv_index + row * kv_stride;
-    long long sum = 0;
-    for (int j = 0; j < c; ++j) sum += ids[j];
-    int k = c > 0 ? (int)(sum / c) : 0;
-    k = k < 0 ? 0 : (k > nkb ? nkb : k);   // invalid ids cannot leave the table
+    const int c = kv_count[(size_t)bh * nqb + I];
+    const int k = nkb - (c < 0 ? 0 : (c > nkb ? nkb : c));   // descending count
     key[I] = k;
     atomicAdd(&cnt[k], 1);
   }
@@ -652,11 +734,12 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
     const size_t lds = sizeof(int) * ((size_t)kb.nblocks + 1 + qb.nblocks);
     if (lds <= 64 * 1024) {
       int32_t* order = tile_ws;
-      qorder_kernel<<<BH, 256, lds, s>>>(kv_count, kv_index, kv_stride, qb.nblocks, kb.nblocks, order);
+      qorder_kernel<<<BH, 256, lds, s>>>(kv_count, qb.nblocks, kb.nblocks, order);
       a.order = order;
     }
   }
-  const long long grid = (long long)BH * a.tiles;
+  a.bh = BH;
+  const long long grid = 8LL * (((long long)BH * a.tiles + 7) / 8);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
 #define BSA_ATTN(DD, QV, KV) attn_fwd_kernel<DD, QV, KV><<<(int)grid, 128, 0, s>>>(a)
   if (d == 128) {

@@ -204,9 +204,10 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
  *   scale     > 0, or <= 0 for 1/sqrt(d)
  *   ws        workspace of bsa_block_sparse_attn_fwd_workspace(...) bytes
  *             (device, 4-byte aligned; contents are overwritten)
- * Query blocks are scheduled grouped by the key blocks they keep (uniform
- * blocks) so that concurrently running tiles share K/V in cache; the order
- * does not change any output bit.
+ * Limits: one head of K or V (N*d*2 bytes) must stay below 4 GiB
+ * (BSA_EUNSUPPORTED otherwise).
+ * Uniform query blocks are scheduled longest first (most kept key blocks
+ * first, per head); the order does not change any output bit.
  */
 int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                               void* o, int B, int H, int N, int d, int n_valid,
