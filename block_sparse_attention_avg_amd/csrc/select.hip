@@ -11,7 +11,9 @@
 // so each lane streams a contiguous quarter of the channel vector). The R x nkb
 // fp32 score rows stay in LDS; the reduced map never touches HBM.
 //
-// Phase 2 -- selection, one wave per row. p_J = exp(s_J - max) in fp32.
+// Phase 2 -- selection, one wave per row (rows of up to 2048 key blocks are
+// held in registers, longer rows are streamed from LDS). p_J = exp(s_J - max)
+// in fp32.
 // Masses are converted to 2^-40 fixed point (m_J = floor(p_J * 2^40)) so that
 // every sum is exact and order-independent. The cut is found by an MSB-first
 // radix select over the 43-bit key (bits(p_J) << 13 | (8191 - J)): keys order
@@ -37,7 +39,143 @@ constexpr int kPasses = (kKeyBits + kDigit - 1) / kDigit;   // 6
 constexpr int kBins = 1 << kDigit;
 }  // namespace
 
-template <int D, int R>
+// Selection of one row with its elements held in registers (E per lane,
+// element j = lane + 64 t): the same exact radix select as the LDS path
+// below, but every pass streams registers instead of re-reading and
+// re-converting the scores. Writes the kept ids in ascending order and
+// returns their count (lane-uniform).
+template <int E>
+__device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float thr, int row,
+                                               const int32_t* ksz, const Window& win,
+                                               unsigned long long* h, int32_t* out, int lane) {
+  float e[E];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int j = lane + kWave * t;
+    e[t] = j < nkb ? sr[j] : -INFINITY;
+    mx = fmaxf(mx, e[t]);
+  }
+  mx = wave_max(mx);
+  unsigned long long key[E], m[E];
+  unsigned long long z = 0;
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int j = lane + kWave * t;
+    const float pj = j < nkb ? expf(e[t] - mx) : 0.f;   // in [0, 1]; exp(-inf) = 0
+    m[t] = (unsigned long long)(pj * 0x1p40f);
+    key[t] = ((unsigned long long)__float_as_uint(pj) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
+    z += m[t];
+  }
+  z = wave_sum_u64(z);
+  const double tt = ceil((double)thr * (double)z);
+  const unsigned long long tint = tt >= (double)z ? z : (unsigned long long)tt;
+
+  unsigned long long prefix = 0, below = 0;
+  bool done = false;
+  unsigned long long kstar = 0;
+  // a zero threshold keeps every block: k* = 0 without any pass
+#pragma unroll 1
+  for (int pass = 0; pass < kPasses && tint > 0; ++pass) {
+    const int shift = kDigit * (kPasses - 1 - pass);
+    if (pass == 2) {
+      // The cut lies among the keys that share the 16-bit prefix. When there
+      // are at most 64 of them, finish exactly with one candidate per lane:
+      // k* is the smallest candidate key whose inclusive cumulative mass
+      // (below + candidates with keys <= it) reaches the threshold.
+      int ncand = 0;
+#pragma unroll
+      for (int t = 0; t < E; ++t) ncand += __popcll(__ballot((key[t] >> (shift + kDigit)) == prefix));
+      if (ncand <= kWave) {
+        unsigned long long* slot = h;          // 64 x (key, mass) = 1 KiB of this wave's histogram
+        int at = 0;
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+          const bool c = (key[t] >> (shift + kDigit)) == prefix;
+          const unsigned long long bal = __ballot(c);
+          if (c) {
+            const int r = at + __popcll(bal & ((1ull << lane) - 1ull));
+            slot[2 * r] = key[t];
+            slot[2 * r + 1] = m[t];
+          }
+          at += __popcll(bal);
+        }
+        wave_lds_sync();
+        const unsigned long long ck = lane < ncand ? slot[2 * lane] : ~0ull;
+        unsigned long long through = below;
+        for (int i = 0; i < ncand; ++i) {
+          const unsigned long long ki = slot[2 * i], mi = slot[2 * i + 1];   // same address in every lane
+          through += ki <= ck ? mi : 0ull;
+        }
+        const bool ok = lane < ncand && through >= tint;
+        // smallest qualifying key; some candidate always qualifies since
+        // below + all candidate mass >= the threshold
+        unsigned long long best = ok ? ck : ~0ull;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const unsigned long long other = __shfl_xor(best, o);
+          best = other < best ? other : best;
+        }
+        kstar = best;
+        done = true;
+        wave_lds_sync();
+        break;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBins / kWave; ++q) h[lane * (kBins / kWave) + q] = 0;
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+      if ((key[t] >> (shift + kDigit)) == prefix && m[t]) atomicAdd(&h[(key[t] >> shift) & (kBins - 1)], m[t]);
+    wave_lds_sync();
+    // lane owns bins [4*lane, 4*lane+4)
+    unsigned long long hv[kBins / kWave];
+    unsigned long long loc = 0;
+#pragma unroll
+    for (int q = 0; q < kBins / kWave; ++q) {
+      hv[q] = h[lane * (kBins / kWave) + q];
+      loc += hv[q];
+    }
+    const unsigned long long incl = wave_incl_scan_u64(loc, lane);
+    const unsigned long long run = incl - loc;
+    const unsigned long long need = tint > below ? tint - below : 0ull;
+    int cand = 1 << 30;
+    unsigned long long before = 0;
+#pragma unroll
+    for (int q = kBins / kWave - 1; q >= 0; --q) {
+      unsigned long long through = run;
+#pragma unroll
+      for (int f = 0; f <= q; ++f) through += hv[f];
+      if (through >= need) {
+        cand = lane * (kBins / kWave) + q;
+        before = through - hv[q];
+      }
+    }
+    int b = wave_min_i32(cand);
+    if (b >= kBins) b = kBins - 1;   // unreachable for finite inputs
+    before = __shfl(before, b / (kBins / kWave));
+    below += before;
+    prefix = (prefix << kDigit) | (unsigned)b;
+    wave_lds_sync();
+  }
+  if (!done) kstar = prefix;
+
+  int base = 0;
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int j = lane + kWave * t;
+    bool keep = j < nkb && key[t] >= kstar;
+    if (keep && ksz && ksz[j] <= 0) keep = false;
+    if (j < nkb && win.enabled && win.inside(row, j)) keep = true;
+    const unsigned long long bal = __ballot(keep);
+    if (keep) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+    base += __popcll(bal);
+  }
+  return base;
+}
+
+template <int D, int R, int E>
 __global__ __launch_bounds__(256) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
     const int32_t* __restrict__ q_sizes, const int32_t* __restrict__ k_sizes, float thr,
@@ -69,19 +207,30 @@ __global__ __launch_bounds__(256) void select_kernel(
   }
   const float* kbh = kbar + (size_t)bh * nkb * D;
   const int ntiles = (nkb + 15) >> 4;
-  for (int t = wave; t < ntiles; t += 4) {
+  // key rows of tile t for this lane (B operand), loaded one tile ahead
+  auto load_b = [&](int t, float* b) {
     const int key = t * 16 + i16;
     const bool kok = key < nkb;
     const float4* src = reinterpret_cast<const float4*>(kbh + (size_t)(kok ? key : 0) * D + g * KQ);
-    float b[KQ];
 #pragma unroll
-    for (int s = 0; s < KQ / 4; ++s) {
-      const float4 v = kok ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
-      b[4 * s + 0] = v.x; b[4 * s + 1] = v.y; b[4 * s + 2] = v.z; b[4 * s + 3] = v.w;
+    for (int s4 = 0; s4 < KQ / 4; ++s4) {
+      const float4 v = kok ? src[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      b[4 * s4 + 0] = v.x; b[4 * s4 + 1] = v.y; b[4 * s4 + 2] = v.z; b[4 * s4 + 3] = v.w;
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  };
+  float b[KQ], bn[KQ] = {};
+  if (wave < ntiles) load_b(wave, b);
+  for (int t = wave; t < ntiles; t += 4) {
+    const int key = t * 16 + i16;
+    const bool kok = key < nkb;
+    if (t + 4 < ntiles) load_b(t + 4, bn);
+    // four independent accumulation chains, summed at the end
+    f32x4 acc4[4];
 #pragma unroll
-    for (int s = 0; s < KQ; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    for (int c4 = 0; c4 < 4; ++c4) acc4[c4] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) acc4[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc4[s & 3], 0, 0, 0);
+    const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     if (kok) {
       float bias = 0.f;
       bool excluded = false;
@@ -96,6 +245,8 @@ __global__ __launch_bounds__(256) void select_kernel(
         if (rr < R) sc[rr * nkb_pad + key] = excluded ? -INFINITY : acc[v] * scale + bias;
       }
     }
+#pragma unroll
+    for (int s4 = 0; s4 < KQ; ++s4) b[s4] = bn[s4];
   }
   __syncthreads();
 
@@ -111,6 +262,12 @@ __global__ __launch_bounds__(256) void select_kernel(
       continue;
     }
     float* sr = sc + rr * nkb_pad;
+    if constexpr (E > 0) {
+      const int n = select_row_regs<E>(sr, nkb, thr, row, k_sizes ? k_sizes + (size_t)bh * nkb : nullptr,
+                                       win, h, out, lane);
+      if (lane == 0) kv_count[orow] = n;
+      continue;
+    }
     float mx = -INFINITY;
     for (int j = lane; j < nkb; j += kWave) mx = fmaxf(mx, sr[j]);
     mx = wave_max(mx);
@@ -194,14 +351,14 @@ __global__ __launch_bounds__(256) void select_kernel(
   }
 }
 
-template <int D, int R>
+template <int D, int R, int E>
 static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
                                   const int32_t* q_sizes, const int32_t* k_sizes, float thr,
                                   float scale, const Window& win, int32_t* kv_count,
                                   int32_t* kv_index, int kv_stride, hipStream_t s) {
   const int nkb_pad = (nkb + 3) & ~3;
   const size_t lds = (size_t)R * nkb_pad * sizeof(float) + 4 * kBins * sizeof(unsigned long long);
-  auto kern = select_kernel<D, R>;
+  auto kern = select_kernel<D, R, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -216,16 +373,21 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
                          const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
                          hipStream_t s) {
   if (BH == 0 || nqb == 0) return hipSuccess;
-#define BSA_SEL(DD, RR) \
-  launch_select_t<DD, RR>(qbar, kbar, BH, nqb, nkb, q_sizes, k_sizes, thr, scale, win, kv_count, kv_index, kv_stride, s)
+#define BSA_SEL(DD, RR, EE) \
+  launch_select_t<DD, RR, EE>(qbar, kbar, BH, nqb, nkb, q_sizes, k_sizes, thr, scale, win, kv_count, kv_index, kv_stride, s)
+  // rows of up to 2048 key blocks are selected from registers (E per lane)
   if (d == 128) {
-    if (nkb <= 2048) return BSA_SEL(128, 16);
-    if (nkb <= 4096) return BSA_SEL(128, 8);
-    return BSA_SEL(128, 4);
+    if (nkb <= 512) return BSA_SEL(128, 16, 8);
+    if (nkb <= 1024) return BSA_SEL(128, 16, 16);
+    if (nkb <= 2048) return BSA_SEL(128, 16, 32);
+    if (nkb <= 4096) return BSA_SEL(128, 8, 0);
+    return BSA_SEL(128, 4, 0);
   }
-  if (nkb <= 2048) return BSA_SEL(64, 16);
-  if (nkb <= 4096) return BSA_SEL(64, 8);
-  return BSA_SEL(64, 4);
+  if (nkb <= 512) return BSA_SEL(64, 16, 8);
+  if (nkb <= 1024) return BSA_SEL(64, 16, 16);
+  if (nkb <= 2048) return BSA_SEL(64, 16, 32);
+  if (nkb <= 4096) return BSA_SEL(64, 8, 0);
+  return BSA_SEL(64, 4, 0);
 #undef BSA_SEL
 }
 

@@ -161,6 +161,48 @@ def test_mask_deterministic(gpu_lib):
         assert torch.equal(a[1].view(-1, a[1].shape[-1])[r, :c], b[1].view(-1, b[1].shape[-1])[r, :c])
 
 
+def test_mask_exact_ties(gpu_lib):
+    """All scores equal: the cut falls inside one run of ties.
+
+    Every block has the same mass 1/n, so dropping lightest-first with the
+    higher index lighter drops the top indices while the inclusive sum stays
+    below thr: with n = 600 and thr = 0.5004 exactly 300 blocks go and every
+    row keeps J = 0..299 (300/600 < 0.5004 < 301/600). Exercises the path
+    where more than 64 keys share the leading radix digits.
+    """
+    n, d = 600, 64
+    x = torch.full((1, 1, n * 64, d), 0.5, dtype=torch.bfloat16)
+    cnt, idx = gpu_lib.build_block_mask(x.cuda(), x.cuda(), 0.5004)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    ref = om.cdf_keep(np.full(n, 1.0 / n), 0.5004)
+    assert ref.sum() == 300 and ref[:300].all()
+    assert (cnt == 300).all()
+    assert (idx[0, 0, :, :300] == np.arange(300)).all()
+
+
+@pytest.mark.parametrize("nkb", [1000, 2112])
+def test_mask_long_rows(gpu_lib, nkb):
+    """Row lengths beyond the 512-block workloads: 1000 key blocks (16
+    elements per lane) and 2112 (rows streamed from LDS)."""
+    rng = np.random.default_rng(nkb)
+    N, d = nkb * 64, 64
+    ph = rng.normal(size=(N, 8)) @ rng.normal(size=(8, d)) * 0.7
+    x = (ph[None, None] + 0.3 * rng.normal(size=(2, 1, N, d))).astype(np.float32)
+    q = torch.from_numpy(x[0:1, 0:1].reshape(1, 1, N, d)).to(torch.bfloat16)
+    k = torch.from_numpy(x[1:2, 0:1].reshape(1, 1, N, d)).to(torch.bfloat16)
+    say(f"mask long rows nkb={nkb}")
+    cnt, idx = gpu_lib.build_block_mask(q.cuda(), k.cuda(), 0.2)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    st, ln = ol.raster_blocks(N)
+    keep = keep_from_lists(cnt[0, 0], idx[0, 0], nkb)
+    rows = np.arange(0, nkb, 7)
+    _, P = om.block_mask(_np(q[0, 0]), _np(k[0, 0]), st, ln, st, ln, 0.2)
+    bad = mask_mismatches(P[rows], 0.2, keep[rows])
+    say(f"  kept {keep[rows].sum()} of {keep[rows].size}, sure-bit mismatches {bad}")
+    assert bad == 0
+    assert (cnt >= 1).all()
+
+
 # ------------------------------------------------------------------- attention
 
 def _attn_case(bsa, w, q, k, v, heads, nsample, seed=0, thr=None):
