@@ -179,6 +179,120 @@ def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
     }
 
 
+# ---------------------------------------------------------------- profiles
+# Summaries of rocprofv3 CSV output (kernel trace statistics, counter runs),
+# written as the text files kept under profiles/.
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan480_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_avg_amd", "csrc", "attn_fwd.hip")
+
+
+def _sha256(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "")
+    return name.split("(")[0]
+
+
+def rocprof_stats(run_dir: str):
+    """[(kernel, calls, avg_us, min_us, max_us, pct)] from run_kernel_stats.csv."""
+    out = []
+    for r in _csv_rows(os.path.join(run_dir, "run_kernel_stats.csv")):
+        out.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return out
+
+
+def rocprof_counter(run_dir: str, counter: str, kernel: str):
+    """Mean per dispatch of one counter over the dispatches of `kernel`."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(run_dir, "run_counter_collection.csv"))
+            if r["Counter_Name"] == counter and _short(r["Kernel_Name"]) == kernel]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for {kernel} in {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel source changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+        if kv.get("source_sha256", "").strip() != _sha256(ATTN_SRC):
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
+    lines = []
+    if kind == "stats":
+        lines.append(f"command: {command}")
+        lines.append("kernel                                   calls    avg_us      min_us      max_us    pct")
+        for name, calls, avg, mn, mx, pct in rocprof_stats(dirs[0]):
+            lines.append(f"{name[:40]:40s} {calls:6d} {avg:10.2f} {mn:10.2f} {mx:10.2f} {pct:6.2f}")
+        if bench_log:
+            with open(bench_log) as f:
+                js = [json.loads(l) for l in f if l.startswith("{")]
+            if js:
+                b = js[-1]
+                att = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::attn_fwd_kernel")]
+                lines.append(f"bench (same run): attention stage {b['stages_ms']['attention'] * 1e3:.1f} us per "
+                             f"call (HIP events around the C-ABI call), roofline.achieved "
+                             f"{b['roofline']['achieved']} TFLOP/s")
+                if att:
+                    lines.append(f"rocprof attn_fwd_kernel average {att[0][2]:.1f} us "
+                                 f"(ratio events / kernel {b['stages_ms']['attention'] * 1e3 / att[0][2]:.3f})")
+    elif kind == "counters":
+        lines.append(f"command: {command}")
+        rows = _csv_rows(os.path.join(dirs[0], "run_counter_collection.csv"))
+        kernels = sorted({_short(r["Kernel_Name"]) for r in rows if _short(r["Kernel_Name"]).startswith("bsa::")})
+        for k in kernels:
+            counters = sorted({r["Counter_Name"] for r in rows if _short(r["Kernel_Name"]) == k})
+            vals = []
+            for c in counters:
+                v, n = rocprof_counter(dirs[0], c, k)
+                vals.append(f"{c}={v:.5g}")
+            lines.append(f"{k} (mean per dispatch): " + " ".join(vals))
+    elif kind == "traffic":
+        fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+        kern = "bsa::attn_fwd_kernel<128, false, false>"
+        copy = "bsa::permute_kernel<16>"
+        f_att, n1 = rocprof_counter(fetch_dir, "FETCH_SIZE", kern)
+        w_att, n2 = rocprof_counter(write_dir, "WRITE_SIZE", kern)
+        f_cp, n3 = rocprof_counter(cfetch_dir, "FETCH_SIZE", copy)
+        w_cp, n4 = rocprof_counter(cwrite_dir, "WRITE_SIZE", copy)
+        gib = 1024.0 ** 3
+        f_scale = gib / (f_cp * 1024.0)          # bytes the copy really read per counted byte
+        w_scale = gib / (w_cp * 1024.0)
+        fetch_b = f_att * 1024.0 * f_scale
+        write_b = w_att * 1024.0 * w_scale
+        lines += [
+            f"command: {command}",
+            f"kernel: {kern} (wan480 workload, bench.py --steps 5 --warmup 2 --no-cpu-baseline --also none)",
+            f"FETCH_SIZE per dispatch: {f_att:.1f} KiB over {n1} dispatches",
+            f"WRITE_SIZE per dispatch: {w_att:.1f} KiB over {n2} dispatches",
+            f"copy calibration ({copy}, identity permutation reading and writing 1 GiB): "
+            f"FETCH_SIZE {f_cp:.1f} KiB (x{f_scale:.3f}), WRITE_SIZE {w_cp:.1f} KiB (x{w_scale:.3f}) over {n3}/{n4}",
+            f"fetch_bytes_per_launch: {fetch_b:.6g}",
+            f"write_bytes_per_launch: {write_b:.6g}",
+            f"traffic_bytes_per_launch: {fetch_b + write_b:.6g}",
+            f"source_sha256: {_sha256(ATTN_SRC)}",
+        ]
+    print("\n".join(lines))
+
+
 def copy_calibration(dev, steps: int):
     """Identity permutation: reads and writes exactly 1 GiB per launch."""
     B, H, N, d = 1, 16, 262144, 128        # 16 * 262144 * 128 * 2 bytes = 1 GiB
@@ -204,7 +318,16 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (identity token permutation of "
                          "1 GiB of bf16 rows) to calibrate hardware byte counters")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar=("KIND", "DIR"),
+                    help="summarise rocprofv3 CSV output: 'stats DIR' (kernel trace), "
+                         "'counters DIR' (counter means) or "
+                         "'traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR'")
+    ap.add_argument("--bench-log", help="bench output of the profiled run (stats summary)")
+    ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     a = ap.parse_args()
+    if a.rocprof_summary:
+        rocprof_summary(a.rocprof_summary[0], a.rocprof_summary[1:], a.bench_log, a.command)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the hot path shards by head with no communication; see the design notes).",
@@ -250,7 +373,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(s["attn_frac_of_peak"], 4),
-            "traffic": None,
+            "traffic": measured_traffic() if a.config == "wan480" else None,
         },
         "pct_bf16_peak_attn": round(100 * s["attn_frac_of_peak"], 2),
         "sparsity": {"blocks": round(s["sparsity_blocks"], 4),
