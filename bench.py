@@ -1,6 +1,6 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config wan480]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config wan480]
 
 One step = the whole hot path on one batch of synthetic input already resident
 in HBM: block mean pooling of Q and K, reduced attention + CDF selection (the
@@ -101,9 +101,16 @@ class Runner:
         self.mask()
         self.attn()
 
-    def timed(self, steps: int, warmup: int):
-        for _ in range(warmup):
+    def timed(self, steps: int, warmup: int, min_warm_s: float = 1.0):
+        # at least `warmup` steps and at least min_warm_s of GPU work, so the
+        # clocks have left their idle state before the timed steps
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t0 < min_warm_s:
             self.step()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         t0 = time.perf_counter()
@@ -310,8 +317,8 @@ def copy_calibration(dev, steps: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="wan480", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="hunyuan720", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -392,7 +399,7 @@ def main():
         torch.cuda.empty_cache()
         w2 = WORKLOADS[a.also]
         r2 = Runner(w2, dev)
-        m2, tm2, ta2 = r2.timed(max(3, a.steps // 2), max(1, a.warmup // 2))
+        m2, tm2, ta2 = r2.timed(max(3, a.steps // 10), max(1, a.warmup // 10))
         s2 = r2.summary(m2, tm2, ta2)
         line["also"] = {w2.key: {
             "workload": describe(w2),
