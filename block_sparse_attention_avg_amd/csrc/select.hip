@@ -14,7 +14,7 @@
 // Phase 2 -- selection, one wave per row (rows of up to 2048 key blocks are
 // held in registers, longer rows are streamed from LDS). p_J = exp(s_J - max)
 // in fp32.
-// Masses are converted to 2^-40 fixed point (m_J = floor(p_J * 2^40)) so that
+// Masses are converted to 2^-31 fixed point (m_J = floor(p_J * 2^31)) so that
 // every sum is exact and order-independent. The cut is found by an MSB-first
 // radix select over the 43-bit key (bits(p_J) << 13 | (8191 - J)): keys order
 // blocks lightest first with ties broken toward the higher index. Each 8-bit
@@ -37,6 +37,10 @@ constexpr int kKeyBits = 30 + kIdxBits;
 constexpr int kDigit = 8;
 constexpr int kPasses = (kKeyBits + kDigit - 1) / kDigit;   // 6
 constexpr int kBins = 1 << kDigit;
+constexpr int kSelWaves = 4;          // waves per workgroup
+constexpr float kMassScale = 0x1p31f; // block masses in 2^-31 fixed point
+constexpr int kHist = 512;           // histogram words per wave
+constexpr int kDigit0 = 192;          // first-digit value of p = 2^-31 (bits(p) >> 22)
 }  // namespace
 
 // Selection of one row with its elements held in registers (E per lane,
@@ -48,25 +52,31 @@ template <int E>
 __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float thr, int row,
                                                const int32_t* ksz, const Window& win,
                                                unsigned long long* h, int32_t* out, int lane) {
-  float e[E];
+  // per element: pb = bits of p (the key is pb << 13 | 8191 - j) and the
+  // fixed-point mass mm = floor(p * 2^31)
+  uint32_t pb[E], mm[E];
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
     const int j = lane + kWave * t;
-    e[t] = j < nkb ? sr[j] : -INFINITY;
-    mx = fmaxf(mx, e[t]);
+    const float sj = j < nkb ? sr[j] : -INFINITY;
+    pb[t] = __float_as_uint(sj);
+    mx = fmaxf(mx, sj);
   }
   mx = wave_max(mx);
-  unsigned long long key[E], m[E];
   unsigned long long z = 0;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
     const int j = lane + kWave * t;
-    const float pj = j < nkb ? expf(e[t] - mx) : 0.f;   // in [0, 1]; exp(-inf) = 0
-    m[t] = (unsigned long long)(pj * 0x1p40f);
-    key[t] = ((unsigned long long)__float_as_uint(pj) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
-    z += m[t];
+    // exp(s - max) as exp2 on the hardware unit: relative error ~1e-6
+    const float pj = j < nkb ? __builtin_amdgcn_exp2f((__uint_as_float(pb[t]) - mx) * 1.4426950408889634f) : 0.f;
+    pb[t] = __float_as_uint(pj);
+    mm[t] = (uint32_t)(pj * kMassScale);
+    z += mm[t];
   }
+  auto key_of = [&](int t) -> unsigned long long {
+    return ((unsigned long long)pb[t] << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - (lane + kWave * t));
+  };
   z = wave_sum_u64(z);
   const double tt = ceil((double)thr * (double)z);
   const unsigned long long tint = tt >= (double)z ? z : (unsigned long long)tt;
@@ -77,32 +87,40 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   // a zero threshold keeps every block: k* = 0 without any pass
 #pragma unroll 1
   for (int pass = 0; pass < kPasses && tint > 0; ++pass) {
-    const int shift = kDigit * (kPasses - 1 - pass);
+    // digits from the top: 8 bits at 35, 27, 19, 11, 3, then bits 2..0
+    const int width = pass < kPasses - 1 ? kDigit : kKeyBits - kDigit * (kPasses - 1);
+    const int shift = pass < kPasses - 1 ? kKeyBits - kDigit * (pass + 1) : 0;
+    // rebuild keys inside each pass instead of keeping 64-bit copies of all
+    // of them alive across passes (register pressure)
+#pragma unroll
+    for (int t = 0; t < E; ++t) asm volatile("" : "+v"(pb[t]));
     if (pass == 2) {
-      // The cut lies among the keys that share the 16-bit prefix. When there
+      // The cut lies among the keys that share the 16-bit prefix (bits 42..27). When there
       // are at most 64 of them, finish exactly with one candidate per lane:
       // k* is the smallest candidate key whose inclusive cumulative mass
       // (below + candidates with keys <= it) reaches the threshold.
       int ncand = 0;
 #pragma unroll
-      for (int t = 0; t < E; ++t) ncand += __popcll(__ballot((key[t] >> (shift + kDigit)) == prefix));
+      for (int t = 0; t < E; ++t) ncand += __popcll(__ballot((key_of(t) >> (shift + width)) == prefix));
       if (ncand <= kWave) {
         unsigned long long* slot = h;          // 64 x (key, mass) = 1 KiB of this wave's histogram
         int at = 0;
 #pragma unroll
         for (int t = 0; t < E; ++t) {
-          const bool c = (key[t] >> (shift + kDigit)) == prefix;
+          const unsigned long long kt = key_of(t);
+          const bool c = (kt >> (shift + width)) == prefix;
           const unsigned long long bal = __ballot(c);
           if (c) {
             const int r = at + __popcll(bal & ((1ull << lane) - 1ull));
-            slot[2 * r] = key[t];
-            slot[2 * r + 1] = m[t];
+            slot[2 * r] = kt;
+            slot[2 * r + 1] = mm[t];
           }
           at += __popcll(bal);
         }
         wave_lds_sync();
         const unsigned long long ck = lane < ncand ? slot[2 * lane] : ~0ull;
         unsigned long long through = below;
+#pragma unroll 8
         for (int i = 0; i < ncand; ++i) {
           const unsigned long long ki = slot[2 * i], mi = slot[2 * i + 1];   // same address in every lane
           through += ki <= ck ? mi : 0ull;
@@ -122,12 +140,37 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
         break;
       }
     }
+    if (pass == 0) {
+      // First digit (key bits 42..35 = bits 29..22 of p): a block with mass
+      // has p >= 2^-31, so its digit is in [kDigit0, 255) -- 64 bins, one per
+      // lane, accumulated in 8 private copies (lanes l, l+8, ... share one).
+      unsigned long long* h0 = h;                  // [8][64]
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h0[q * kWave + lane] = 0;
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < E; ++t)
+        if (mm[t]) atomicAdd(&h0[(lane & 7) * kWave + ((pb[t] >> 22) - kDigit0)], (unsigned long long)mm[t]);
+      wave_lds_sync();
+      unsigned long long v = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v += h0[q * kWave + lane];
+      const unsigned long long through = wave_incl_scan_u64(v, lane);
+      const int b0 = wave_min_i32(through >= tint ? lane : 1 << 30);
+      below = __shfl(through - v, b0);
+      prefix = (unsigned)(kDigit0 + b0);
+      wave_lds_sync();
+      continue;
+    }
 #pragma unroll
     for (int q = 0; q < kBins / kWave; ++q) h[lane * (kBins / kWave) + q] = 0;
     wave_lds_sync();
 #pragma unroll
-    for (int t = 0; t < E; ++t)
-      if ((key[t] >> (shift + kDigit)) == prefix && m[t]) atomicAdd(&h[(key[t] >> shift) & (kBins - 1)], m[t]);
+    for (int t = 0; t < E; ++t) {
+      const unsigned long long kt = key_of(t);
+      if ((kt >> (shift + width)) == prefix && mm[t])
+        atomicAdd(&h[(kt >> shift) & ((1 << width) - 1)], (unsigned long long)mm[t]);
+    }
     wave_lds_sync();
     // lane owns bins [4*lane, 4*lane+4)
     unsigned long long hv[kBins / kWave];
@@ -156,7 +199,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
     if (b >= kBins) b = kBins - 1;   // unreachable for finite inputs
     before = __shfl(before, b / (kBins / kWave));
     below += before;
-    prefix = (prefix << kDigit) | (unsigned)b;
+    prefix = (prefix << width) | (unsigned)b;
     wave_lds_sync();
   }
   if (!done) kstar = prefix;
@@ -165,7 +208,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
 #pragma unroll
   for (int t = 0; t < E; ++t) {
     const int j = lane + kWave * t;
-    bool keep = j < nkb && key[t] >= kstar;
+    bool keep = j < nkb && key_of(t) >= kstar;
     if (keep && ksz && ksz[j] <= 0) keep = false;
     if (j < nkb && win.enabled && win.inside(row, j)) keep = true;
     const unsigned long long bal = __ballot(keep);
@@ -176,7 +219,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
 }
 
 template <int D, int R, int E>
-__global__ __launch_bounds__(256) void select_kernel(
+__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
     const int32_t* __restrict__ q_sizes, const int32_t* __restrict__ k_sizes, float thr,
     float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
@@ -220,10 +263,10 @@ __global__ __launch_bounds__(256) void select_kernel(
   };
   float b[KQ], bn[KQ] = {};
   if (wave < ntiles) load_b(wave, b);
-  for (int t = wave; t < ntiles; t += 4) {
+  for (int t = wave; t < ntiles; t += kSelWaves) {
     const int key = t * 16 + i16;
     const bool kok = key < nkb;
-    if (t + 4 < ntiles) load_b(t + 4, bn);
+    if (t + kSelWaves < ntiles) load_b(t + kSelWaves, bn);
     // four independent accumulation chains, summed at the end
     f32x4 acc4[4];
 #pragma unroll
@@ -251,8 +294,8 @@ __global__ __launch_bounds__(256) void select_kernel(
   __syncthreads();
 
   // ---------------- phase 2: per-row CDF selection
-  unsigned long long* h = hist + wave * kBins;
-  for (int rr = wave; rr < R; rr += 4) {
+  unsigned long long* h = hist + wave * kHist;
+  for (int rr = wave; rr < R; rr += kSelWaves) {
     const int row = row0 + rr;
     if (row >= nqb) break;
     const size_t orow = (size_t)bh * nqb + row;
@@ -275,7 +318,7 @@ __global__ __launch_bounds__(256) void select_kernel(
     for (int j = lane; j < nkb; j += kWave) {
       const float p = expf(sr[j] - mx);     // in [0, 1]; exp(-inf) = 0
       sr[j] = p;
-      z += (unsigned long long)(p * 0x1p40f);
+      z += (unsigned long long)(p * kMassScale);
     }
     z = wave_sum_u64(z);
     const double tt = ceil((double)thr * (double)z);
@@ -294,7 +337,7 @@ __global__ __launch_bounds__(256) void select_kernel(
         const unsigned long long key =
             ((unsigned long long)__float_as_uint(p) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
         if ((key >> (shift + kDigit)) == prefix) {
-          const unsigned long long m = (unsigned long long)(p * 0x1p40f);
+          const unsigned long long m = (unsigned long long)(p * kMassScale);
           if (m) atomicAdd(&h[(key >> shift) & (kBins - 1)], m);
         }
       }
@@ -357,13 +400,13 @@ static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, 
                                   float scale, const Window& win, int32_t* kv_count,
                                   int32_t* kv_index, int kv_stride, hipStream_t s) {
   const int nkb_pad = (nkb + 3) & ~3;
-  const size_t lds = (size_t)R * nkb_pad * sizeof(float) + 4 * kBins * sizeof(unsigned long long);
+  const size_t lds = (size_t)R * nkb_pad * sizeof(float) + kSelWaves * kHist * sizeof(unsigned long long);
   auto kern = select_kernel<D, R, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((nqb + R - 1) / R, BH);
-  kern<<<grid, 256, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, q_sizes, k_sizes, thr, scale, win,
+  kern<<<grid, 64 * kSelWaves, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, q_sizes, k_sizes, thr, scale, win,
                               kv_count, kv_index, kv_stride);
   return hipGetLastError();
 }
