@@ -23,7 +23,7 @@
 //                      lane-local plus one permlane32 swap with the lane
 //                      holding the other 32.
 //   online softmax     fp32, log2 domain (scale*log2e folded into one FMA),
-//                      O rescaled only when some row max grew by > 2^8.
+//                      O rescaled only when some row max grew by > 2^64.
 //   O^T += V^T P^T     bf16 MFMA 32x32x16; P^T is the S^T accumulator
 //                      rounded to bf16 in registers (hardware convert), and
 //                      V^T comes straight from the row-major V tile through the
@@ -152,7 +152,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   constexpr int NI = TILE / 1024;              // direct-to-LDS loads per tile
   constexpr int RPI = 1024 / ROWB;             // rows per load instruction
   constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
-  constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
+  // rescale O only when a row max grows by > 2^TAU: until then P <= 2^TAU,
+  // and O, l stay far inside fp32 / bf16 range (their ratio is unaffected);
+  // a small TAU would rescale on most chunks, since any of the 64 rows can
+  // trigger it
+  constexpr float TAU = 64.f;
   constexpr uint32_t OOB = 0xFFFFFFF0u;        // lane offset past every descriptor: loads zeros
   constexpr int NS = D / 8;                    // K (and V) operand reads per chunk
   constexpr int EPS = 64 / NS;                 // softmax elements per lane per read
@@ -404,7 +408,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
 
     // ---- region A: S(c+1) on MFMA || P(c) on VALU
     uint32_t pw[2][2][2][4];           // [kb][hh][qh][word]
-    float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     {
 #pragma unroll
       for (int x = 0; x < 4; ++x)
@@ -427,8 +430,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
           const int q2 = el >> 5, kb = (el >> 4) & 1, r = el & 15;
           const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * kb + q2][r], a.sl2, -m_run[q2]));
           const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * kb + q2][r + 1], a.sl2, -m_run[q2]));
-          rsum[q2][0] += x0;
-          rsum[q2][1] += x1;
           pw[kb][r >> 3][q2][(r & 7) >> 1] = pack2(x0, x1);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -443,10 +444,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     asm volatile("" ::"v"(pw[1][0][0][0]), "v"(pw[1][0][0][1]), "v"(pw[1][0][0][2]), "v"(pw[1][0][0][3]),
                  "v"(pw[1][0][1][0]), "v"(pw[1][0][1][1]), "v"(pw[1][0][1][2]), "v"(pw[1][0][1][3]),
                  "v"(pw[1][1][0][0]), "v"(pw[1][1][0][1]), "v"(pw[1][1][0][2]), "v"(pw[1][1][0][3]),
-                 "v"(pw[1][1][1][0]), "v"(pw[1][1][1][1]), "v"(pw[1][1][1][2]), "v"(pw[1][1][1][3]),
-                 "v"(rsum[0][0]), "v"(rsum[0][1]), "v"(rsum[1][0]), "v"(rsum[1][1]));
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) l_run[q2] += rsum[q2][0] + rsum[q2][1];
+                 "v"(pw[1][1][1][0]), "v"(pw[1][1][1][1]), "v"(pw[1][1][1][2]), "v"(pw[1][1][1][3]));
     bf16x8 pf[2][2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -472,6 +470,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     asm volatile("" ::: "memory");
     mask_tail(sn, kl_n);
     float mx[2] = {-INFINITY, -INFINITY};
+    // row sums of the bf16-rounded P that PV multiplies (so the output is a
+    // convex combination with exactly the weights used), one bf16 dot
+    // product with (1, 1) per packed pair, in the VALU slack of region B
+    float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     {
       bf16x8 vr[4];
       vr[0] = v_read(0);
@@ -490,9 +492,20 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
           const int q2 = el >> 5, kb2 = (el >> 4) & 1, r = el & 15;
           mx[q2] = fmaxf(mx[q2], fmaxf(sn[2 * kb2 + q2][r], sn[2 * kb2 + q2][r + 1]));
         }
+        // the 8 words of pf[kb][hh][*] are summed over the D/32 steps that use them
+#pragma unroll
+        for (int u = 0; u < 8 / (D / 32); ++u) {
+          const int wi = dg * (8 / (D / 32)) + u;          // word 0..7 of this (kb, hh)
+          const int q2 = wi >> 2;
+          rsum[q2][u & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kb][hh][q2][wi & 3]),
+                                                            __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                                            rsum[q2][u & 1], false);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) l_run[q2] += rsum[q2][0] + rsum[q2][1];
     wait_lgkm0();                      // V(c) reads done before the buffer is refilled
     asm volatile("" ::: "memory");
     {
