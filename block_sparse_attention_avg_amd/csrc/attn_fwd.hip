@@ -4,26 +4,26 @@
 // and value rows of the kept blocks are gathered sparsely, so variable-size
 // blocks waste no padding on the key side).
 //
-// Work item: one 64-row query tile of one head on one wave (a one-wave
-// workgroup). The kept key blocks of the tile's query block are walked in
-// ascending order as a stream of key rows cut into 64-row chunks; with
+// Work item: one 64-row query tile of one head, 2 waves (wave w owns query
+// rows 32w..32w+31). The kept key blocks of the tile's query block are walked
+// in ascending order as a stream of key rows cut into 64-row chunks; with
 // uniform 64-token blocks a chunk is exactly one key block.
 //
-// Data movement: K and V chunks go HBM -> LDS with direct-to-LDS buffer loads
-// (no staging registers), row-major, each row's 16-byte pieces XOR-swizzled so
+// Data movement: K and V chunks go HBM -> LDS with direct-to-LDS loads (no
+// staging registers), row-major, each row's 16-byte pieces XOR-swizzled so
 // that both the K operand reads and the transposed V reads below are free of
-// bank conflicts. The next chunk's K is in flight while this chunk's softmax
-// and PV run, the next V while the next S runs. Waits are explicit vmcnt
-// counts.
+// bank conflicts. The pipeline is split by phase: the next chunk's K is in
+// flight while this chunk's softmax and PV run, the next V while the next S
+// runs. Waits are explicit vmcnt counts; barriers carry no memory fence (a
+// fence would drain every in-flight load).
 //
-// Math per chunk (two 32-row query halves qh share each operand read):
+// Math per wave and chunk:
 //   S^T = K Q^T        bf16 MFMA 32x32x16; Q^T stays in registers as the B
 //                      operand for the whole tile, so each lane ends up with
-//                      32 key scores of one query per half: max/sum are
-//                      lane-local plus one permlane32 swap with the lane
-//                      holding the other 32.
+//                      32 key scores of ONE query: max/sum are lane-local plus
+//                      one permlane32 swap with the lane holding the other 32.
 //   online softmax     fp32, log2 domain (scale*log2e folded into one FMA),
-//                      O rescaled only when some row max grew by > 2^64.
+//                      O rescaled only when some row max moved.
 //   O^T += V^T P^T     bf16 MFMA 32x32x16; P^T is the S^T accumulator
 //                      rounded to bf16 in registers (hardware convert), and
 //                      V^T comes straight from the row-major V tile through the
@@ -90,6 +90,17 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
 }
 
+// Workgroup barrier for the LDS pipeline: this wave's LDS accesses complete
+// before it arrives (so no other wave can refill a tile under a read still in
+// the LDS queue), compiler-level ordering of memory accesses on both sides,
+// but no wait on in-flight direct-to-LDS loads (those are waited explicitly).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -120,76 +131,65 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 }  // namespace
 
-// One query tile of 64 rows on ONE wave. The two 32-row halves qh = 0, 1 of
-// the MFMA output share every K and V operand read from LDS (half the LDS
-// traffic per FLOP of two 32-row waves), and a one-wave workgroup needs no
-// barrier: LDS reads and refills are ordered by the wave's own waits. K and V
-// tiles are separate LDS arrays so the compiler can tell the two
-// direct-to-LDS load streams apart; all waits on those loads are explicit
-// vmcnt counts.
+// One query tile. K and V tiles are separate LDS arrays so the compiler can
+// tell the two direct-to-LDS load streams apart; all waits on those loads are
+// explicit vmcnt counts.
 //
-// Software pipeline (iteration c):
+// Software pipeline (iteration c, every wave):
+//   prep:      mask and row max of S(c); rare rescale of O;
 //   region A:  S(c+1) = K(c+1) Q^T on MFMA, interleaved instruction by
 //              instruction with exp2 / row sum / bf16 pack of S(c) on the
-//              VALU (independent work, so the two pipes overlap);
-//   region B:  O^T += V(c)^T P(c)^T on MFMA, interleaved with the row max of
-//              S(c+1); then the rare rescale of O for S(c+1)'s max.
-// K(c+2) is issued when region A has read K(c+1), V(c+1) when region B has
-// read V(c). Each iteration issues exactly one K and one V tile load (after
-// the last chunk they re-load rows of a chunk that exists into the free
-// buffer, and the extra S is discarded), so the number of loads in flight is
-// the same on every path. The loop body is unrolled twice so S(c) and S(c+1)
-// swap registers instead of being copied.
+//              VALU (independent work, so the two pipes overlap in one wave);
+//   region B:  O^T += V(c)^T P(c)^T on MFMA.
+// Loads: K(c+2) is issued once every wave has finished region A, V(c+1) once
+// every wave has finished region B. Each iteration issues exactly one K and
+// one V tile load (after the last chunk they re-load rows of a chunk that
+// exists into the free buffer, and the extra S is discarded), so the number
+// of loads in flight is the same on every path. The loop body is unrolled
+// twice so S(c) and S(c+1) swap registers instead of being copied.
 //
-// Loads go through buffer descriptors that end at the chunk's last row: rows
-// past it (a partial last block, gathered rows past the chunk) read as zeros,
-// so no clamping is needed and padding never reaches P V.
+// Loads go through buffer descriptors that end at the chunk's last row:
+// rows past it (a partial last block, gathered rows past the chunk) read as
+// zeros, so no clamping is needed and padding never reaches P V.
 template <int D, bool KVAR>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
-                                             lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
+                                          lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
   constexpr int ROWB = D * 2;                  // bytes per K/V row
   constexpr int TILE = 64 * ROWB;              // bytes per K or V tile
-  constexpr int NI = TILE / 1024;              // direct-to-LDS loads per tile
+  constexpr int NI = TILE / 1024 / 2;          // direct-to-LDS loads per wave per tile
   constexpr int RPI = 1024 / ROWB;             // rows per load instruction
   constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
-  // rescale O only when a row max grows by > 2^TAU: until then P <= 2^TAU,
-  // and O, l stay far inside fp32 / bf16 range (their ratio is unaffected);
-  // a small TAU would rescale on most chunks, since any of the 64 rows can
-  // trigger it
-  constexpr float TAU = 64.f;
+  constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
   constexpr uint32_t OOB = 0xFFFFFFF0u;        // lane offset past every descriptor: loads zeros
-  constexpr int NS = D / 8;                    // K (and V) operand reads per chunk
-  constexpr int EPS = 64 / NS;                 // softmax elements per lane per read
 
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const size_t head_off = (size_t)bh * a.N * D;
-  const uint16_t* qh_ = a.q + head_off;
+  const uint16_t* qh = a.q + head_off;
   const unsigned char* kh = reinterpret_cast<const unsigned char*>(a.k + head_off);
   const unsigned char* vh = reinterpret_cast<const unsigned char*>(a.v + head_off);
 
-  // Q^T as MFMA B operand: lane supplies Q[32qh + l32][16c + 8*half .. +7].
-  bf16x8 qf[2][D / 16];
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int qr = 32 * q2 + l32;
+  // Q^T as MFMA B operand: lane supplies Q[row][16c + 8*half .. +7].
+  bf16x8 qf[D / 16];
+  {
+    const int qr = 32 * wave + l32;
     const bool ok = qr < ql;
-    const uint16_t* src = qh_ + (size_t)(qs + (ok ? qr : 0)) * D + 8 * half;
+    const uint16_t* src = qh + (size_t)(qs + (ok ? qr : 0)) * D + 8 * half;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       uint4 w = ok ? *reinterpret_cast<const uint4*>(src + 16 * c) : make_uint4(0, 0, 0, 0);
-      qf[q2][c] = __builtin_bit_cast(bf16x8, w);
+      qf[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  f32x16 oacc[D / 32][2];
+  f32x16 oacc[D / 32];
 #pragma unroll
   for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dg][q2][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   const size_t qrow = (size_t)bh * a.nqb + I;
   const int cnt = ((const cint*)a.kv_count)[qrow];
@@ -209,26 +209,31 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int row = 8 * t + 4 * half + sj;
+      const int row = 8 * t + 4 * half + sj;               // + 32kb + 16hh (multiple of 16)
       const int piece = 4 * dg + 2 * g16 + (sq >> 1);
       voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
     }
+
+  // Lane byte offsets of the loads of a full chunk of 64 consecutive rows.
   uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int r = i * RPI + lane / PPR;
+    const int r = (wave * NI + i) * RPI + lane / PPR;
     loff[i] = r * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4);
   }
+  // Buffer descriptor over `rows` rows starting at row `ks` of a head.
   auto desc = [&](const unsigned char* base, int ks, int rows) -> __amdgpu_buffer_rsrc_t {
     return make_rsrc(base + (size_t)ks * ROWB, (uint32_t)rows * (uint32_t)ROWB);
   };
+  // Direct-to-LDS issue of one K or V tile. Row r comes from token ks + r
+  // (uniform blocks) or tk[r] (gathered); rows >= kl load zeros.
   auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
     uint32_t off[NI];
     const __amdgpu_buffer_rsrc_t rs = KVAR ? desc(isv ? vh : kh, 0, a.N) : desc(isv ? vh : kh, ks, kl);
     if constexpr (KVAR) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int r = i * RPI + lane / PPR;
+        const int r = (wave * NI + i) * RPI + lane / PPR;
         const int t = tk[r < kl ? r : 0];
         off[i] = (r < kl && (unsigned)t < (unsigned)a.N)
                      ? (uint32_t)t * ROWB + (((lane % PPR) ^ swz<D>(r & 15)) << 4)
@@ -238,28 +243,30 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
 #pragma unroll
       for (int i = 0; i < NI; ++i) off[i] = loff[i];
     }
+    // separate call sites: each load names its own destination tile
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      const int ins = wave * NI + i;
       if (isv)
-        dma16(rs, Vp + i * 1024, off[i]);
+        dma16(rs, Vp + ins * 1024, off[i]);
       else
-        dma16(rs, Kp + i * 1024, off[i]);
+        dma16(rs, Kp + ins * 1024, off[i]);
     }
   };
 
   // ---- chunk descriptors
   // Uniform blocks: chunk c is key block list[c] (scalar loads).
-  // Gathered blocks: the token indices of chunk c go to the ring slot
-  // tok[c & 3], produced with a cursor (list entry e_cur, offset off_cur).
   auto chunk_uniform = [&](int c, int& ks, int& kl) {
     if (c >= cnt) { ks = 0; kl = 0; return; }
     int J = slist[c];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;   // invalid ids stay in bounds
-    ks = J * 64;
+    ks = J * 64;                       // uniform 64-token key blocks
     kl = min(64, a.n_valid - ks);
   };
+  // Gathered blocks: wave 0 writes the token indices of chunk c to the ring
+  // slot tok[c & 3] with a cursor (list entry e_cur, offset off_cur).
   int e_cur = 0, off_cur = 0;
-  auto next_chunk = [&](int slot) {
+  auto next_chunk = [&](int slot) {   // wave 0 only
     int rows = 0;
     while (rows == 0 && e_cur < cnt) {
       const int ent = e_cur + lane;
@@ -313,11 +320,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   };
 
   // ---- LDS operand reads
+  // K operand of S^T step j (k-step cc = j / 2, key half kb = j % 2)
   auto k_read = [&](int j) -> bf16x8 {
     const int cc = j >> 1, kb = j & 1;
     const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
   };
+  // V^T operand of PV step j (key half kb, 16-key group hh, channel group dg)
   auto v_read = [&](int j) -> bf16x8 {
     const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
     const int base = (32 * kb + 16 * hh) * ROWB;
@@ -325,94 +334,91 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // S[kb][qh] (s has 4 accumulators, index 2*kb + qh)
+  constexpr int NS = D / 8;            // MFMA steps of S^T (and of PV)
+  constexpr int EPS = 32 / NS;         // softmax elements per step
+
+  // S^T = K Q^T from the K tile into s (prologue only)
   auto compute_s = [&](f32x16* s) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[x][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const bf16x8 ka = k_read(j);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-        s[2 * (j & 1) + q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[q2][j >> 1], s[2 * (j & 1) + q2], 0, 0, 0);
-    }
+    for (int j = 0; j < NS; ++j) s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(j), qf[j >> 1], s[j & 1], 0, 0, 0);
   };
+  // keys >= kl of a chunk get -inf
   auto mask_tail = [&](f32x16* s, int kl_s) {
     if (kl_s < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= kl_s) s[2 * kb + q2][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kl_s) s[kb][r] = -INFINITY;
+        }
     }
   };
-  auto settle_max = [&](const float* mx) {
-    float mloc[2];
-    bool grow[2];
+  // row max in log2 units -> move the reference max when it grew by > TAU
+  auto settle_max = [&](float mx) {
+    const float mloc = halves_max(mx) * a.sl2;
+    const bool grow = mloc > m_run + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow)) {   // rare: rescale O and l
+      const float m_new = grow ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      mloc[q2] = halves_max(mx[q2]) * a.sl2;
-      grow[q2] = mloc[q2] > m_run[q2] + TAU;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1])) {   // rare: rescale O and l
+      for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const float m_new = grow[q2] ? mloc[q2] : m_run[q2];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[q2] - m_new);
-        l_run[q2] *= alpha;
-#pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dg][q2][r] *= alpha;
-        m_run[q2] = m_new;
-      }
+        for (int r = 0; r < 16; ++r) oacc[dg][r] *= alpha;
+      m_run = m_new;
     }
   };
 
-  // ---- prologue
+  // ---- prologue: descriptors of chunks 0 and 1, load K0, S(0), loads K1 V0
   if constexpr (KVAR) {
-    next_chunk(0);
-    next_chunk(1);
+    if (wave == 0) {
+      next_chunk(0);
+      next_chunk(1);
+    }
     wait_lgkm0();
+    wg_barrier();
   }
   int ks0, kl0, ks1, kl1;
   chunk_info(0, ks0, kl0);
-  if (kl0 == 0) {
+  if (kl0 == 0) {                      // nothing kept: zero rows
     ks1 = ks0; kl1 = kl0;
   } else {
     chunk_info(1, ks1, kl1);
   }
-  f32x16 sA[4], sB[4];
+  f32x16 sA[2], sB[2];
   int c = 0;
-  int kl = kl0, ks_c = ks0;
-  int ks_n = ks1, kl_n = kl1;
+  int kl = kl0, ks_c = ks0;            // chunk c
+  int ks_n = ks1, kl_n = kl1;          // chunk c+1
 
+  // One pipeline iteration; sc holds S(c) (masked, reference max settled),
+  // sn receives S(c+1).
   auto iter = [&](f32x16* sc, f32x16* sn) -> bool {
     int ks_2 = 0, kl_2 = 0;
     if constexpr (KVAR) {
-      next_chunk((c + 2) & 3);
+      if (wave == 0) next_chunk((c + 2) & 3);   // ring slot of chunk c+2
     } else {
-      chunk_uniform(c + 2, ks_2, kl_2);
+      chunk_uniform(c + 2, ks_2, kl_2);         // scalar load, lands by the barrier
     }
     // outstanding loads, oldest first: [K(c+1)] [V(c)]
     wait_vm<NI>();                     // K(c+1) landed
     wait_lgkm0();
-    asm volatile("" ::: "memory");
+    wg_barrier();
     if constexpr (KVAR) chunk_info(c + 2, ks_2, kl_2);
 
-    // ---- region A: S(c+1) on MFMA || P(c) on VALU
-    uint32_t pw[2][2][2][4];           // [kb][hh][qh][word]
+    // ---- region A: S(c+1) on MFMA || P(c) = exp2(S(c) - m) on VALU.
+    // Step j: K read for step j+3, MFMA j, softmax elements of step j.
+    uint32_t pw[2][2][4];
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
     {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sn[x][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
       bf16x8 kr[4];
       kr[0] = k_read(0);
       kr[1] = k_read(1);
@@ -420,60 +426,51 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         if (j + 3 < NS) kr[(j + 3) & 3] = k_read(j + 3);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-          sn[2 * (j & 1) + q2] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j & 3], qf[q2][j >> 1], sn[2 * (j & 1) + q2], 0, 0, 0);
+        sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j & 3], qf[j >> 1], sn[j & 1], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < EPS; e += 2) {
-          const int el = j * EPS + e;            // element 0..63: qh, kb, r
-          const int q2 = el >> 5, kb = (el >> 4) & 1, r = el & 15;
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * kb + q2][r], a.sl2, -m_run[q2]));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * kb + q2][r + 1], a.sl2, -m_run[q2]));
-          pw[kb][r >> 3][q2][(r & 7) >> 1] = pack2(x0, x1);
+          const int el = j * EPS + e;            // element 0..31 of this lane
+          const int kb = el >> 4, r = el & 15;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], a.sl2, -m_run));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r + 1], a.sl2, -m_run));
+          rsum[el & 3] += x0;
+          rsum[(el + 1) & 3] += x1;
+          pw[kb][r >> 3][(r & 7) >> 1] = pack2(x0, x1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // keep the softmax in region A: without a use here the compiler sinks it
-    // past the refill of the K tile to its consumer, region B
-    asm volatile("" ::"v"(pw[0][0][0][0]), "v"(pw[0][0][0][1]), "v"(pw[0][0][0][2]), "v"(pw[0][0][0][3]),
-                 "v"(pw[0][0][1][0]), "v"(pw[0][0][1][1]), "v"(pw[0][0][1][2]), "v"(pw[0][0][1][3]),
-                 "v"(pw[0][1][0][0]), "v"(pw[0][1][0][1]), "v"(pw[0][1][0][2]), "v"(pw[0][1][0][3]),
-                 "v"(pw[0][1][1][0]), "v"(pw[0][1][1][1]), "v"(pw[0][1][1][2]), "v"(pw[0][1][1][3]));
-    asm volatile("" ::"v"(pw[1][0][0][0]), "v"(pw[1][0][0][1]), "v"(pw[1][0][0][2]), "v"(pw[1][0][0][3]),
-                 "v"(pw[1][0][1][0]), "v"(pw[1][0][1][1]), "v"(pw[1][0][1][2]), "v"(pw[1][0][1][3]),
-                 "v"(pw[1][1][0][0]), "v"(pw[1][1][0][1]), "v"(pw[1][1][0][2]), "v"(pw[1][1][0][3]),
-                 "v"(pw[1][1][1][0]), "v"(pw[1][1][1][1]), "v"(pw[1][1][1][2]), "v"(pw[1][1][1][3]));
-    bf16x8 pf[2][2][2];
+    // past the barriers to its consumer, region B
+    asm volatile("" ::"v"(pw[0][0][0]), "v"(pw[0][0][1]), "v"(pw[0][0][2]), "v"(pw[0][0][3]),
+                 "v"(pw[0][1][0]), "v"(pw[0][1][1]), "v"(pw[0][1][2]), "v"(pw[0][1][3]),
+                 "v"(pw[1][0][0]), "v"(pw[1][0][1]), "v"(pw[1][0][2]), "v"(pw[1][0][3]),
+                 "v"(pw[1][1][0]), "v"(pw[1][1][1]), "v"(pw[1][1][2]), "v"(pw[1][1][3]),
+                 "v"(rsum[0]), "v"(rsum[1]), "v"(rsum[2]), "v"(rsum[3]));
+    l_run += (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-          pf[kb][hh][q2] = __builtin_bit_cast(
-              bf16x8, (u32x4){pw[kb][hh][q2][0], pw[kb][hh][q2][1], pw[kb][hh][q2][2], pw[kb][hh][q2][3]});
+        pf[kb][hh] = __builtin_bit_cast(bf16x8, (u32x4){pw[kb][hh][0], pw[kb][hh][1], pw[kb][hh][2], pw[kb][hh][3]});
 
-    wait_lgkm0();                      // K(c+1) reads done before the buffer is refilled
-    asm volatile("" ::: "memory");
+    wg_barrier();                      // every wave is done reading K(c+1)
     {
+      // K(c+2); without a chunk c+2 a re-load of a chunk that has rows
+      // (c+1 if it exists, else c itself) into the free buffer
       const int kc = kl_2 > 0 ? c + 2 : (kl_n > 0 ? c + 1 : c);
       const int ks_k = kl_2 > 0 ? ks_2 : (kl_n > 0 ? ks_n : ks_c);
       const int kl_k = kl_2 > 0 ? kl_2 : (kl_n > 0 ? kl_n : kl);
       issue_tile(false, ks_k, kl_k, tok + (kc & 3) * 64);
     }
 
-    // ---- region B: O^T += V(c)^T P(c)^T || row max of S(c+1)
+    // ---- region B: O^T += V(c)^T P(c)^T on MFMA || row max of S(c+1)
     // outstanding loads, oldest first: [V(c)] [K(c+2)]
     wait_vm<NI>();                     // V(c) landed
-    asm volatile("" ::: "memory");
+    wg_barrier();
     mask_tail(sn, kl_n);
-    float mx[2] = {-INFINITY, -INFINITY};
-    // row sums of the bf16-rounded P that PV multiplies (so the output is a
-    // convex combination with exactly the weights used), one bf16 dot
-    // product with (1, 1) per packed pair, in the VALU slack of region B
-    float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    float mx = -INFINITY;
     {
       bf16x8 vr[4];
       vr[0] = v_read(0);
@@ -483,37 +480,24 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
       for (int j = 0; j < NS; ++j) {
         if (j + 3 < NS) vr[(j + 3) & 3] = v_read(j + 3);
         const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-          oacc[dg][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j & 3], pf[kb][hh][q2], oacc[dg][q2], 0, 0, 0);
+        oacc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j & 3], pf[kb][hh], oacc[dg], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < EPS; e += 2) {
           const int el = j * EPS + e;
-          const int q2 = el >> 5, kb2 = (el >> 4) & 1, r = el & 15;
-          mx[q2] = fmaxf(mx[q2], fmaxf(sn[2 * kb2 + q2][r], sn[2 * kb2 + q2][r + 1]));
-        }
-        // the 8 words of pf[kb][hh][*] are summed over the D/32 steps that use them
-#pragma unroll
-        for (int u = 0; u < 8 / (D / 32); ++u) {
-          const int wi = dg * (8 / (D / 32)) + u;          // word 0..7 of this (kb, hh)
-          const int q2 = wi >> 2;
-          rsum[q2][u & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kb][hh][q2][wi & 3]),
-                                                            __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                                            rsum[q2][u & 1], false);
+          mx = fmaxf(mx, fmaxf(sn[el >> 4][el & 15], sn[el >> 4][(el & 15) + 1]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) l_run[q2] += rsum[q2][0] + rsum[q2][1];
-    wait_lgkm0();                      // V(c) reads done before the buffer is refilled
-    asm volatile("" ::: "memory");
+    wg_barrier();                      // every wave is done reading V(c)
     {
+      // V(c+1), or a re-load of chunk c's rows when there is no chunk c+1
       const bool more = kl_n > 0;
       const int vc = more ? c + 1 : c;
       issue_tile(true, more ? ks_n : ks_c, more ? kl_n : kl, tok + (vc & 3) * 64);
     }
-    settle_max(mx);
+    settle_max(mx);                    // reference max for S(c+1)
+    // advance: chunk c+1 becomes current
     ks_c = ks_n; kl = kl_n;
     ks_n = ks_2; kl_n = kl_2;
     ++c;
@@ -522,25 +506,24 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
 
   if (kl0 > 0) {
     issue_tile(false, ks0, kl0, tok);
-    wait_vm<0>();
-    asm volatile("" ::: "memory");
+    wait_vm<0>();                      // K0 landed
+    wg_barrier();
     compute_s(sA);
-    wait_lgkm0();
-    asm volatile("" ::: "memory");
+    wg_barrier();
     {
       const bool more = kl1 > 0;
       issue_tile(false, more ? ks1 : ks0, more ? kl1 : kl0, tok + (more ? 1 : 0) * 64);
     }
+    // V0 after K1: an iteration starts with loads outstanding in the order
+    // [K(c+1)] [V(c)]
     issue_tile(true, ks0, kl0, tok);
     mask_tail(sA, kl0);
     {
-      float mx[2] = {-INFINITY, -INFINITY};
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx[q2] = fmaxf(mx[q2], sA[2 * kb + q2][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sA[kb][r]);
       settle_max(mx);
     }
     for (;;) {
@@ -549,31 +532,29 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     }
   }
   wait_vm<0>();                        // no load may still target LDS
-  asm volatile("" ::: "memory");
 
-  // ---- epilogue: O = O^T / l, staged through the K tile, stored as bf16 rows
+  // ---- epilogue: O = O^T / l, staged through the K tile (swizzled rows),
+  // stored as bf16 rows.
+  const float lt = halves_sum(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int orow = 32 * wave + l32;
+  const int fo = swz<D>(orow & 15);
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const float lt = halves_sum(l_run[q2]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int orow = 32 * q2 + l32;
-    const int fo = swz<D>(orow & 15);
+  for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const u32x2 w = {pack2(oacc[dg][q2][4 * j4 + 0] * inv, oacc[dg][q2][4 * j4 + 1] * inv),
-                         pack2(oacc[dg][q2][4 * j4 + 2] * inv, oacc[dg][q2][4 * j4 + 3] * inv)};
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-            Kp + orow * ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
-      }
-  }
+    for (int j4 = 0; j4 < 4; ++j4) {
+      // channels 32dg + 8*j4 + 4*half .. +3 = piece 4dg + j4, byte 8*half
+      const u32x2 w = {pack2(oacc[dg][4 * j4 + 0] * inv, oacc[dg][4 * j4 + 1] * inv),
+                       pack2(oacc[dg][4 * j4 + 2] * inv, oacc[dg][4 * j4 + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          Kp + orow * ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
+    }
   wait_lgkm0();
-  asm volatile("" ::: "memory");
+  wg_barrier();
   uint16_t* oh = a.o + head_off;
 #pragma unroll
-  for (int r = 0; r < TILE / 16 / 64; ++r) {
-    const int u = lane + 64 * r;            // 16-byte piece of the 64 x D tile
+  for (int r = 0; r < TILE / 16 / 128; ++r) {
+    const int u = tid + 128 * r;            // 16-byte piece of the 64 x D tile
     const int row = u / PPR, p = u % PPR;
     if (row < ql)
       *reinterpret_cast<u32x4*>(oh + (size_t)(qs + row) * D + p * 8) =
@@ -583,7 +564,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
 }
 
 template <int D, bool QVAR, bool KVAR>
-__global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = 64 * D * 2;
   __shared__ __align__(16) unsigned char Ks[TILE];
   __shared__ __align__(16) unsigned char Vs[TILE];
@@ -760,7 +741,7 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.bh = BH;
   const long long grid = 8LL * (((long long)BH * a.tiles + 7) / 8);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-#define BSA_ATTN(DD, QV, KV) attn_fwd_kernel<DD, QV, KV><<<(int)grid, 64, 0, s>>>(a)
+#define BSA_ATTN(DD, QV, KV) attn_fwd_kernel<DD, QV, KV><<<(int)grid, 128, 0, s>>>(a)
   if (d == 128) {
     if (qvar && kvar) BSA_ATTN(128, true, true);
     else if (qvar) BSA_ATTN(128, true, false);

@@ -119,8 +119,8 @@ int bsa_pool_blocks(const void* x, int B, int H, int N, int d, int n_valid,
  * computed exactly on the fp32 values p_J: order the blocks lightest first
  * (equal p: higher J lighter), drop J exactly when the inclusive cumulative
  * mass up to J is below thr times the row total. Masses are summed in
- * 2^-40 fixed point, so the result does not depend on summation order and
- * is bit-reproducible. thr = 0 keeps every block; the heaviest block is
+ * 2^-31 fixed point (m_J = floor(p_J * 2^31), 64-bit sums), so the result
+ * does not depend on summation order and is bit-reproducible. thr = 0 keeps every block; the heaviest block is
  * always kept. The window, if any, is OR'd in afterwards.
  *
  *   qbar     fp32 [B,H,nqb,d], kbar fp32 [B,H,nkb,d] (device), d in {64,128}
@@ -193,7 +193,8 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
  * on bf16 MFMA with fp32 accumulation; the softmax is an fp32 online
  * softmax. A query block with no kept key block gets zero rows.
  *
- *   q, k, v   bf16 [B,H,N,d] (device), d in {64, 128}
+ *   q, k, v   bf16 [B,H,N,d] (device), d in {64, 128}, finite values (the
+ *             kernel is built without NaN semantics)
  *   o         bf16 [B,H,N,d] (device); every row of every query block is
  *             written, rows n_valid..N-1 are zeroed, other rows untouched
  *   qb, kb    block descriptors (NULL = uniform `block`-token blocks,
