@@ -20,7 +20,8 @@ OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "permute.hip", "kmeans.hip"]
+SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_fwd_1w.hip", "permute.hip",
+           "kmeans.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -37,10 +38,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# Per-source flags. The attention kernel assumes finite inputs: without NaN
-# semantics its running row maxima need no quieting of the MFMA results
+# Per-source flags. The attention kernels assume finite inputs: without NaN
+# semantics their running row maxima need no quieting of the MFMA results
 # (one v_max_f32 per score fewer).
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_fwd_1w.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

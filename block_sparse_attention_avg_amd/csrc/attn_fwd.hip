@@ -31,28 +31,12 @@
 //                      its key order matches the accumulator layout of S^T.
 // O is divided by the row sum once at the end, staged through LDS and
 // written as bf16 rows.
-#include "common.h"
+#include "attn.h"
 
 #include <math.h>
 
 namespace bsa {
 
-struct AttnArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  int N, n_valid, nqb, nkb;
-  Blocks qb, kb;
-  const int32_t* tile_base;   // variable query blocks: [BH][nqb + 1] tile prefix
-  const int32_t* order;       // uniform query blocks: [BH][nqb] processing order
-  int tiles;                  // tiles per (b, h)
-  int bh;                     // B * H
-  const int32_t* kv_count;
-  const int32_t* kv_index;
-  int kv_stride;
-  float sl2;                  // scale * log2(e)
-};
 
 namespace {
 
@@ -701,6 +685,9 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(uint4* __restrict__ o, i
   }
 }
 
+// Key-block count from which uniform d = 128 attention runs one wave per tile.
+constexpr int kOneWaveKeyBlocks = 1024;
+
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int BH, int N, int d, int n_valid, const Blocks& qb, const Blocks& kb,
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
@@ -741,6 +728,12 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.bh = BH;
   const long long grid = 8LL * (((long long)BH * a.tiles + 7) / 8);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  // Rows over many key blocks (large heads) leave the kernel bound by K/V
+  // traffic that mostly misses L2; there one wave per 64-row tile, which
+  // shares each K/V operand read between both query halves, does better
+  // (measured at 1857 key blocks: +8..11 %; at 512: -12 %).
+  if (d == 128 && !qvar && !kvar && a.order && kb.nblocks >= kOneWaveKeyBlocks)
+    return launch_attn_fwd_1w(a, (int)grid, s);
 #define BSA_ATTN(DD, QV, KV) attn_fwd_kernel<DD, QV, KV><<<(int)grid, 128, 0, s>>>(a)
   if (d == 128) {
     if (qvar && kvar) BSA_ATTN(128, true, true);

@@ -328,6 +328,52 @@ def test_hunyuan720_sampled(gpu_lib, part):
         _attn_case(gpu_lib, w, q, k, v, [4, 19], 5)
 
 
+def test_attn_long_rows_one_wave_path(gpu_lib):
+    # >= 1024 key blocks at d = 128 with uniform blocks selects the one-wave
+    # kernel: random kept lists (dense and single-block rows, the ragged last
+    # block) on a ragged length, sampled query blocks against the oracle, then
+    # repeat runs and poisoned padding must give the same bits
+    bsa = gpu_lib
+    H, d, nkb = 2, 128, 1025
+    N = nkb * 64
+    nv = N - 37
+    say(f"attention one-wave path H={H} N={N} n_valid={nv}")
+    rng = np.random.default_rng(1025)
+    x = rng.normal(size=(3, 1, H, N, d)).astype(np.float32)
+    x[:, :, :, nv:] = 0
+    q, k, v = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(3))
+    st, ln = ol.raster_blocks(nv)
+    assert len(st) == nkb
+    keep = rng.random((H, nkb, nkb)) < 0.03
+    keep[:, :, nkb - 1] |= rng.random((H, nkb)) < 0.3       # ragged last key block
+    keep[:, 5, :] = True                                     # one dense row
+    keep[:, 9, :] = False
+    keep[:, 9, 700] = True                                   # one single-block row
+    keep[:, :, 0] |= ~keep.any(2)
+    cnt = keep.sum(2).astype(np.int32)
+    idx = np.full((H, nkb, nkb), -1, np.int32)
+    for h in range(H):
+        for i in range(nkb):
+            ids = np.nonzero(keep[h, i])[0]
+            idx[h, i, :len(ids)] = ids
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cd, id_ = torch.from_numpy(cnt[None]).cuda(), torch.from_numpy(idx[None]).cuda()
+    o1 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    o = _np(o1)
+    blocks = sorted({0, 5, 9, nkb - 1} | set(rng.choice(nkb, 10, replace=False).tolist()))
+    for h in range(H):
+        ref = oa.masked_attention(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), st, ln, st, ln, keep[h],
+                                  blocks=blocks)
+        _check_out(o[0, h], ref, _rows_of(st, ln, blocks), f"head {h} ({len(blocks)} query blocks)")
+    assert (o[:, :, nv:] == 0).all()
+    o2 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    assert torch.equal(o1, o2)
+    for t in (qd, kd, vd):
+        t[:, :, nv:] = float("nan")
+    o3 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    assert torch.equal(o1, o3)
+
+
 def _random_partition(rng, n, lens=(0, 1, 7, 17, 33, 64, 65, 100, 150, 230)):
     st, ln, pos = [], [], 0
     while pos < n:
