@@ -254,12 +254,12 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
                 js = [json.loads(l) for l in f if l.startswith("{")]
             if js:
                 b = js[-1]
-                att = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::attn_fwd_kernel")]
+                att = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::attn_fwd")]
                 lines.append(f"bench (same run): attention stage {b['stages_ms']['attention'] * 1e3:.1f} us per "
                              f"call (HIP events around the C-ABI call), roofline.achieved "
                              f"{b['roofline']['achieved']} TFLOP/s")
                 if att:
-                    lines.append(f"rocprof attn_fwd_kernel average {att[0][2]:.1f} us "
+                    lines.append(f"rocprof {att[0][0]} average {att[0][2]:.1f} us "
                                  f"(ratio events / kernel {b['stages_ms']['attention'] * 1e3 / att[0][2]:.3f})")
     elif kind == "counters":
         lines.append(f"command: {command}")
