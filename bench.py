@@ -122,9 +122,32 @@ class Runner:
             e[2].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        self.attn_each = [e[1].elapsed_time(e[2]) for e in evs]
         t_mask = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-        t_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        t_attn = sum(self.attn_each) / steps
         return wall / steps * 1e3, t_mask, t_attn
+
+    def cold(self, reps: int, scratch_mib: int = 512):
+        """Median mask / attention times with the caches flushed before each step.
+
+        A scratch buffer larger than the 256 MB Infinity Cache is overwritten
+        before every step (outside the timed events), so Q, K, V come from HBM.
+        """
+        scratch = torch.empty(scratch_mib << 20, dtype=torch.uint8, device=self.q.device)
+        tm, ta = [], []
+        for _ in range(reps):
+            scratch.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            self.mask()
+            e[1].record()
+            self.attn()
+            e[2].record()
+            torch.cuda.synchronize()
+            tm.append(e[0].elapsed_time(e[1]))
+            ta.append(e[1].elapsed_time(e[2]))
+        del scratch
+        return float(np.median(tm)), float(np.median(ta))
 
     def summary(self, ms_step, t_mask, t_attn):
         w = self.w
@@ -149,6 +172,30 @@ class Runner:
             "kept_per_row_mean": float(cnt.mean()),
             "kept_per_row_max": int(cnt.max()),
         }
+
+
+def attn_kernel_name(w) -> str:
+    # the library runs one wave per tile for uniform d = 128 rows over at
+    # least 1024 key blocks, two waves per tile otherwise
+    nb = -(-w.n_valid // w.block)
+    return "attn_fwd_1w_kernel" if (w.d == 128 and nb >= 1024) else "attn_fwd_kernel"
+
+
+def dense_gemm_ref(dev, n: int = 8192, reps: int = 20):
+    """bf16 dense GEMM throughput of the vendor library on this machine (TFLOP/s)."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    return 2.0 * n ** 3 / t / 1e12
 
 
 def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
@@ -322,6 +369,9 @@ def main():
     ap.add_argument("--config", default="wan480", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="hunyuan720", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="extra steps timed with flushed caches (reported under cold_cache; 0 = skip)")
+    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the dense bf16 GEMM reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (identity token permutation of "
                          "1 GiB of bf16 rows) to calibrate hardware byte counters")
@@ -375,7 +425,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel",
+            "kernel": attn_kernel_name(w),
             "achieved": round(s["attn_tflops"], 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -388,10 +438,23 @@ def main():
                      "kept_per_row_mean": round(s["kept_per_row_mean"], 2),
                      "kept_per_row_max": s["kept_per_row_max"]},
         "stages_ms": {"mask": round(t_mask, 4), "attention": round(t_attn, 4),
+                      "attention_median": round(float(np.median(r.attn_each)), 4),
+                      "attention_min": round(float(np.min(r.attn_each)), 4),
                       "mask_over_attention": round(s["mask_over_attn"], 4),
                       "mask_gbs": round(s["mask_gbs"], 1)},
         "flops_eff_per_step": s["flops_eff"],
     }
+    if a.cold_reps > 0:
+        cm, ca = r.cold(a.cold_reps)
+        line["cold_cache"] = {"mask_ms": round(cm, 4), "attention_ms": round(ca, 4),
+                              "attn_tflops": round(s["flops_eff"] / (ca * 1e-3) / 1e12, 3),
+                              "reps": a.cold_reps,
+                              "how": "median; 512 MiB written before each step (outside the events)"}
+    if not a.no_gemm_ref:
+        g = dense_gemm_ref(dev)
+        line["dense_gemm_ref"] = {"tflops": round(g, 1), "frac_of_peak": round(g / PEAK_BF16_TFLOPS, 4),
+                                  "attn_over_gemm": round(s["attn_tflops"] / g, 4),
+                                  "how": "torch.matmul bf16 8192x8192x8192 (vendor GEMM) on this box"}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r, s["flops_eff"])
     if a.also and a.also != "none" and a.also != a.config:
@@ -406,6 +469,7 @@ def main():
             "ms_per_step": round(m2, 4),
             "step_tflops": round(s2["step_tflops"], 3),
             "attn_tflops": round(s2["attn_tflops"], 3),
+            "attn_kernel": attn_kernel_name(w2),
             "pct_bf16_peak_attn": round(100 * s2["attn_frac_of_peak"], 2),
             "mask_ms": round(tm2, 4),
             "attention_ms": round(ta2, 4),
