@@ -174,6 +174,20 @@ class Runner:
         }
 
 
+def mfma_probe():
+    """Sustained bf16 MFMA rate from the measurement program built beside the
+    library (a child process; None when it is missing or fails)."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_sparse_attention_avg_amd", "mfma_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except Exception:
+        return None
+
+
 def attn_kernel_name(w) -> str:
     # the library runs one wave per tile for uniform d = 128 rows over at
     # least 1024 key blocks, two waves per tile otherwise
@@ -371,7 +385,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="extra steps timed with flushed caches (reported under cold_cache; 0 = skip)")
-    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the dense bf16 GEMM reference")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the MFMA-rate probe and the dense bf16 GEMM reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (identity token permutation of "
                          "1 GiB of bf16 rows) to calibrate hardware byte counters")
@@ -451,6 +466,10 @@ def main():
                               "reps": a.cold_reps,
                               "how": "median; 512 MiB written before each step (outside the events)"}
     if not a.no_gemm_ref:
+        mp = mfma_probe()
+        if mp:
+            mp["attn_over_probe"] = round(s["attn_tflops"] / mp["tflops"], 4)
+            line["mfma_probe"] = mp
         g = dense_gemm_ref(dev)
         line["dense_gemm_ref"] = {"tflops": round(g, 1), "frac_of_peak": round(g / PEAK_BF16_TFLOPS, 4),
                                   "attn_over_gemm": round(s["attn_tflops"] / g, 4),

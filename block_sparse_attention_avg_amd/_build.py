@@ -18,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
+PROBE = os.path.join(PKG, "mfma_probe")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_fwd_1w.hip", "permute.hip",
@@ -63,8 +64,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # measurement helper for bench.py (a program, not part of the library)
+    cmd = [_hipcc(), *FLAGS, "-x", "hip", os.path.join(CSRC, "mfma_probe.hip"), "-o", PROBE + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for mfma_probe.hip:\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
 
 
