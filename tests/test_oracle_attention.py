@@ -89,3 +89,97 @@ def test_permutation_equivariance():
     bq[pq] = np.repeat(np.arange(3), ql)
     bk[pk] = np.repeat(np.arange(3), kl)
     np.testing.assert_allclose(o, _sdpa(q, k, v, keep[bq][:, bk]), atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward
+
+def _token_mask(qstart, qlen, kstart, klen, keep, N):
+    m = np.zeros((N, N), dtype=bool)
+    for I in range(len(qstart)):
+        for J in np.nonzero(keep[I])[0]:
+            m[qstart[I]:qstart[I] + qlen[I], kstart[J]:kstart[J] + klen[J]] = True
+    return m
+
+
+def _autograd_masked(q, k, v, do, m, scale):
+    # torch autograd of softmax(scale Q K^T + log mask) V in float64
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * qt @ kt.T
+    s = s.masked_fill(~torch.tensor(m), float("-inf"))
+    o = torch.softmax(s, dim=1) @ vt
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    lse = torch.logsumexp(s.detach(), dim=1).numpy()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(), lse
+
+
+def _random_case(seed, N, d, nb):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.normal(size=(N, d)) for _ in range(4))
+    st, ln = ol.raster_blocks(N, N // nb)
+    keep = rng.random((len(st), len(st))) < 0.4
+    keep[np.arange(len(st)), rng.integers(0, len(st), len(st))] = True    # every row keeps one
+    return q, k, v, do, st, ln, keep
+
+
+def test_backward_all_blocks_kept_is_dense_autograd():
+    q, k, v, do, st, ln, _ = _random_case(1, 96, 8, 4)
+    keep = np.ones((len(st), len(st)), bool)
+    dq, dk, dv = oa.masked_attention_bwd(q, k, v, do, st, ln, st, ln, keep)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None])[0]
+    o.backward(torch.tensor(do))
+    for a, b in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_and_lse_match_autograd_of_token_masked_softmax():
+    q, k, v, do, st, ln, keep = _random_case(2, 120, 8, 5)
+    scale = 0.37
+    dq, dk, dv = oa.masked_attention_bwd(q, k, v, do, st, ln, st, ln, keep, scale=scale)
+    lse = oa.masked_attention_lse(q, k, st, ln, st, ln, keep, scale=scale)
+    rq, rk, rv, rl = _autograd_masked(q, k, v, do, _token_mask(st, ln, st, ln, keep, len(q)), scale)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv), (lse, rl)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    # variable block lengths; loss = sum(O * do)
+    rng = np.random.default_rng(3)
+    N, d = 11, 3
+    q, k, v, do = (rng.normal(size=(N, d)) for _ in range(4))
+    st, ln = np.array([0, 4, 5]), np.array([4, 1, 6])
+    keep = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], bool)
+    dq, dk, dv = oa.masked_attention_bwd(q, k, v, do, st, ln, st, ln, keep)
+
+    def loss(qq, kk, vv):
+        return float((oa.masked_attention(qq, kk, vv, st, ln, st, ln, keep) * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for i, j in ((0, 0), (4, 2), (7, 1), (10, 0)):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += h
+            xm[i, j] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[i, j]) < 1e-6 * max(1.0, abs(fd)), (name, i, j, fd, g[i, j])
+
+
+def test_backward_one_key_rows_closed_form():
+    # every query block keeps a single one-token key block: P = 1, so the
+    # scores get no gradient and dv is the upstream gradient summed per key
+    rng = np.random.default_rng(4)
+    N, d = 8, 4
+    q, k, v, do = (rng.normal(size=(N, d)) for _ in range(4))
+    qst, qln = np.array([0, 4]), np.array([4, 4])
+    kst, kln = np.array([2, 6]), np.array([1, 1])
+    keep = np.array([[1, 0], [0, 1]], bool)
+    dq, dk, dv = oa.masked_attention_bwd(q, k, v, do, qst, qln, kst, kln, keep)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    ref = np.zeros_like(v)
+    ref[2] = do[0:4].sum(0)
+    ref[6] = do[4:8].sum(0)
+    np.testing.assert_allclose(dv, ref, rtol=1e-14, atol=1e-14)
+    lse = oa.masked_attention_lse(q, k, qst, qln, kst, kln, keep)
+    np.testing.assert_allclose(lse[:4], q[:4] @ k[2] / 2.0, rtol=1e-14)
