@@ -50,6 +50,11 @@ _SIGS = {
     "bsa_build_centroid_mask": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P], _I),
     "bsa_block_sparse_attn_fwd_workspace": ([_I, _I, _I, _P], _Z),
     "bsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z, _P], _I),
+    "bsa_block_sparse_attn_fwd_lse": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z,
+                                       _P], _I),
+    "bsa_block_sparse_attn_bwd_workspace": ([_I, _I, _I], _Z),
+    "bsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _F, _P, _P, _P, _P,
+                                   _Z, _P], _I),
     "bsa_permute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "bsa_unpermute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "bsa_fractal_order": ([_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_I)], _I),
@@ -268,6 +273,85 @@ def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
                                          0 if workspace is None else workspace.numel(),
                                          _stream(q.device)), "block_sparse_attn_fwd")
     return o
+
+
+def block_sparse_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_count: torch.Tensor,
+                              kv_index: torch.Tensor, n_valid: Optional[int] = None, block: int = 64,
+                              qb: Optional[Blocks] = None, kb: Optional[Blocks] = None, scale: float = 0.0,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The forward, plus each row's fp32 softmax log-normaliser [B, H, N]."""
+    B, H, N, d = _qkv(q, "q")
+    for t, n in ((k, "k"), (v, "v")):
+        if _qkv(t, n) != q.shape:
+            raise ValueError(f"{n} must have the shape of q")
+    _dev_tensor(kv_count, torch.int32, "kv_count")
+    _dev_tensor(kv_index, torch.int32, "kv_index")
+    n_valid = N if n_valid is None else n_valid
+    nqb = _nblocks(qb, n_valid, block)
+    if kv_count.numel() != B * H * nqb:
+        raise ValueError("kv_count must have B*H*nqb entries")
+    kv_stride = kv_index.shape[-1]
+    if kv_index.numel() != B * H * nqb * kv_stride:
+        raise ValueError("kv_index must be [B, H, nqb, kv_stride]")
+    o = torch.empty_like(q) if out is None else _dev_tensor(out, torch.bfloat16, "out")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _dev_tensor(lse, torch.float32, "lse")
+    if lse.numel() != B * H * N:
+        raise ValueError("lse must have B*H*N entries")
+    lib = load()
+    qbc, kbc = (None if qb is None else qb._c()), (None if kb is None else kb._c())
+    ws_bytes = lib.bsa_block_sparse_attn_fwd_workspace(B, H, nqb, None if qbc is None else ctypes.byref(qbc))
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_block_sparse_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                             lse.data_ptr(), B, H, N, d, n_valid, block,
+                                             None if qbc is None else ctypes.byref(qbc),
+                                             None if kbc is None else ctypes.byref(kbc), kv_count.data_ptr(),
+                                             kv_index.data_ptr(), kv_stride, scale,
+                                             None if workspace is None else workspace.data_ptr(),
+                                             0 if workspace is None else workspace.numel(),
+                                             _stream(q.device)), "block_sparse_attn_fwd_lse")
+    return o, lse
+
+
+def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          dout: torch.Tensor, lse: torch.Tensor, kv_count: torch.Tensor,
+                          kv_index: torch.Tensor, n_valid: Optional[int] = None, block: int = 64,
+                          scale: float = 0.0, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv) of the block-sparse attention (uniform blocks)."""
+    B, H, N, d = _qkv(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        if _qkv(t, n) != q.shape:
+            raise ValueError(f"{n} must have the shape of q")
+    _dev_tensor(lse, torch.float32, "lse")
+    if lse.numel() != B * H * N:
+        raise ValueError("lse must have B*H*N entries")
+    _dev_tensor(kv_count, torch.int32, "kv_count")
+    _dev_tensor(kv_index, torch.int32, "kv_index")
+    n_valid = N if n_valid is None else n_valid
+    nqb = -(-n_valid // block)
+    if kv_count.numel() != B * H * nqb:
+        raise ValueError("kv_count must have B*H*nqb entries")
+    kv_stride = kv_index.shape[-1]
+    if kv_index.numel() != B * H * nqb * kv_stride:
+        raise ValueError("kv_index must be [B, H, nqb, kv_stride]")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if _qkv(t, n) != q.shape:
+            raise ValueError(f"{n} must have the shape of q")
+    lib = load()
+    ws_bytes = lib.bsa_block_sparse_attn_bwd_workspace(B, H, N)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_block_sparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                         lse.data_ptr(), B, H, N, d, n_valid, block, kv_count.data_ptr(),
+                                         kv_index.data_ptr(), kv_stride, scale, dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                         _stream(q.device)), "block_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------------ reorder

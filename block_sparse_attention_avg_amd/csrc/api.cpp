@@ -187,10 +187,10 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb, const bsa_bloc
   return round256(sizeof(int32_t) * (size_t)B * H * (nqb + 1));
 }
 
-int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-                              int n_valid, int block, const bsa_blocks* qb, const bsa_blocks* kb,
-                              const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
+static int attn_fwd_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                         int n_valid, int block, const bsa_blocks* qb, const bsa_blocks* kb,
+                         const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_msg[0] = 0;
   if (int e = check_shape(B, H, N, d, n_valid)) return e;
   if (!q || !k || !v || !o || !kv_count || !kv_index) return fail(BSA_EINVAL, "attn_fwd: null pointer");
@@ -209,8 +209,61 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void*
   return hip_status(bsa::launch_attn_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), B * H, N, d,
                                          n_valid, bq, bk, kv_count, kv_index, kv_stride, sc,
-                                         static_cast<int32_t*>(ws), stream),
+                                         static_cast<int32_t*>(ws), lse, stream),
                     "attn_fwd");
+}
+
+int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                              int n_valid, int block, const bsa_blocks* qb, const bsa_blocks* kb,
+                              const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  return attn_fwd_impl(q, k, v, o, B, H, N, d, n_valid, block, qb, kb, kv_count, kv_index, kv_stride, scale,
+                       nullptr, ws, ws_bytes, stream);
+}
+
+int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                  int N, int d, int n_valid, int block, const bsa_blocks* qb,
+                                  const bsa_blocks* kb, const int32_t* kv_count, const int32_t* kv_index,
+                                  int kv_stride, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (!lse) return fail(BSA_EINVAL, "attn_fwd_lse: null lse");
+  if (!aligned16(lse)) return fail(BSA_EINVAL, "attn_fwd_lse: lse must be 16-byte aligned");
+  return attn_fwd_impl(q, k, v, o, B, H, N, d, n_valid, block, qb, kb, kv_count, kv_index, kv_stride, scale, lse,
+                       ws, ws_bytes, stream);
+}
+
+size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return bsa::attn_bwd_workspace(B * H, N, (N + 63) / 64);
+}
+
+int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, int B, int H, int N, int d, int n_valid, int block,
+                              const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                              void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (!q || !k || !v || !o || !dout || !lse || !kv_count || !kv_index || !dq || !dk || !dv)
+    return fail(BSA_EINVAL, "attn_bwd: null pointer");
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(BSA_EINVAL, "attn_bwd: tensors must be 16-byte aligned");
+  if (block != 64) return fail(BSA_EUNSUPPORTED, "attn_bwd: block must be 64");
+  if ((long long)N * d * 2 > 0xFFFFFFFFLL)
+    return fail(BSA_EUNSUPPORTED, "attn_bwd: one head (N*d*2 bytes) must be below 4 GiB");
+  const int nb = (n_valid + 63) / 64;
+  if (kv_stride < 0 || (nb > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_bwd: bad kv_stride");
+  const size_t need = bsa_block_sparse_attn_bwd_workspace(B, H, N);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(BSA_ENOSPC, "attn_bwd: workspace %zu bytes < %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(BSA_EINVAL, "attn_bwd: workspace must be 16-byte aligned");
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return hip_status(bsa::launch_attn_bwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+                                         static_cast<const uint16_t*>(dout), lse, B * H, N, d, n_valid, kv_count,
+                                         kv_index, kv_stride, sc, static_cast<uint16_t*>(dq),
+                                         static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), ws, stream),
+                    "attn_bwd");
 }
 
 static int permute_common(const void* x, void* y, const int32_t* perm, int B, int H, int N, int d,

@@ -20,6 +20,7 @@ struct AttnArgs {
   const int32_t* kv_index;
   int kv_stride;
   float sl2;                  // scale * log2(e)
+  float* lse;                 // null, or [BH][N] natural-log row normaliser of the scaled scores
 };
 
 // One-wave kernel (attn_fwd_1w.hip): uniform 64-token blocks, d = 128,

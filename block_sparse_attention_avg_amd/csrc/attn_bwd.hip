@@ -1,0 +1,589 @@
+// Block-sparse attention backward: dQ, dK, dV of the forward in attn_fwd.hip
+// over the same kept-block lists (NABLA summary, Contributi Chiave,
+// "Accelerazione a Due Fasi", and Risultati Sperimentali 2: the sparse
+// attention is used in pre-training and fine-tuning too, so its gradient runs
+// over the same tiles). Uniform 64-token blocks, d in {64, 128}.
+//
+// Per query block I and kept key block J (S, P, dP, dS are 64 x 64 tiles):
+//   S  = scale Q_I K_J^T,   P = exp(S - lse_I)     (lse from the forward)
+//   dP = dO_I V_J^T,        dS = P * (dP - Dr_I)   (Dr_i = dO_i . O_i)
+//   dQ_I += scale dS K_J,   dK_J += scale dS^T Q_I,   dV_J += P^T dO_I
+// Three kernels, each deterministic (no atomics on the gradients):
+//   bwd_dot_kernel   Dr = rowsum(dO * O), fp32;
+//   bwd_dq_kernel    one 64-row query tile per workgroup (2 waves x 32 rows),
+//                    walks the tile's kept key blocks (the forward's lists);
+//   bwd_dkdv_kernel  one 64-key tile per workgroup (2 waves x 32 keys), walks
+//                    the query blocks that kept it: the lists transposed by
+//                    the csc_* kernels (a bit matrix, then ascending lists).
+// The MFMA layouts are those of the forward: a 32 x 32 accumulator whose
+// lane holds one column (query, resp. key) and 16 rows; the second product of
+// each pair takes its bf16 B operand straight from that accumulator, and the
+// A operand through the LDS transpose read whose row order matches it.
+#include "common.h"
+
+#include <math.h>
+
+namespace bsa {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(4))) const int32_t cint;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Swizzle of the 16-byte piece index inside a tile row (as in the forward).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  else return (r >> 1) & 7;
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
+// Tile geometry shared by the two gradient kernels: 64 rows of D bf16,
+// row-major in LDS with swizzled 16-byte pieces; wave w of 2 loads rows
+// 32w .. 32w+31.
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int NI = BYTES / 1024 / 2;      // direct-to-LDS loads per wave
+  static constexpr int RPI = 1024 / ROWB;          // rows per load
+  static constexpr int PPR = ROWB / 16;            // 16-byte pieces per row
+};
+
+// Lane offsets of a wave's share of a 64-row tile load.
+template <int D>
+__device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int r = (wave * T::NI + i) * T::RPI + lane / T::PPR;
+    off[i] = r * T::ROWB + (((lane % T::PPR) ^ swz<D>(r & 15)) << 4);
+  }
+}
+// Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros.
+template <int D>
+__device__ __forceinline__ void tile_load(const uint16_t* head, int r0, int n, lds_u8* dst, int wave,
+                                          const uint32_t* off) {
+  using T = Tile<D>;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)max(n, 0) * T::ROWB);
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) dma16(rs, dst + (wave * T::NI + i) * 1024, off[i]);
+}
+// Row operand: lane supplies row (32 g + l32), channels 16 c + 8 half .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_read(const lds_u8* t, int g, int c, int l32, int half) {
+  const int off = (32 * g + l32) * Tile<D>::ROWB + (((2 * c + half) ^ swz<D>(l32 & 15)) << 4);
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off);
+}
+// Transposed operand through the LDS transpose read: lane receives channel
+// 32 dg + l32 of rows 32 g + 16 hh + (8 t + 4 half + 0..3, t = 0, 1): the row
+// order of the accumulator layout (see the forward).
+template <int D>
+struct TrOffsets {
+  int voff[D / 32][2];
+  __device__ __forceinline__ TrOffsets(int lane) {
+    const int half = lane >> 5, g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 8 * t + 4 * half + sj;
+        const int piece = 4 * dg + 2 * g16 + (sq >> 1);
+        voff[dg][t] = row * Tile<D>::ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
+      }
+  }
+};
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(const lds_u8* t, const TrOffsets<D>& o, int g, int hh, int dg) {
+  const lds_u8* b = t + (32 * g + 16 * hh) * Tile<D>::ROWB;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][0]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator element r of a 32 x 32 tile: row 8 (r / 4) + 4 half + (r & 3).
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// 64 x D accumulator tile (transposed: channels x rows, 32 rows per wave) ->
+// bf16 rows [r0, r0 + n) of `out`, staged through `stage` (a free tile).
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16* acc, float mul, lds_u8* stage, uint16_t* out, int r0,
+                                           int n, int wave, int lane) {
+  using T = Tile<D>;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int orow = 32 * wave + l32;
+  const int fo = swz<D>(orow & 15);
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const u32x2 w = {pack2(acc[dg][4 * j4 + 0] * mul, acc[dg][4 * j4 + 1] * mul),
+                       pack2(acc[dg][4 * j4 + 2] * mul, acc[dg][4 * j4 + 3] * mul)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + orow * T::ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
+    }
+  wg_barrier();
+#pragma unroll
+  for (int r = 0; r < T::BYTES / 16 / 128; ++r) {
+    const int u = threadIdx.x + 128 * r;
+    const int row = u / T::PPR, p = u % T::PPR;
+    if (row < n)
+      *reinterpret_cast<u32x4*>(out + (size_t)(r0 + row) * D + p * 8) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              stage + row * T::ROWB + ((p ^ swz<D>(row & 15)) << 4));
+  }
+}
+
+}  // namespace
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;           // [BH][N] natural-log row normaliser from the forward
+  float* dr;                  // [BH][N] rowsum(dO * O), written by bwd_dot_kernel
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int N, n_valid, nqb, nkb;
+  const int32_t* kv_count;    // [BH][nqb] kept key blocks per query block
+  const int32_t* kv_index;    // [BH][nqb][kv_stride]
+  int kv_stride;
+  int32_t* q_count;           // [BH][nkb] query blocks that kept each key block
+  int32_t* q_index;           // [BH][nkb][nqb], ascending
+  uint32_t* bits;             // [BH][nkb][W] bit matrix key block x query block
+  int W;                      // 32-bit words per bit-matrix row
+  float scale;
+};
+
+// Dr[row] = sum_c dO[row, c] O[row, c] (fp32), 0 on pad rows.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a, size_t rows) {
+  constexpr int LPR = D / 8;                       // lanes per row, 8 channels each
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / LPR;
+  const int part = (int)(gid % LPR);
+  float acc = 0.f;
+  if (row < rows && (int)(row % a.N) < a.n_valid) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a.o + row * D + part * 8);
+    const uint4 y = *reinterpret_cast<const uint4*>(a.dout + row * D + part * 8);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += bf16_lo(xs[i]) * bf16_lo(ys[i]) + bf16_hi(xs[i]) * bf16_hi(ys[i]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) a.dr[row] = acc;
+}
+
+// Transposed lists, step 1: clear the bit matrix.
+__global__ __launch_bounds__(256) void csc_clear_kernel(uint32_t* bits, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) bits[i] = 0u;
+}
+// Step 2: bit I of row (bh, J) for every kept pair (I, J); one wave per query
+// block row. Invalid key ids are skipped.
+__global__ __launch_bounds__(256) void csc_set_kernel(BwdArgs a, size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const size_t bh = row / a.nqb;
+  const int I = (int)(row % a.nqb);
+  const int c = min(max(a.kv_count[row], 0), a.kv_stride);
+  for (int e = lane; e < c; e += 64) {
+    const int J = a.kv_index[row * a.kv_stride + e];
+    if ((unsigned)J < (unsigned)a.nkb) atomicOr(&a.bits[(bh * a.nkb + J) * a.W + (I >> 5)], 1u << (I & 31));
+  }
+}
+// Step 3: one wave per key-block row turns its bits into an ascending list.
+__global__ __launch_bounds__(256) void csc_list_kernel(BwdArgs a, size_t cols) {
+  const size_t col = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (col >= cols) return;
+  const uint32_t* b = a.bits + col * a.W;
+  int32_t* out = a.q_index + col * a.nqb;
+  int base = 0;
+  for (int w0 = 0; w0 < a.W; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t word = w < a.W ? b[w] : 0u;
+    const int n = __popc(word);
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int pos = base + incl - n;
+    while (word) {
+      out[pos++] = 32 * w + (__ffs(word) - 1);
+      word &= word - 1u;
+    }
+    base += __shfl(incl, 63);
+  }
+  if (lane == 0) a.q_count[col] = base;
+}
+
+// dQ of one 64-row query tile (wave w owns query rows 32w .. 32w+31).
+// Per kept key block, on double-buffered K / V tiles:
+//   S^T = K Q^T, dP^T = V dO^T      (Q^T, dO^T stay in registers)
+//   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)   (lane-local)
+//   dQ^T += K^T dS^T                (K^T through the transpose read)
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
+  using T = Tile<D>;
+  constexpr int NS = D / 8;                        // MFMA steps per product
+  __shared__ __align__(16) unsigned char K0[T::BYTES];
+  __shared__ __align__(16) unsigned char V0[T::BYTES];
+  __shared__ __align__(16) unsigned char K1[T::BYTES];
+  __shared__ __align__(16) unsigned char V1[T::BYTES];
+
+  const int bh = blockIdx.x / a.nqb, I = blockIdx.x % a.nqb;
+  const int qs = 64 * I, ql = min(64, a.n_valid - qs);
+  if (ql <= 0) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * a.N;
+  const uint16_t* kh = a.k + head * D;
+  const uint16_t* vh = a.v + head * D;
+  const float sl2 = a.scale * kLog2e;
+
+  // Q^T and dO^T as MFMA B operands: lane supplies row 32w + l32,
+  // channels 16 c + 8 half .. +7
+  const int qr = 32 * wave + l32;
+  const bool qok = qr < ql;
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const size_t off = (head + qs + (qok ? qr : 0)) * D + 16 * c + 8 * half;
+    qf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.q + off) : bf16x8{};
+    gf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.dout + off) : bf16x8{};
+  }
+  const float lse2 = qok ? a.lse[head + qs + qr] * kLog2e : INFINITY;   // pad rows: P = 0
+  const float drow = qok ? a.dr[head + qs + qr] : 0.f;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dg][r] = 0.f;
+
+  const size_t lrow = (size_t)bh * a.nqb + I;
+  const int cnt = min(max(((const cint*)a.kv_count)[lrow], 0), a.kv_stride);
+  const cint* list = (const cint*)(a.kv_index + lrow * a.kv_stride);
+  uint32_t off[T::NI];
+  tile_offsets<D>(wave, lane, off);
+  const TrOffsets<D> tro(lane);
+  auto block_of = [&](int c, int& ks, int& kl) {   // chunk c of the list (clamped into range)
+    int J = list[c < cnt ? c : cnt - 1];
+    J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;
+    ks = 64 * J;
+    kl = min(64, a.n_valid - ks);
+  };
+
+  // one chunk: loads of chunk c+1 (or a reload of c) into (Kn, Vn) go out
+  // first; chunk c must have landed in (Kc, Vc)
+  auto step = [&](int c, const lds_u8* Kc, const lds_u8* Vc, lds_u8* Kn, lds_u8* Vn) {
+    int ks, kl, ks1, kl1;
+    block_of(c, ks, kl);
+    block_of(c + 1, ks1, kl1);
+    tile_load<D>(kh, ks1, kl1, Kn, wave, off);
+    tile_load<D>(vh, ks1, kl1, Vn, wave, off);
+    wait_vm<2 * T::NI>();                          // this wave's share of chunk c landed
+    wg_barrier();                                  // and the other wave's
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int kb = j & 1, cc = j >> 1;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Kc, kb, cc, l32, half), qf[cc], s[kb], 0, 0, 0);
+      dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Vc, kb, cc, l32, half), gf[cc], dp[kb], 0, 0, 0);
+    }
+    uint32_t pw[2][2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float d2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int key = 32 * kb + acc_row(r + u, half);
+          const float p = key < kl ? __builtin_amdgcn_exp2f(fmaf(s[kb][r + u], sl2, -lse2)) : 0.f;
+          d2[u] = p * (dp[kb][r + u] - drow);
+        }
+        pw[kb][r >> 3][(r & 7) >> 1] = pack2(d2[0], d2[1]);
+      }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
+      const bf16x8 ds = __builtin_bit_cast(bf16x8, (u32x4){pw[kb][hh][0], pw[kb][hh][1], pw[kb][hh][2], pw[kb][hh][3]});
+      dq[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Kc, tro, kb, hh, dg), ds, dq[dg], 0, 0, 0);
+    }
+    wg_barrier();                                  // (Kc, Vc) free for chunk c+2
+  };
+
+  if (cnt > 0) {
+    int ks0, kl0;
+    block_of(0, ks0, kl0);
+    tile_load<D>(kh, ks0, kl0, (lds_u8*)K0, wave, off);
+    tile_load<D>(vh, ks0, kl0, (lds_u8*)V0, wave, off);
+    for (int c = 0;;) {
+      step(c, (const lds_u8*)K0, (const lds_u8*)V0, (lds_u8*)K1, (lds_u8*)V1);
+      if (++c >= cnt) break;
+      step(c, (const lds_u8*)K1, (const lds_u8*)V1, (lds_u8*)K0, (lds_u8*)V0);
+      if (++c >= cnt) break;
+    }
+  }
+  wait_vm<0>();                                    // no load of this wave targets LDS
+  wg_barrier();                                    // nor one of the other wave
+  store_rows<D>(dq, a.scale, (lds_u8*)K0, a.dq + head * D, qs, ql, wave, lane);
+}
+
+// dK, dV of one 64-key tile (wave w owns keys 32w .. 32w+31). Per query block
+// that kept it, on double-buffered Q / dO tiles, for each 32-row query half g:
+//   S = Q K^T, dP = dO V^T          (K^T, V^T stay in registers)
+//   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)
+//   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through the transpose read)
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = Tile<D>;
+  __shared__ __align__(16) unsigned char Q0[T::BYTES];
+  __shared__ __align__(16) unsigned char G0[T::BYTES];
+  __shared__ __align__(16) unsigned char Q1[T::BYTES];
+  __shared__ __align__(16) unsigned char G1[T::BYTES];
+  __shared__ __align__(16) float L0[64];           // lse * log2e of the chunk's rows (+inf on pads)
+  __shared__ __align__(16) float R0[64];           // Dr of the chunk's rows (0 on pads)
+  __shared__ __align__(16) float L1[64];
+  __shared__ __align__(16) float R1[64];
+
+  const int bh = blockIdx.x / a.nkb, J = blockIdx.x % a.nkb;
+  const int ks = 64 * J, kl = min(64, a.n_valid - ks);
+  if (kl <= 0) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * a.N;
+  const uint16_t* qh = a.q + head * D;
+  const uint16_t* gh = a.dout + head * D;
+  const float sl2 = a.scale * kLog2e;
+
+  // K^T and V^T as MFMA B operands: lane supplies key 32w + l32, channels
+  // 16 c + 8 half .. +7
+  const int kr = 32 * wave + l32;
+  const bool kok = kr < kl;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const size_t o = (head + ks + (kok ? kr : 0)) * D + 16 * c + 8 * half;
+    kf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.k + o) : bf16x8{};
+    vf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.v + o) : bf16x8{};
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dg][r] = dv[dg][r] = 0.f;
+
+  const size_t lcol = (size_t)bh * a.nkb + J;
+  const int cnt = ((const cint*)a.q_count)[lcol];
+  const cint* list = (const cint*)(a.q_index + lcol * a.nqb);
+  uint32_t off[T::NI];
+  tile_offsets<D>(wave, lane, off);
+  const TrOffsets<D> tro(lane);
+
+  // rows, lse and Dr of chunk c (clamped into range); lane l of each wave
+  // fetches row l's lse and Dr into registers (wave 0 stores them to LDS)
+  auto issue = [&](int c, lds_u8* Qn, lds_u8* Gn, float& lv, float& rv) {
+    const int I = list[c < cnt ? c : cnt - 1];
+    const int qs = 64 * I, ql = min(64, a.n_valid - qs);
+    const bool ok = lane < ql;
+    lv = INFINITY;
+    rv = 0.f;
+    if (ok) {                                      // both waves: equal load counts
+      lv = a.lse[head + qs + lane];
+      rv = a.dr[head + qs + lane];
+    }
+    tile_load<D>(qh, qs, ql, Qn, wave, off);
+    tile_load<D>(gh, qs, ql, Gn, wave, off);
+  };
+  // one chunk: chunk c+1 (or a reload of c) goes out first; chunk c's tiles
+  // must have landed and its lse / Dr are in registers lv, rv (wave 0)
+  auto step = [&](int c, const lds_u8* Qc, const lds_u8* Gc, lds_f32* Lc, lds_f32* Rc, lds_u8* Qn, lds_u8* Gn,
+                  float& lv, float& rv, float& lv_n, float& rv_n) {
+    if (wave == 0) {
+      Lc[lane] = lv == INFINITY ? INFINITY : lv * kLog2e;
+      Rc[lane] = rv;
+    }
+    issue(c + 1, Qn, Gn, lv_n, rv_n);
+    wait_vm<2 * T::NI + 2>();                      // chunk c landed (and its lse / Dr before it)
+    wg_barrier();
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {                  // 32-row query half
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Qc, g, cc, l32, half), kf[cc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Gc, g, cc, l32, half), vf[cc], dp, 0, 0, 0);
+      }
+      uint32_t pp[2][4], pd[2][4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        // rows 32g + 8 r4 + 4 half + 0..3 of the chunk
+        const int row0 = 32 * g + 8 * r4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Lc + row0);
+        const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Rc + row0);
+        float p[4], d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * r4 + u;
+          p[u] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[u]));
+          d[u] = p[u] * (dp[r] - d4[u]);
+        }
+        pp[r4 >> 1][2 * (r4 & 1) + 0] = pack2(p[0], p[1]);
+        pp[r4 >> 1][2 * (r4 & 1) + 1] = pack2(p[2], p[3]);
+        pd[r4 >> 1][2 * (r4 & 1) + 0] = pack2(d[0], d[1]);
+        pd[r4 >> 1][2 * (r4 & 1) + 1] = pack2(d[2], d[3]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
+        const bf16x8 db = __builtin_bit_cast(bf16x8, (u32x4){pd[hh][0], pd[hh][1], pd[hh][2], pd[hh][3]});
+#pragma unroll
+        for (int dg = 0; dg < D / 32; ++dg) {
+          dv[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Gc, tro, g, hh, dg), pb, dv[dg], 0, 0, 0);
+          dk[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Qc, tro, g, hh, dg), db, dk[dg], 0, 0, 0);
+        }
+      }
+    }
+    wg_barrier();                                  // chunk c's buffers free for chunk c+2
+  };
+
+  if (cnt > 0) {
+    float lA = INFINITY, rA = 0.f, lB = INFINITY, rB = 0.f;
+    issue(0, (lds_u8*)Q0, (lds_u8*)G0, lA, rA);
+    for (int c = 0;;) {
+      step(c, (const lds_u8*)Q0, (const lds_u8*)G0, (lds_f32*)L0, (lds_f32*)R0, (lds_u8*)Q1, (lds_u8*)G1, lA, rA,
+           lB, rB);
+      if (++c >= cnt) break;
+      step(c, (const lds_u8*)Q1, (const lds_u8*)G1, (lds_f32*)L1, (lds_f32*)R1, (lds_u8*)Q0, (lds_u8*)G0, lB, rB,
+           lA, rA);
+      if (++c >= cnt) break;
+    }
+  }
+  wait_vm<0>();
+  wg_barrier();
+  store_rows<D>(dk, a.scale, (lds_u8*)Q0, a.dk + head * D, ks, kl, wave, lane);
+  wg_barrier();
+  store_rows<D>(dv, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, wave, lane);
+}
+
+// Pad rows n_valid .. N-1 of dq, dk, dv are zero.
+__global__ __launch_bounds__(256) void bwd_zero_pad_kernel(uint4* dq, uint4* dk, uint4* dv, int N, int n_valid,
+                                                           int cpr, size_t total) {
+  const size_t per_head = (size_t)(N - n_valid) * cpr;
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (size_t)gridDim.x * 256) {
+    const size_t bh = u / per_head, rem = u % per_head;
+    const size_t i = (bh * N + n_valid) * cpr + rem;
+    dq[i] = dk[i] = dv[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const uint16_t* dout, const float* lse, int BH, int N, int d, int n_valid,
+                           const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  const int nb = (n_valid + 63) / 64;
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.N = N; a.n_valid = n_valid; a.nqb = nb; a.nkb = nb;
+  a.kv_count = kv_count; a.kv_index = kv_index; a.kv_stride = kv_stride;
+  a.W = (nb + 31) / 32;
+  a.scale = scale;
+  // workspace: Dr [BH][N] fp32 | q_count [BH][nkb] | q_index [BH][nkb][nqb] | bits [BH][nkb][W]
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return r;
+  };
+  a.dr = reinterpret_cast<float*>(take(sizeof(float) * (size_t)BH * N));
+  a.q_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
+  a.q_index = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb * nb));
+  a.bits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)BH * nb * a.W));
+
+  if (n_valid < N) {
+    const int cpr = d / 8;
+    const size_t total = (size_t)BH * (N - n_valid) * cpr;
+    const size_t want = (total + 255) / 256;
+    bwd_zero_pad_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, s>>>(
+        reinterpret_cast<uint4*>(dq), reinterpret_cast<uint4*>(dk), reinterpret_cast<uint4*>(dv), N, n_valid, cpr,
+        total);
+  }
+  if (nb == 0) return hipGetLastError();
+  const size_t rows = (size_t)BH * N;
+  const size_t lanes = rows * (d / 8);
+  if (d == 128)
+    bwd_dot_kernel<128><<<(int)((lanes + 255) / 256), 256, 0, s>>>(a, rows);
+  else
+    bwd_dot_kernel<64><<<(int)((lanes + 255) / 256), 256, 0, s>>>(a, rows);
+  const size_t nbits = (size_t)BH * nb * a.W;
+  csc_clear_kernel<<<(int)((nbits + 255) / 256 < 4096 ? (nbits + 255) / 256 : 4096), 256, 0, s>>>(a.bits, nbits);
+  const size_t lrows = (size_t)BH * nb;
+  csc_set_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
+  csc_list_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
+  const int tiles = (int)lrows;
+  if (d == 128) {
+    bwd_dq_kernel<128><<<tiles, 128, 0, s>>>(a);
+    bwd_dkdv_kernel<128><<<tiles, 128, 0, s>>>(a);
+  } else {
+    bwd_dq_kernel<64><<<tiles, 128, 0, s>>>(a);
+    bwd_dkdv_kernel<64><<<tiles, 128, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+size_t attn_bwd_workspace(int BH, int N, int nb) {
+  auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t W = ((size_t)nb + 31) / 32;
+  return r(sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nb) +
+         r(sizeof(int32_t) * (size_t)BH * nb * nb) + r(sizeof(uint32_t) * (size_t)BH * nb * W);
+}
+
+}  // namespace bsa

@@ -523,6 +523,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int orow = 32 * wave + l32;
   const int fo = swz<D>(orow & 15);
+  // log sum_j exp(scale s_ij) = ln 2 * (m + log2 l), m the reference max in
+  // log2 units; rows with no kept key get -inf
+  if (a.lse && half == 0 && orow < ql)
+    a.lse[(size_t)bh * a.N + qs + orow] = lt > 0.f ? (m_run + log2f(lt)) * 0.69314718055994531f : -INFINITY;
 #pragma unroll
   for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
@@ -676,12 +680,13 @@ __global__ __launch_bounds__(256) void tile_base_kernel(Blocks qb, int32_t* __re
   if (threadIdx.x == 255) out[n] = run;
 }
 
-__global__ __launch_bounds__(256) void zero_rows_kernel(uint4* __restrict__ o, int N, int n_valid,
-                                                        int cpr, size_t total) {
+__global__ __launch_bounds__(256) void zero_rows_kernel(uint4* __restrict__ o, float* __restrict__ lse, int N,
+                                                        int n_valid, int cpr, size_t total) {
   const size_t per_head = (size_t)(N - n_valid) * cpr;
   for (size_t u = blockIdx.x * (size_t)256 + threadIdx.x; u < total; u += (size_t)gridDim.x * 256) {
     const size_t bh = u / per_head, rem = u % per_head;
     o[(bh * N + n_valid) * cpr + rem] = make_uint4(0, 0, 0, 0);
+    if (lse && rem % cpr == 0) lse[bh * N + n_valid + rem / cpr] = -INFINITY;
   }
 }
 
@@ -691,14 +696,14 @@ constexpr int kOneWaveKeyBlocks = 1024;
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int BH, int N, int d, int n_valid, const Blocks& qb, const Blocks& kb,
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
-                           float scale, int32_t* tile_ws, hipStream_t s) {
+                           float scale, int32_t* tile_ws, float* lse, hipStream_t s) {
   if (BH == 0) return hipSuccess;
   if (n_valid < N) {
     const int cpr = d / 8;
     const size_t total = (size_t)BH * (N - n_valid) * cpr;
     const size_t want = (total + 255) / 256;
     const int grid = (int)(want < 4096 ? want : 4096);
-    zero_rows_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<uint4*>(o), N, n_valid, cpr, total);
+    zero_rows_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<uint4*>(o), lse, N, n_valid, cpr, total);
   }
   if (qb.nblocks == 0) return hipGetLastError();
   AttnArgs a;
@@ -707,6 +712,7 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.qb = qb; a.kb = kb;
   a.kv_count = kv_count; a.kv_index = kv_index; a.kv_stride = kv_stride;
   a.sl2 = scale * 1.4426950408889634f;
+  a.lse = lse;
   // Uniform 64-token query blocks need no tiling table; key blocks that are not
   // uniform 64-token blocks are gathered row by row.
   const bool qvar = qb.start != nullptr;

@@ -464,6 +464,9 @@ __device__ __forceinline__ void attn_tile_1w(const AttnArgs& a, int bh, int I, i
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int orow = 32 * q2 + l32;
     const int fo = swz<D>(orow & 15);
+    if (a.lse && half == 0 && orow < ql)
+      a.lse[(size_t)bh * a.N + qs + orow] =
+          lt > 0.f ? (m_run[q2] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
 #pragma unroll
     for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll

@@ -107,7 +107,12 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int BH, int N, int d, int n_valid, const Blocks& qb, const Blocks& kb,
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
-                           float scale, int32_t* tile_ws, hipStream_t s);
+                           float scale, int32_t* tile_ws, float* lse, hipStream_t s);
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const uint16_t* dout, const float* lse, int BH, int N, int d, int n_valid,
+                           const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
+size_t attn_bwd_workspace(int BH, int N, int nb);
 hipError_t launch_permute(const uint16_t* x, uint16_t* y, const int32_t* perm, int BH, int N,
                           int d, int per_head, bool inverse, hipStream_t s);
 hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,

@@ -218,6 +218,65 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                               float scale, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/*
+ * The forward above, also writing each row's softmax log-normaliser, which
+ * the backward needs (NABLA summary, Contributi Chiave, "Accelerazione a Due
+ * Fasi": the sparse attention runs in training as well):
+ *   lse[b,h,i] = log sum_j exp(scale * q_i . k_j)   over the same kept keys
+ *   lse       fp32 [B,H,N] (device, 16-byte aligned); -inf for rows of a
+ *             query block with no kept key block and for rows n_valid..N-1
+ * Every other argument, limit and error is that of bsa_block_sparse_attn_fwd.
+ */
+int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int B, int H, int N,
+                                  int d, int n_valid, int block,
+                                  const bsa_blocks* qb, const bsa_blocks* kb,
+                                  const int32_t* kv_count,
+                                  const int32_t* kv_index, int kv_stride,
+                                  float scale, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* Workspace bytes needed by bsa_block_sparse_attn_bwd: fp32 row terms
+ * [B,H,N] plus the transposed block lists (int32 [B,H,nb] counts,
+ * [B,H,nb,nb] ids, and a [B,H,nb,ceil(nb/32)] bit matrix; nb = ceil(N/64)). */
+size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N);
+
+/*
+ * Block-sparse attention backward (NABLA summary, Contributi Chiave,
+ * "Accelerazione a Due Fasi"; Risultati Sperimentali 2, pre-training): the
+ * gradients of bsa_block_sparse_attn_fwd with respect to q, k and v for an
+ * upstream gradient dout, over the same kept tiles. Per query block I and
+ * kept key block J:
+ *   P = exp(scale Q_I K_J^T - lse_I),  dP = dO_I V_J^T,  Dr_i = dO_i . O_i
+ *   dS = P (dP - Dr),  dQ_I += scale dS K_J,  dK_J += scale dS^T Q_I,
+ *   dV_J += P^T dO_I
+ * MFMA bf16 products with fp32 accumulation; deterministic (no atomics on
+ * the gradients). Uniform `block`-token blocks only (block = 64).
+ *
+ *   q, k, v, o, dout  bf16 [B,H,N,d] (device), d in {64, 128}; o is the
+ *             forward's output
+ *   lse       fp32 [B,H,N] from bsa_block_sparse_attn_fwd_lse with the same
+ *             lists
+ *   kv_count, kv_index, kv_stride   the mask lists of the forward; ids must
+ *             be valid key blocks
+ *   scale     > 0, or <= 0 for 1/sqrt(d) (the forward's)
+ *   dq, dk, dv  bf16 [B,H,N,d] (device), fully written: rows n_valid..N-1,
+ *             query rows with no kept key block and key rows no query block
+ *             kept are zero
+ *   ws        workspace of bsa_block_sparse_attn_bwd_workspace(B, H, N)
+ *             bytes (device, 16-byte aligned; contents are overwritten)
+ * All pointers 16-byte aligned. Errors: BSA_EINVAL (null or misaligned
+ * pointers, bad kv_stride), BSA_EUNSUPPORTED (d, block, 4 GiB head limit),
+ * BSA_ENOSPC (workspace).
+ */
+int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v,
+                              const void* o, const void* dout,
+                              const float* lse, int B, int H, int N, int d,
+                              int n_valid, int block, const int32_t* kv_count,
+                              const int32_t* kv_index, int kv_stride,
+                              float scale, void* dq, void* dk, void* dv,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Token reorder helpers
  * ------------------------------------------------------------------------ */

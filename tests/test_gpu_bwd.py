@@ -1,0 +1,127 @@
+"""GPU parity of the block-sparse attention backward (and the forward's row
+log-normaliser) against the float64 CPU reference in oracle/attention.py.
+
+Tolerance: the kernels round P and dS to bf16 before the second product of
+each pair (relative 2^-9 per factor) and store bf16 gradients (another
+2^-9), with fp32 accumulation; errors are measured relative to the size of
+each gradient: max |g - ref| <= 2e-2 * max(1, max |ref|) and mean
+|g - ref| <= 2e-3 * max(1, max |ref|). The row normaliser is fp32 throughout
+(one log2 per row): |lse - ref| <= 1e-3 absolute.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gen import WORKLOADS, generate
+from oracle import attention as oa
+from oracle import layout as ol
+from tests.band import keep_from_lists
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX = 2e-2
+REL_MEAN = 2e-3
+LSE_ABS = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_grad(g, ref, rows, what):
+    g, ref = g[rows], ref[rows]
+    scale = max(1.0, float(np.abs(ref).max()))
+    d = np.abs(g - ref)
+    say(f"  {what}: max-abs {d.max():.3e} mean-abs {d.mean():.3e} (scale {scale:.3g})")
+    assert np.isfinite(g).all(), what
+    assert d.max() <= REL_MAX * scale and d.mean() <= REL_MEAN * scale, what
+
+
+def _lists(keep):
+    H, nq, nk = keep.shape
+    cnt = keep.sum(2).astype(np.int32)
+    idx = np.full((H, nq, nk), -1, np.int32)
+    for h in range(H):
+        for i in range(nq):
+            ids = np.nonzero(keep[h, i])[0]
+            idx[h, i, :len(ids)] = ids
+    return cnt, idx
+
+
+def _run_case(bsa, q, k, v, do, cnt, idx, nv, heads=None):
+    """GPU forward (with lse) + backward, compared to the oracle per head."""
+    H, N = q.shape[1], q.shape[2]
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    cd, id_ = torch.from_numpy(cnt[None]).cuda(), torch.from_numpy(idx[None]).cuda()
+    o, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cd, id_, n_valid=nv)
+    o_plain = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    assert torch.equal(o, o_plain)                 # the lse output changes no bit of O
+    dq, dk, dv = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv)
+    torch.cuda.synchronize()
+    dq2, dk2, dv2 = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)   # deterministic
+    st, ln = ol.raster_blocks(nv)
+    nb = len(st)
+    lse_g, dq, dk, dv = (_np(t)[0] for t in (lse, dq, dk, dv))
+    rows = np.arange(nv)
+    for h in (range(H) if heads is None else heads):
+        keep = keep_from_lists(cnt[h], idx[h], nb)
+        args = [_np(t[0, h]) for t in (q, k, v)]
+        ref_l = oa.masked_attention_lse(args[0], args[1], st, ln, st, ln, keep)
+        fin = np.isfinite(ref_l[rows])
+        assert np.array_equal(np.isfinite(lse_g[h][rows]), fin), f"head {h}: -inf rows differ"
+        dl = np.abs(lse_g[h][rows][fin] - ref_l[rows][fin])
+        say(f"  head {h} lse: max-abs {dl.max() if dl.size else 0:.3e}")
+        assert dl.size == 0 or dl.max() <= LSE_ABS
+        rq, rk, rv = oa.masked_attention_bwd(*args, _np(do[0, h]), st, ln, st, ln, keep)
+        _check_grad(dq[h], rq, rows, f"head {h} dq")
+        _check_grad(dk[h], rk, rows, f"head {h} dk")
+        _check_grad(dv[h], rv, rows, f"head {h} dv")
+    for t in (dq, dk, dv):
+        assert (t[:, nv:] == 0).all()
+    assert np.isneginf(lse_g[:, nv:]).all()
+
+
+@pytest.mark.parametrize("H,N,nv,d", [(2, 256, 256, 64), (2, 704, 650, 128), (1, 1088, 1030, 64)])
+def test_bwd_random_masks(gpu_lib, H, N, nv, d):
+    say(f"backward random masks H={H} N={N} n_valid={nv} d={d}")
+    rng = np.random.default_rng(N + d)
+    x = rng.normal(size=(4, 1, H, N, d)).astype(np.float32)
+    x[:, :, :, nv:] = 0
+    q, k, v, do = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(4))
+    nb = -(-nv // 64)
+    keep = rng.random((H, nb, nb)) < 0.35
+    keep[:, :, 0] |= ~keep.any(2)
+    keep[:, 0, :] = True                            # a dense row
+    if nb > 3:
+        keep[:, 2, :] = False                       # a row that keeps nothing
+        keep[:, :, nb - 2] = False                  # a key block nobody keeps
+    cnt, idx = _lists(keep)
+    _run_case(gpu_lib, q, k, v, do, cnt, idx, nv)
+
+
+def test_bwd_mask_stage_lists(gpu_lib):
+    # the lists the mask stage builds on the Fourier-feature inputs (the
+    # tiny workload and the first 4096 tokens of the 480p layer, two heads)
+    bsa = gpu_lib
+    for key, N in (("tiny", None), ("wan480", 4096)):
+        w = WORKLOADS[key]
+        q, k, v = generate(w, heads=[0, 1])
+        if N is not None:
+            q, k, v = (t[:, :, :N].contiguous() for t in (q, k, v))
+        N = q.shape[2]
+        nv = min(w.n_valid, N)
+        say(f"backward on mask-stage lists: {key} N={N}")
+        do = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+        cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), w.thr, n_valid=nv)
+        _run_case(bsa, q, k, v, do, cnt.cpu().numpy()[0], idx.cpu().numpy()[0], nv)
