@@ -127,6 +127,42 @@ class Runner:
         t_attn = sum(self.attn_each) / steps
         return wall / steps * 1e3, t_mask, t_attn
 
+    def backward(self, steps: int, warmup: int = 3):
+        """Mean times of the forward-with-lse and the backward on this step's
+        lists (upstream gradient: seeded Gaussian)."""
+        g = torch.randn(self.q.shape, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16)
+        g = g.to(self.q.device)
+        self.mask()
+        o, lse = bsa.block_sparse_attn_fwd_lse(self.q, self.k, self.v, self.cnt, self.idx, n_valid=self.w.n_valid)
+        grads = tuple(torch.empty_like(self.q) for _ in range(3))
+        lib = bsa.load()
+        ws = torch.empty(lib.bsa_block_sparse_attn_bwd_workspace(self.w.B, self.w.H, self.w.N),
+                         dtype=torch.uint8, device=self.q.device)
+
+        def fwd():
+            bsa.block_sparse_attn_fwd_lse(self.q, self.k, self.v, self.cnt, self.idx, n_valid=self.w.n_valid,
+                                          out=o, lse=lse, workspace=self.ws_attn)
+
+        def bwd():
+            bsa.block_sparse_attn_bwd(self.q, self.k, self.v, o, g, lse, self.cnt, self.idx,
+                                      n_valid=self.w.n_valid, out=grads, workspace=ws)
+
+        for _ in range(warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            e[0].record()
+            fwd()
+            e[1].record()
+            bwd()
+            e[2].record()
+        torch.cuda.synchronize()
+        t_f = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        t_b = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        return t_f, t_b
+
     def cold(self, reps: int, scratch_mib: int = 512):
         """Median mask / attention times with the caches flushed before each step.
 
@@ -385,6 +421,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="extra steps timed with flushed caches (reported under cold_cache; 0 = skip)")
+    ap.add_argument("--bwd-steps", type=int, default=20,
+                    help="steps timing the backward on the same lists (reported under backward; 0 = skip)")
     ap.add_argument("--no-gemm-ref", action="store_true",
                     help="skip the MFMA-rate probe and the dense bf16 GEMM reference")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -459,6 +497,14 @@ def main():
                       "mask_gbs": round(s["mask_gbs"], 1)},
         "flops_eff_per_step": s["flops_eff"],
     }
+    if a.bwd_steps > 0:
+        tf, tb = r.backward(a.bwd_steps)
+        fb = 2.5 * s["flops_eff"]                  # five products per kept tile
+        line["backward"] = {"ms": round(tb, 4), "tflops_eff": round(fb / (tb * 1e-3) / 1e12, 3),
+                            "frac_of_peak": round(fb / (tb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "fwd_with_lse_ms": round(tf, 4), "steps": a.bwd_steps,
+                            "flops": "2.5 x the forward's effective FLOP (S, dP, dV, dK, dQ products of "
+                                     "kept tiles; the dQ pass also recomputes S and dP, not counted)"}
     if a.cold_reps > 0:
         cm, ca = r.cold(a.cold_reps)
         line["cold_cache"] = {"mask_ms": round(cm, 4), "attention_ms": round(ca, 4),

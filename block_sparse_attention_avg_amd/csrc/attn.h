@@ -27,4 +27,9 @@ struct AttnArgs {
 // a.order set; `grid` workgroups of one wave.
 hipError_t launch_attn_fwd_1w(const AttnArgs& a, int grid, hipStream_t s);
 
+// Longest-first processing order of n rows per head (attn_fwd.hip): order[bh][i]
+// lists the rows by descending count (clamped to [0, cap]). Returns false when
+// the counting sort does not fit in LDS (then nothing is launched).
+bool launch_qorder(const int32_t* counts, int BH, int n, int cap, int32_t* order, hipStream_t s);
+
 }  // namespace bsa

@@ -19,7 +19,7 @@
 // lane holds one column (query, resp. key) and 16 rows; the second product of
 // each pair takes its bf16 B operand straight from that accumulator, and the
 // A operand through the LDS transpose read whose row order matches it.
-#include "common.h"
+#include "attn.h"
 
 #include <math.h>
 
@@ -186,8 +186,22 @@ struct BwdArgs {
   int32_t* q_index;           // [BH][nkb][nqb], ascending
   uint32_t* bits;             // [BH][nkb][W] bit matrix key block x query block
   int W;                      // 32-bit words per bit-matrix row
+  const int32_t* order_q;     // null, or [BH][nqb] longest-first order of the query tiles
+  const int32_t* order_k;     // null, or [BH][nkb] longest-first order of the key tiles
   float scale;
 };
+
+// Workgroup -> (head, tile): workgroups are dealt round-robin to the 8 XCDs,
+// and XCD x takes a contiguous range of the flattened (head, position) order,
+// so a head's operands stay in one XCD's L2; within a head, longest first.
+__device__ __forceinline__ void tile_of(int L, int n, int BH, const int32_t* order, int& bh, int& t) {
+  const int total = BH * n, per = total >> 3, rem = total & 7;
+  const int x = L & 7, i = L >> 3;
+  const int p = x * per + min(x, rem) + i;
+  bh = p / n;
+  const int pos = p - bh * n;
+  t = order ? ((const __attribute__((address_space(4))) int32_t*)order)[(size_t)bh * n + pos] : pos;
+}
 
 // Dr[row] = sum_c dO[row, c] O[row, c] (fp32), 0 on pad rows.
 template <int D>
@@ -269,7 +283,8 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char K1[T::BYTES];
   __shared__ __align__(16) unsigned char V1[T::BYTES];
 
-  const int bh = blockIdx.x / a.nqb, I = blockIdx.x % a.nqb;
+  int bh, I;
+  tile_of(blockIdx.x, a.nqb, (int)(gridDim.x / a.nqb), a.order_q, bh, I);
   const int qs = 64 * I, ql = min(64, a.n_valid - qs);
   if (ql <= 0) return;
   const int tid = threadIdx.x;
@@ -391,7 +406,8 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __align__(16) float L1[64];
   __shared__ __align__(16) float R1[64];
 
-  const int bh = blockIdx.x / a.nkb, J = blockIdx.x % a.nkb;
+  int bh, J;
+  tile_of(blockIdx.x, a.nkb, (int)(gridDim.x / a.nkb), a.order_k, bh, J);
   const int ks = 64 * J, kl = min(64, a.n_valid - ks);
   if (kl <= 0) return;
   const int tid = threadIdx.x;
@@ -547,6 +563,8 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.q_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
   a.q_index = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb * nb));
   a.bits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)BH * nb * a.W));
+  int32_t* oq = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
+  int32_t* ok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
 
   if (n_valid < N) {
     const int cpr = d / 8;
@@ -568,6 +586,8 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const size_t lrows = (size_t)BH * nb;
   csc_set_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
   csc_list_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
+  a.order_q = launch_qorder(kv_count, BH, nb, nb, oq, s) ? oq : nullptr;
+  a.order_k = launch_qorder(a.q_count, BH, nb, nb, ok, s) ? ok : nullptr;
   const int tiles = (int)lrows;
   if (d == 128) {
     bwd_dq_kernel<128><<<tiles, 128, 0, s>>>(a);
@@ -583,7 +603,8 @@ size_t attn_bwd_workspace(int BH, int N, int nb) {
   auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t W = ((size_t)nb + 31) / 32;
   return r(sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nb) +
-         r(sizeof(int32_t) * (size_t)BH * nb * nb) + r(sizeof(uint32_t) * (size_t)BH * nb * W);
+         r(sizeof(int32_t) * (size_t)BH * nb * nb) + r(sizeof(uint32_t) * (size_t)BH * nb * W) +
+         2 * r(sizeof(int32_t) * (size_t)BH * nb);
 }
 
 }  // namespace bsa

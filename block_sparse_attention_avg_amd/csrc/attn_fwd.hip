@@ -690,6 +690,15 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(uint4* __restrict__ o, f
   }
 }
 
+// Longest-first order of n rows per head by count (counts clamped to [0, cap]);
+// false when the counting sort does not fit in LDS.
+bool launch_qorder(const int32_t* counts, int BH, int n, int cap, int32_t* order, hipStream_t s) {
+  const size_t lds = sizeof(int) * ((size_t)cap + 1 + n);
+  if (lds > 64 * 1024) return false;
+  qorder_kernel<<<BH, 256, lds, s>>>(counts, n, cap, order);
+  return true;
+}
+
 // Key-block count from which uniform d = 128 attention runs one wave per tile.
 constexpr int kOneWaveKeyBlocks = 1024;
 
