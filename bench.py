@@ -358,6 +358,13 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
                 if att:
                     lines.append(f"rocprof {att[0][0]} average {att[0][2]:.1f} us "
                                  f"(ratio events / kernel {b['stages_ms']['attention'] * 1e3 / att[0][2]:.3f})")
+                if "backward" in b:
+                    bw = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::bwd_") or
+                          x[0].startswith("bsa::csc_")]
+                    per_call = sum(x[2] * x[1] for x in bw) / max(1, max((x[1] for x in bw), default=1))
+                    lines.append(f"bench (same run): backward {b['backward']['ms'] * 1e3:.1f} us per call "
+                                 f"(HIP events), {b['backward']['tflops_eff']} TFLOP/s effective; rocprof "
+                                 f"backward kernels {per_call:.1f} us per call")
     elif kind == "counters":
         lines.append(f"command: {command}")
         rows = _csv_rows(os.path.join(dirs[0], "run_counter_collection.csv"))
