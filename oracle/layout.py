@@ -2,6 +2,9 @@
 
 Pins: ``fractal_order`` -- bijection, per-block coordinate consistency and the
 closed-form patch-length histogram (tests/test_oracle_layout.py);
+``tile_order`` -- equals ``fractal_order`` for (1, P, P), one box over the
+whole latent is the identity, bijection, every block is one box at its grid
+position, closed-form box lengths;
 ``window_blocks`` -- closed-form per-row counts (product of clipped ranges) and
 a brute-force token-level check; ``raster_blocks`` -- closed form.
 """
@@ -60,6 +63,41 @@ def fractal_order(T: int, Hl: int, Wl: int, P: int, N: int | None = None):
     perm.extend(range(n_valid, N))
     return (np.asarray(perm, dtype=np.int64), np.asarray(start, dtype=np.int64),
             np.asarray(length, dtype=np.int64), np.asarray(coords, dtype=np.int64))
+
+
+def tile_order(T: int, Hl: int, Wl: int, pt: int, ph: int, pw: int, N: int | None = None):
+    """Head-aware tiling layout: every pt x ph x pw box of the latent becomes
+    one contiguous block.
+
+    Veda summary, section 2.2 ("Tiling Consapevole delle Teste"): each layer and
+    head gets its own tiling configuration pi = (p_t, p_h, p_w), a
+    factorisation of the hardware tile, so the tokens of one tile are a
+    p_t x p_h x p_w box of the video instead of a fixed spatial patch.
+
+    Reading (as for the fractal order): boxes are numbered row-major over the
+    ceil(T/pt) x ceil(Hl/ph) x ceil(Wl/pw) grid, frame boxes slowest; inside a
+    box tokens keep raster order (t, y, x); edge boxes are smaller and no
+    padding tokens are inserted, so blocks have variable length. Positions
+    >= T*Hl*Wl map to themselves.
+
+    Computed as a stable sort of the raster tokens by box number. Returns
+    (perm, start, length, coords) like ``fractal_order``, with coords the box
+    grid position (bt, by, bx).
+    """
+    n_valid = T * Hl * Wl
+    N = n_valid if N is None else N
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Hl), np.arange(Wl), indexing="ij")
+    nby, nbx = -(-Hl // ph), -(-Wl // pw)
+    nbt = -(-T // pt)
+    box = ((t // pt) * nby + y // ph) * nbx + x // pw
+    box = box.reshape(-1)
+    order = np.argsort(box, kind="stable")
+    counts = np.bincount(box, minlength=nbt * nby * nbx)
+    start = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    g = np.arange(nbt * nby * nbx)
+    coords = np.stack([g // (nby * nbx), (g // nbx) % nby, g % nbx], axis=1)
+    perm = np.concatenate([order, np.arange(n_valid, N)]).astype(np.int64)
+    return perm, start.astype(np.int64), counts.astype(np.int64), coords.astype(np.int64)
 
 
 def block_coords_from_tokens(token_xyz: np.ndarray, perm: np.ndarray,

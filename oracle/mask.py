@@ -14,7 +14,11 @@ Readings where the pages are silent (each listed in the design notes):
     stays below thr * total. Equivalently the kept set is the smallest
     heaviest-first set whose mass exceeds (1 - thr) * total, so thr = 0 keeps
     every block and the heaviest block is always kept;
-  * pooling averages only the real tokens of a block.
+  * pooling averages only the real tokens of a block;
+  * a block with no tokens (length 0: padding of per-head layouts with
+    different block counts) has no average, so it takes no part in the
+    reduced attention: it is never kept by the CDF rule as a key block, and
+    as a query block it keeps nothing (the window included).
 
 Pins (tests/test_oracle_mask.py): pooling -- constant blocks, linearity, a
 hand-worked fixture; reduced map -- two-block logistic closed form, identical
@@ -38,7 +42,8 @@ def pool(x: np.ndarray, start: np.ndarray, length: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     out = np.zeros((len(start), x.shape[1]), dtype=np.float64)
     for i, (s, n) in enumerate(zip(start, length)):
-        out[i] = x[s:s + n].sum(axis=0) / n
+        if n > 0:                       # a block with no tokens stays 0 (never used)
+            out[i] = x[s:s + n].sum(axis=0) / n
     return out
 
 
@@ -107,10 +112,13 @@ def block_mask(q: np.ndarray, k: np.ndarray, qstart, qlen, kstart, klen,
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     qbar = pool(q, qstart, qlen)
     kbar = pool(k, kstart, klen)
-    p = softmax_rows(reduced_scores(qbar, kbar, scale))
+    logw = np.where(np.asarray(klen) > 0, 0.0, -np.inf)
+    p = softmax_rows(reduced_scores(qbar, kbar, scale), logw)
     keep = cdf_mask(p, thr)
+    keep[:, np.asarray(klen) == 0] = False
     if window is not None:
         keep = keep | window
+    keep[np.asarray(qlen) == 0, :] = False
     return keep, p
 
 

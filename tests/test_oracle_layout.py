@@ -83,3 +83,46 @@ def test_window_matches_token_level_brute_force():
             inside = (abs(a[0] - b[0]) <= 1 and abs(a[1] // P - b[1] // P) <= 1
                       and abs(a[2] // P - b[2] // P) <= 1)
             assert inside == w[blk[i], blk[j]]
+
+
+# ----------------------------------------------------------- head-aware tiling
+
+@pytest.mark.parametrize("T,Hl,Wl,P", [(21, 30, 52, 8), (2, 5, 7, 3), (3, 8, 8, 8)])
+def test_tile_order_with_flat_boxes_is_the_fractal_order(T, Hl, Wl, P):
+    a = ol.tile_order(T, Hl, Wl, 1, P, P, N=T * Hl * Wl + 3)
+    b = ol.fractal_order(T, Hl, Wl, P, N=T * Hl * Wl + 3)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_tile_order_one_box_is_the_identity():
+    perm, st, ln, co = ol.tile_order(3, 5, 7, 3, 5, 7)
+    assert np.array_equal(perm, np.arange(105)) and st.tolist() == [0] and ln.tolist() == [105]
+    assert co.tolist() == [[0, 0, 0]]
+
+
+def _box_len(dim, p, b):
+    return np.minimum(p, dim - b * p)
+
+
+@pytest.mark.parametrize("T,Hl,Wl,pt,ph,pw", [(21, 30, 52, 2, 4, 8), (21, 30, 52, 4, 4, 4), (5, 6, 9, 2, 4, 8),
+                                              (4, 7, 5, 3, 2, 5), (1, 3, 3, 4, 4, 4)])
+def test_tile_order_blocks_are_boxes(T, Hl, Wl, pt, ph, pw):
+    n = T * Hl * Wl
+    perm, st, ln, co = ol.tile_order(T, Hl, Wl, pt, ph, pw, N=n + 4)
+    assert sorted(perm.tolist()) == list(range(n + 4)) and (perm[n:] == np.arange(n, n + 4)).all()
+    nbt, nby, nbx = -(-T // pt), -(-Hl // ph), -(-Wl // pw)
+    assert len(st) == nbt * nby * nbx
+    assert st[0] == 0 and (st[1:] == np.cumsum(ln)[:-1]).all() and ln.sum() == n
+    # block b sits at grid position (bt, by, bx), row-major, frame boxes slowest
+    g = np.arange(len(st))
+    assert (co[:, 0] == g // (nby * nbx)).all() and (co[:, 1] == (g // nbx) % nby).all()
+    assert (co[:, 2] == g % nbx).all()
+    # closed-form box lengths (edge boxes are clipped)
+    exp = _box_len(T, pt, co[:, 0]) * _box_len(Hl, ph, co[:, 1]) * _box_len(Wl, pw, co[:, 2])
+    assert np.array_equal(ln, exp)
+    xyz = token_coords(T, Hl, Wl)
+    for b, (s, m) in enumerate(zip(st, ln)):
+        c = xyz[perm[s:s + m]]
+        assert (c // np.array([pt, ph, pw]) == co[b]).all()      # every token inside the box
+        assert (np.diff(perm[s:s + m]) > 0).all()                 # raster order inside a box

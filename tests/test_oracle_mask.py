@@ -214,3 +214,30 @@ def test_centroid_mask_special_cases():
     sel = nk > 0
     p = om.softmax_rows(om.reduced_scores(cq, ck[sel], 0.25))
     np.testing.assert_allclose(w[:, sel], p, rtol=1e-13)
+
+
+def test_block_mask_empty_blocks_take_no_part():
+    # inserting blocks with no tokens changes nothing else: they are never kept
+    # as key blocks and keep nothing as query blocks (window included)
+    rng = np.random.default_rng(17)
+    q = 3 * rng.normal(size=(200, 16))
+    k = 3 * rng.normal(size=(200, 16))
+    st = np.array([0, 64, 128, 192])
+    ln = np.array([64, 64, 64, 8])
+    pos = [1, 3, 6]                                   # where the empty blocks go
+    st2, ln2 = list(st), list(ln)
+    for i in pos:
+        st2.insert(i, 200)
+        ln2.insert(i, 0)
+    st2, ln2 = np.array(st2), np.array(ln2)
+    real = ln2 > 0
+    for thr in (0.0, 0.3, 0.9):
+        keep, p = om.block_mask(q, k, st, ln, st, ln, thr)
+        keep2, p2 = om.block_mask(q, k, st2, ln2, st2, ln2, thr)
+        assert np.array_equal(keep2[np.ix_(real, real)], keep)
+        np.testing.assert_allclose(p2[np.ix_(real, real)], p, rtol=1e-13)
+        assert not keep2[~real].any() and not keep2[:, ~real].any()
+        assert (p2[:, ~real] == 0).all()
+    win = np.ones((7, 7), dtype=bool)
+    keep3, _ = om.block_mask(q, k, st2, ln2, st2, ln2, 0.9, window=win)
+    assert not keep3[~real].any() and keep3[real].all()
