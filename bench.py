@@ -210,6 +210,119 @@ class Runner:
         }
 
 
+def _var_flops(d, cnt, idx, lq, lk):
+    """F_eff over variable blocks: 4 d sum_I len_I sum_{J kept} len_J (device tensors)."""
+    valid = torch.arange(idx.shape[-1], device=idx.device) < cnt[..., None].long()
+    lk = lk.long().expand(*cnt.shape[:2], lk.shape[-1]) if lk.dim() == 1 else lk.long()
+    lq = lq.long().expand(*cnt.shape) if lq.dim() == 1 else lq.long()
+    kl = torch.gather(lk, 2, idx.long().clamp(0, lk.shape[-1] - 1).flatten(2)).view(idx.shape)
+    kl = torch.where(valid, kl, torch.zeros_like(kl)).sum(-1)
+    return 4.0 * d * float((kl * lq).sum())
+
+
+def paths_bench(r: Runner, steps: int = 10, warmup: int = 3):
+    """Stage times (HIP events, means over `steps`) of the reorder-based paths on
+    the 480p layer: fractal + window, per-head box tilings, semantic clusters."""
+    import block_sparse_attention_avg_amd.pipelines as pl
+    from gen import kmeans_uniforms
+    w = r.w
+    dev = r.q.device
+    q, k, v = r.q, r.k, r.v
+    out = {}
+
+    def run(stages):
+        for _ in range(warmup):
+            for _, f in stages:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            for i, (_, f) in enumerate(stages):
+                f()
+                e[i + 1].record()
+        torch.cuda.synchronize()
+        t = {name: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i, (name, _) in enumerate(stages)}
+        t["total"] = sum(e[0].elapsed_time(e[-1]) for e in ev) / steps
+        return {k2: round(v2, 4) for k2, v2 in t.items()}
+
+    def reorder_path(key, perm, blocks, window):
+        st = {}
+        buf = [torch.empty_like(q) for _ in range(4)]
+        nb = blocks.nblocks
+        cnt = torch.empty((w.B, w.H, nb), dtype=torch.int32, device=dev)
+        idx = torch.empty((w.B, w.H, nb, nb), dtype=torch.int32, device=dev)
+
+        def permute():
+            bsa.permute_tokens(q, perm, out=buf[0])
+            bsa.permute_tokens(k, perm, out=buf[1])
+            bsa.permute_tokens(v, perm, out=buf[2])
+
+        def mask():
+            bsa.build_block_mask(buf[0], buf[1], w.thr, window=window, n_valid=w.n_valid, qb=blocks, kb=blocks,
+                                 out=(cnt, idx))
+
+        def attn():
+            bsa.block_sparse_attn_fwd(buf[0], buf[1], buf[2], cnt, idx, n_valid=w.n_valid, qb=blocks, kb=blocks,
+                                      out=buf[3])
+
+        def unpermute():
+            bsa.unpermute_tokens(buf[3], perm, out=r.o)
+        st = run([("permute_qkv", permute), ("mask", mask), ("attention", attn), ("unpermute_o", unpermute)])
+        f = _var_flops(w.d, cnt, idx, blocks.length, blocks.length)
+        st["attn_tflops"] = round(f / (st["attention"] * 1e-3) / 1e12, 3)
+        st["step_tflops"] = round(f / (st["total"] * 1e-3) / 1e12, 3)
+        st["kept_blocks"] = int(cnt.sum())
+        out[key] = st
+
+    wf = WORKLOADS["wan480_fractal_sta"]
+    lay = pl.fractal_layout(wf.T, wf.Hl, wf.Wl, wf.patch, wf.N, dev)
+    reorder_path("fractal_sta", lay.perm, lay.blocks, (*lay.grid, *wf.window))
+    wh = WORKLOADS["wan480_head_tiling"]
+    factors = [wh.tilings[h % len(wh.tilings)] for h in range(wh.H)]
+    ht = pl.head_tiling_layout(wh.T, wh.Hl, wh.Wl, factors, wh.N, wh.B, dev)
+    reorder_path("head_tiling", ht.perm, ht.blocks, None)
+    out["head_tiling"]["factors"] = sorted(set(factors))
+
+    ws = WORKLOADS["wan480_semantic"]
+    uq = torch.from_numpy(kmeans_uniforms(ws.B, ws.H, ws.Cq, stream=0)).to(dev)
+    uk = torch.from_numpy(kmeans_uniforms(ws.B, ws.H, ws.Ck, stream=1)).to(dev)
+    S = {}
+
+    def km():
+        S["cq"], S["aq"], S["nq"] = bsa.kmeans(q, ws.Cq, ws.kmeans_iters, uq, ws.n_valid)
+        S["ck"], S["ak"], S["nk"] = bsa.kmeans(k, ws.Ck, ws.kmeans_iters, uk, ws.n_valid)
+
+    def order():
+        S["pq"], S["sq"], S["lq"] = bsa.cluster_order(S["aq"], ws.Cq, ws.n_valid)
+        S["pk"], S["sk"], S["lk"] = bsa.cluster_order(S["ak"], ws.Ck, ws.n_valid)
+
+    def permute():
+        S["qp"] = bsa.permute_tokens(q, S["pq"])
+        S["kp"] = bsa.permute_tokens(k, S["pk"])
+        S["vp"] = bsa.permute_tokens(v, S["pk"])
+
+    def mask():
+        S["cnt"], S["idx"] = bsa.build_centroid_mask(S["cq"], S["nq"], S["ck"], S["nk"], ws.top_p)
+
+    def attn():
+        S["op"] = bsa.block_sparse_attn_fwd(S["qp"], S["kp"], S["vp"], S["cnt"], S["idx"], n_valid=ws.n_valid,
+                                            qb=bsa.Blocks(S["sq"], S["lq"]), kb=bsa.Blocks(S["sk"], S["lk"]))
+
+    def unpermute():
+        bsa.unpermute_tokens(S["op"], S["pq"], out=r.o)
+    st = run([("kmeans_qk", km), ("cluster_order", order), ("permute_qkv", permute), ("mask", mask),
+              ("attention", attn), ("unpermute_o", unpermute)])
+    f = _var_flops(ws.d, S["cnt"], S["idx"], S["lq"], S["lk"])
+    st["attn_tflops"] = round(f / (st["attention"] * 1e-3) / 1e12, 3)
+    st["step_tflops"] = round(f / (st["total"] * 1e-3) / 1e12, 3)
+    st["kept_blocks"] = int(S["cnt"].sum())
+    st["clusters"] = [ws.Cq, ws.Ck]
+    st["kmeans_iters"] = ws.kmeans_iters
+    out["semantic"] = st
+    return out
+
+
 def mfma_probe():
     """Sustained bf16 MFMA rate from the measurement program built beside the
     library (a child process; None when it is missing or fails)."""
@@ -430,6 +543,9 @@ def main():
                     help="extra steps timed with flushed caches (reported under cold_cache; 0 = skip)")
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="steps timing the backward on the same lists (reported under backward; 0 = skip)")
+    ap.add_argument("--path-steps", type=int, default=10,
+                    help="steps timing the reorder-based paths on the 480p layer (fractal + window, "
+                         "per-head box tilings, semantic clusters; reported under paths; 0 = skip)")
     ap.add_argument("--no-gemm-ref", action="store_true",
                     help="skip the MFMA-rate probe and the dense bf16 GEMM reference")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -512,6 +628,8 @@ def main():
                             "fwd_with_lse_ms": round(tf, 4), "steps": a.bwd_steps,
                             "flops": "2.5 x the forward's effective FLOP (S, dP, dV, dK, dQ products of "
                                      "kept tiles; the dQ pass also recomputes S and dP, not counted)"}
+    if a.path_steps > 0 and a.config == "wan480":
+        line["paths"] = paths_bench(r, a.path_steps)
     if a.cold_reps > 0:
         cm, ca = r.cold(a.cold_reps)
         line["cold_cache"] = {"mask_ms": round(cm, 4), "attention_ms": round(ca, 4),

@@ -58,6 +58,7 @@ _SIGS = {
     "bsa_permute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "bsa_unpermute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "bsa_fractal_order": ([_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_I)], _I),
+    "bsa_tile_order": ([_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_I)], _I),
     "bsa_kmeans_workspace": ([_I, _I, _I, _I, _I], _Z),
     "bsa_kmeans": ([_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
     "bsa_cluster_order_workspace": ([_I, _I, _I, _I], _Z),
@@ -398,6 +399,22 @@ def fractal_order(T: int, Hl: int, Wl: int, P: int, N: Optional[int] = None):
     nb = ctypes.c_int(0)
     _check(load().bsa_fractal_order(T, Hl, Wl, P, N, perm.data_ptr(), st.data_ptr(), ln.data_ptr(),
                                     co.data_ptr(), nb_max, ctypes.byref(nb)), "fractal_order")
+    return perm, st[:nb.value], ln[:nb.value], co[:nb.value]
+
+
+def tile_order(T: int, Hl: int, Wl: int, pt: int, ph: int, pw: int, N: Optional[int] = None):
+    """Host function: pt x ph x pw boxes as contiguous blocks. Returns int32 CPU
+    tensors (perm [N], start [nb], length [nb], coords [nb, 3])."""
+    n = T * Hl * Wl
+    N = n if N is None else N
+    nb_max = (-(-T // pt)) * (-(-Hl // ph)) * (-(-Wl // pw)) if min(pt, ph, pw) > 0 else 1
+    perm = torch.empty(N, dtype=torch.int32)
+    st = torch.empty(nb_max, dtype=torch.int32)
+    ln = torch.empty(nb_max, dtype=torch.int32)
+    co = torch.empty((nb_max, 3), dtype=torch.int32)
+    nb = ctypes.c_int(0)
+    _check(load().bsa_tile_order(T, Hl, Wl, pt, ph, pw, N, perm.data_ptr(), st.data_ptr(), ln.data_ptr(),
+                                 co.data_ptr(), nb_max, ctypes.byref(nb)), "tile_order")
     return perm, st[:nb.value], ln[:nb.value], co[:nb.value]
 
 

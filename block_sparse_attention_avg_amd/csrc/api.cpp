@@ -1,5 +1,6 @@
 // C ABI of libbsa: argument validation, workspace carving and kernel launch
 // (declarations and the contract of every entry point are in include/bsa.h).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -128,7 +129,8 @@ int bsa_select_blocks(const float* qbar, const float* kbar, int B, int H, int nq
   bsa::Window w;
   if (int e = make_window(win, nqb, nkb, w)) return e;
   const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
-  return hip_status(bsa::launch_select(qbar, kbar, B * H, nqb, nkb, d, q_sizes, k_sizes, thr, sc, w,
+  const bsa::Sizes sz{q_sizes, k_sizes, 1, 1, 1};
+  return hip_status(bsa::launch_select(qbar, kbar, B * H, nqb, nkb, d, sz, thr, sc, w,
                                        kv_count, kv_index, kv_stride, stream),
                     "select");
 }
@@ -166,7 +168,9 @@ int bsa_build_block_mask(const void* q, const void* k, int B, int H, int N, int 
   if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(q), BH, N, d, bq, qbar, stream), "pool q")) return e;
   if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(k), BH, N, d, bk, kbar, stream), "pool k")) return e;
   const float sc = 1.f / sqrtf((float)d);
-  return hip_status(bsa::launch_select(qbar, kbar, BH, bq.nblocks, bk.nblocks, d, nullptr, nullptr, thr, sc, w,
+  // descriptor blocks: a block with no tokens takes no part (lengths, no bias)
+  const bsa::Sizes sz{bq.start ? bq.len : nullptr, bk.start ? bk.len : nullptr, bq.per_head, bk.per_head, 0};
+  return hip_status(bsa::launch_select(qbar, kbar, BH, bq.nblocks, bk.nblocks, d, sz, thr, sc, w,
                                        kv_count, kv_index, kv_stride, stream),
                     "select");
 }
@@ -290,36 +294,48 @@ int bsa_unpermute_tokens(const void* x, void* y, const int32_t* perm, int B, int
   return permute_common(x, y, perm, B, H, N, d, perm_per_head, true, stream);
 }
 
-int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm, int32_t* blk_start, int32_t* blk_len,
-                      int32_t* blk_coords, int max_blocks, int* nblocks) {
+int bsa_tile_order(int T, int Hl, int Wl, int pt, int ph, int pw, int N, int32_t* perm, int32_t* blk_start,
+                   int32_t* blk_len, int32_t* blk_coords, int max_blocks, int* nblocks) {
   g_msg[0] = 0;
-  if (T <= 0 || Hl <= 0 || Wl <= 0 || P <= 0) return fail(BSA_EINVAL, "fractal_order: sizes must be positive");
+  if (T <= 0 || Hl <= 0 || Wl <= 0) return fail(BSA_EINVAL, "tile_order: latent sizes must be positive");
+  if (pt <= 0 || ph <= 0 || pw <= 0) return fail(BSA_EINVAL, "tile_order: box sizes must be positive");
   const long long n = (long long)T * Hl * Wl;
-  if (n > 0x7fffffffLL || N < n) return fail(BSA_EINVAL, "fractal_order: N must be >= T*Hl*Wl");
-  if (!perm || !blk_start || !blk_len || !nblocks) return fail(BSA_EINVAL, "fractal_order: null pointer");
-  const int npy = (Hl + P - 1) / P, npx = (Wl + P - 1) / P;
-  const long long nb = (long long)T * npy * npx;
+  if (n > 0x7fffffffLL || N < n) return fail(BSA_EINVAL, "tile_order: N must be >= T*Hl*Wl");
+  if (!perm || !blk_start || !blk_len || !nblocks) return fail(BSA_EINVAL, "tile_order: null pointer");
+  const int nbt = (T + pt - 1) / pt, nby = (Hl + ph - 1) / ph, nbx = (Wl + pw - 1) / pw;
+  const long long nb = (long long)nbt * nby * nbx;
   *nblocks = (int)nb;
-  if (nb > max_blocks) return fail(BSA_ENOSPC, "fractal_order: %lld blocks > max_blocks %d", nb, max_blocks);
+  if (nb > max_blocks) return fail(BSA_ENOSPC, "tile_order: %lld blocks > max_blocks %d", nb, max_blocks);
+  // walk the boxes in grid order and each box in raster order
   int pos = 0, b = 0;
-  for (int t = 0; t < T; ++t)
-    for (int py = 0; py < npy; ++py)
-      for (int px = 0; px < npx; ++px) {
+  for (int bt = 0; bt < nbt; ++bt)
+    for (int by = 0; by < nby; ++by)
+      for (int bx = 0; bx < nbx; ++bx) {
         blk_start[b] = pos;
-        const int y1 = py * P + P < Hl ? py * P + P : Hl;
-        const int x1 = px * P + P < Wl ? px * P + P : Wl;
-        for (int y = py * P; y < y1; ++y)
-          for (int x = px * P; x < x1; ++x) perm[pos++] = (t * Hl + y) * Wl + x;
+        const int t1 = std::min(T, bt * pt + pt), y1 = std::min(Hl, by * ph + ph), x1 = std::min(Wl, bx * pw + pw);
+        for (int t = bt * pt; t < t1; ++t)
+          for (int y = by * ph; y < y1; ++y)
+            for (int x = bx * pw; x < x1; ++x) perm[pos++] = (t * Hl + y) * Wl + x;
         blk_len[b] = pos - blk_start[b];
         if (blk_coords) {
-          blk_coords[3 * b + 0] = t;
-          blk_coords[3 * b + 1] = py;
-          blk_coords[3 * b + 2] = px;
+          blk_coords[3 * b + 0] = bt;
+          blk_coords[3 * b + 1] = by;
+          blk_coords[3 * b + 2] = bx;
         }
         ++b;
       }
   for (int i = (int)n; i < N; ++i) perm[i] = i;
   return BSA_OK;
+}
+
+int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm, int32_t* blk_start, int32_t* blk_len,
+                      int32_t* blk_coords, int max_blocks, int* nblocks) {
+  // P x P patches of one frame: boxes of 1 x P x P
+  if (P <= 0) {
+    g_msg[0] = 0;
+    return fail(BSA_EINVAL, "fractal_order: sizes must be positive");
+  }
+  return bsa_tile_order(T, Hl, Wl, 1, P, P, N, perm, blk_start, blk_len, blk_coords, max_blocks, nblocks);
 }
 
 size_t bsa_kmeans_workspace(int B, int H, int N, int C, int d) {

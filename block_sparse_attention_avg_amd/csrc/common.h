@@ -50,6 +50,23 @@ struct Blocks {
   }
 };
 
+// Per-block sizes seen by the select kernel. bias != 0: cluster sizes n_J
+// (centroid rule: log n_J added to the logits, per head); bias == 0: block
+// lengths (a block with no tokens takes no part). In both, a size <= 0
+// excludes a key block and empties a query row.
+struct Sizes {
+  const int32_t* q;     // null, or [nqb] / [BH][nqb]
+  const int32_t* k;     // null, or [nkb] / [BH][nkb]
+  int q_per_head, k_per_head;
+  int bias;
+  __device__ __forceinline__ const int32_t* krow(int bh, int nkb) const {
+    return k ? k + (k_per_head ? (size_t)bh * nkb : 0) : nullptr;
+  }
+  __device__ __forceinline__ bool q_empty(int bh, int nqb, int row) const {
+    return q && q[(q_per_head ? (size_t)bh * nqb : 0) + row] <= 0;
+  }
+};
+
 struct Window {
   int nt, ny, nx, rt, ry, rx;
   int enabled;
@@ -101,7 +118,7 @@ namespace bsa {
 hipError_t launch_pool(const uint16_t* x, int BH, int N, int d, const Blocks& blk, float* out,
                        hipStream_t s);
 hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, int nkb, int d,
-                         const int32_t* q_sizes, const int32_t* k_sizes, float thr, float scale,
+                         const Sizes& sizes, float thr, float scale,
                          const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
                          hipStream_t s);
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,

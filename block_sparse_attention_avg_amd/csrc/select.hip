@@ -221,8 +221,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
 template <int D, int R, int E>
 __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
-    const int32_t* __restrict__ q_sizes, const int32_t* __restrict__ k_sizes, float thr,
-    float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+    Sizes sz, float thr, float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
     int kv_stride) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
@@ -277,10 +276,10 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
     if (kok) {
       float bias = 0.f;
       bool excluded = false;
-      if (k_sizes) {
-        const int n = k_sizes[(size_t)bh * nkb + key];
+      if (const int32_t* ks = sz.krow(bh, nkb)) {
+        const int n = ks[key];
         excluded = n <= 0;
-        bias = excluded ? 0.f : logf((float)n);
+        bias = excluded || !sz.bias ? 0.f : logf((float)n);
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -300,13 +299,13 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
     if (row >= nqb) break;
     const size_t orow = (size_t)bh * nqb + row;
     int32_t* out = kv_index + orow * kv_stride;
-    if (q_sizes && q_sizes[orow] <= 0) {
+    if (sz.q_empty(bh, nqb, row)) {
       if (lane == 0) kv_count[orow] = 0;
       continue;
     }
     float* sr = sc + rr * nkb_pad;
     if constexpr (E > 0) {
-      const int n = select_row_regs<E>(sr, nkb, thr, row, k_sizes ? k_sizes + (size_t)bh * nkb : nullptr,
+      const int n = select_row_regs<E>(sr, nkb, thr, row, sz.krow(bh, nkb),
                                        win, h, out, lane);
       if (lane == 0) kv_count[orow] = n;
       continue;
@@ -383,7 +382,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
         const unsigned long long key =
             ((unsigned long long)__float_as_uint(sr[j]) << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - j);
         keep = key >= kstar;
-        if (k_sizes && k_sizes[(size_t)bh * nkb + j] <= 0) keep = false;
+        if (const int32_t* ks = sz.krow(bh, nkb)) keep = keep && ks[j] > 0;
         if (win.enabled && win.inside(row, j)) keep = true;
       }
       const unsigned long long bal = __ballot(keep);
@@ -396,8 +395,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
 
 template <int D, int R, int E>
 static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
-                                  const int32_t* q_sizes, const int32_t* k_sizes, float thr,
-                                  float scale, const Window& win, int32_t* kv_count,
+                                  const Sizes& sz, float thr, float scale, const Window& win, int32_t* kv_count,
                                   int32_t* kv_index, int kv_stride, hipStream_t s) {
   const int nkb_pad = (nkb + 3) & ~3;
   const size_t lds = (size_t)R * nkb_pad * sizeof(float) + kSelWaves * kHist * sizeof(unsigned long long);
@@ -406,18 +404,18 @@ static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((nqb + R - 1) / R, BH);
-  kern<<<grid, 64 * kSelWaves, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, q_sizes, k_sizes, thr, scale, win,
+  kern<<<grid, 64 * kSelWaves, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, sz, thr, scale, win,
                               kv_count, kv_index, kv_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, int nkb, int d,
-                         const int32_t* q_sizes, const int32_t* k_sizes, float thr, float scale,
+                         const Sizes& sz, float thr, float scale,
                          const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
                          hipStream_t s) {
   if (BH == 0 || nqb == 0) return hipSuccess;
 #define BSA_SEL(DD, RR, EE) \
-  launch_select_t<DD, RR, EE>(qbar, kbar, BH, nqb, nkb, q_sizes, k_sizes, thr, scale, win, kv_count, kv_index, kv_stride, s)
+  launch_select_t<DD, RR, EE>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win, kv_count, kv_index, kv_stride, s)
   // rows of up to 2048 key blocks are selected from registers (E per lane)
   if (d == 128) {
     if (nkb <= 512) return BSA_SEL(128, 16, 8);

@@ -5,6 +5,11 @@ are reordered by fractal flattening, the content-adaptive CDF mask is built
 on the patch blocks and OR'd with the static sliding-tile window, attention
 runs over the kept patch tiles and the output is put back in raster order.
 
+``head_tiled_attention`` -- Veda summary, section 2.2: every head has its
+own p_t x p_h x p_w factorisation of the tile, so each head gets its own token
+order and its own box blocks; the CDF mask and the attention then run over
+each head's boxes and the output returns to raster order.
+
 ``semantic_attention`` -- Sparse VideoGen2 summary, Metodologia A-C: Q and K
 are clustered with k-means, tokens are permuted cluster-contiguously, the
 centroid top-p rule selects key clusters per query cluster, attention runs
@@ -22,7 +27,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import (Blocks, block_sparse_attn_fwd, build_block_mask, build_centroid_mask,
-               cluster_order, fractal_order, kmeans, permute_tokens, unpermute_tokens)
+               cluster_order, fractal_order, kmeans, permute_tokens, tile_order, unpermute_tokens)
 
 
 @dataclasses.dataclass
@@ -52,6 +57,46 @@ def fractal_sta_attention(q, k, v, layout: FractalLayout, thr: float,
                                 qb=layout.blocks, kb=layout.blocks)
     op = block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=n_valid,
                                qb=layout.blocks, kb=layout.blocks)
+    o = unpermute_tokens(op, layout.perm)
+    return (o, cnt, idx) if return_mask else o
+
+
+@dataclasses.dataclass
+class HeadTiling:
+    """Per-head box orders of a T x Hl x Wl latent, on the device."""
+    perm: torch.Tensor          # int32 [B, H, N]: head h's token order
+    blocks: Blocks              # per head [B, H, nb]: head h's boxes, then empty blocks
+    factors: Tuple[Tuple[int, int, int], ...]   # (pt, ph, pw) of each head
+    nblocks: Tuple[int, ...]    # real boxes of each head
+
+
+def head_tiling_layout(T: int, Hl: int, Wl: int, factors, N: int, B: int, device) -> HeadTiling:
+    """One ``tile_order`` per head; block lists are padded to a common count
+    with blocks of length 0 (they take no part in the mask)."""
+    orders = [tile_order(T, Hl, Wl, *f, N) for f in factors]
+    nb = max(len(o[1]) for o in orders)
+    H = len(factors)
+    perm = torch.stack([o[0] for o in orders])
+    st = torch.full((H, nb), T * Hl * Wl, dtype=torch.int32)
+    ln = torch.zeros((H, nb), dtype=torch.int32)
+    for h, o in enumerate(orders):
+        st[h, :len(o[1])] = o[1]
+        ln[h, :len(o[2])] = o[2]
+
+    def dev(x):
+        return x.unsqueeze(0).expand(B, *x.shape).contiguous().to(device)
+    return HeadTiling(dev(perm), Blocks(dev(st), dev(ln)), tuple(tuple(f) for f in factors),
+                      tuple(len(o[1]) for o in orders))
+
+
+def head_tiled_attention(q, k, v, layout: HeadTiling, thr: float, n_valid: Optional[int] = None,
+                         return_mask: bool = False):
+    """Per-head reorder -> CDF mask over each head's boxes -> attention -> inverse reorder."""
+    qp = permute_tokens(q, layout.perm)
+    kp = permute_tokens(k, layout.perm)
+    vp = permute_tokens(v, layout.perm)
+    cnt, idx = build_block_mask(qp, kp, thr, n_valid=n_valid, qb=layout.blocks, kb=layout.blocks)
+    op = block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=n_valid, qb=layout.blocks, kb=layout.blocks)
     o = unpermute_tokens(op, layout.perm)
     return (o, cnt, idx) if return_mask else o
 

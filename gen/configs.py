@@ -13,7 +13,12 @@ The method parameters come from the pages:
   * fractal flattening into P x P spatial patches -- NABLA summary
     (Metodologia, section 1);
   * k-means clusters C_q, C_k and the top-p budget -- Sparse VideoGen2
-    summary (Metodologia A "Clustering" and B "Strategia Top-p").
+    summary (Metodologia A "Clustering" and B "Strategia Top-p");
+  * per-head tile factorisations (p_t, p_h, p_w) of the 64-token tile --
+    Veda summary, section 2.2 (the three factorisations of 64 into a
+    frame x row x column box that fit a 480p latent; the pages choose one per
+    head offline on a calibration set, which is not reproduced: heads take
+    them in turn).
 
 ``gain`` is the scale g applied to the Fourier-feature Q/K generator so that
 the content-adaptive mask drops the target share of key blocks. The values
@@ -49,6 +54,7 @@ class Workload:
     kmeans_iters: int = 0
     top_p: float = 0.0
     target_sparsity: Optional[Tuple[float, float]] = None
+    tilings: Optional[Tuple[Tuple[int, int, int], ...]] = None   # head h takes tilings[h % len]
 
     @property
     def n_valid(self) -> int:
@@ -86,8 +92,12 @@ WAN480_SEMANTIC = dataclasses.replace(
     WAN480, key="wan480_semantic", order="semantic", Cq=64, Ck=256,
     kmeans_iters=10, top_p=0.9, thr=0.1, target_sparsity=None)
 
+WAN480_HEAD_TILING = dataclasses.replace(
+    WAN480, key="wan480_head_tiling", order="head_tiling",
+    tilings=((1, 8, 8), (2, 4, 8), (4, 4, 4)), target_sparsity=None)
+
 WORKLOADS = {w.key: w for w in (TINY, WAN480, HUNYUAN720,
-                                WAN480_FRACTAL_STA, WAN480_SEMANTIC)}
+                                WAN480_FRACTAL_STA, WAN480_SEMANTIC, WAN480_HEAD_TILING)}
 
 # Configs in the order they are listed for this method (1-based index).
 BY_INDEX = {1: TINY, 2: WAN480, 3: HUNYUAN720, 4: WAN480_FRACTAL_STA,

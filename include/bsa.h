@@ -148,7 +148,9 @@ size_t bsa_build_block_mask_workspace(int B, int H, int nqb, int nkb, int d);
 /*
  * Whole mask stage: bsa_pool_blocks on q and k, then bsa_select_blocks with
  * equal weights. q, k bf16 [B,H,N,d]; qb/kb block descriptors (NULL =
- * uniform `block`-token blocks); ws of at least
+ * uniform `block`-token blocks); a descriptor block of length 0 has no
+ * average and takes no part: never kept as a key block (unless the window
+ * covers it), and as a query block it keeps nothing; ws of at least
  * bsa_build_block_mask_workspace(...) bytes (device, 256-byte aligned).
  * Outputs as in bsa_select_blocks.
  */
@@ -318,6 +320,30 @@ int bsa_unpermute_tokens(const void* x, void* y, const int32_t* perm, int B,
 int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm,
                       int32_t* blk_start, int32_t* blk_len,
                       int32_t* blk_coords, int max_blocks, int* nblocks);
+
+/*
+ * Head-aware tiling layout (Veda summary, section 2.2 "Tiling Consapevole
+ * delle Teste"): a pure host function on caller-owned HOST arrays. Each
+ * pt x ph x pw box of the T x Hl x Wl latent (a factorisation of the
+ * hardware tile, e.g. 1x8x8, 2x4x8 or 4x4x4 for 64-token tiles) becomes one
+ * contiguous block. Boxes are numbered row-major over the
+ * ceil(T/pt) x ceil(Hl/ph) x ceil(Wl/pw) grid (frame boxes slowest); tokens
+ * inside a box keep raster order; edge boxes are smaller, no tokens are
+ * inserted. A caller gives each head its own factorisation by calling this
+ * once per head and stacking the results into per-head permutations
+ * ([B,H,N], see bsa_permute_tokens) and per-head block descriptors
+ * ([B,H,nblocks], padded to a common count with blocks of length 0, which
+ * take no part in the mask). bsa_fractal_order is the (1, P, P) case.
+ *   perm        int32 [N] out: perm[new] = old raster index; positions
+ *               >= T*Hl*Wl map to themselves (N >= T*Hl*Wl)
+ *   blk_start, blk_len  int32 [max_blocks] out: one block per box
+ *   blk_coords  int32 [max_blocks*3] out or NULL: (box_t, box_y, box_x)
+ *   nblocks     out: the box count; BSA_ENOSPC if larger than max_blocks
+ * Errors: BSA_EINVAL for non-positive sizes, N < T*Hl*Wl or a null pointer.
+ */
+int bsa_tile_order(int T, int Hl, int Wl, int pt, int ph, int pw, int N,
+                   int32_t* perm, int32_t* blk_start, int32_t* blk_len,
+                   int32_t* blk_coords, int max_blocks, int* nblocks);
 
 /* ------------------------------------------------------------------------
  * Semantic clustering (Sparse VideoGen2 summary, Metodologia A)

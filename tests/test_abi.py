@@ -100,6 +100,28 @@ def test_fractal_order_host_function_matches_reference(T, Hl, Wl, P, N):
     assert np.array_equal(ln.numpy(), rl) and np.array_equal(co.numpy(), rc)
 
 
+@pytest.mark.parametrize("T,Hl,Wl,f,N", [(21, 30, 52, (2, 4, 8), 32768), (21, 30, 52, (4, 4, 4), 32768),
+                                         (5, 6, 9, (3, 2, 5), 280), (2, 3, 3, (4, 4, 4), 18)])
+def test_tile_order_host_function_matches_reference(T, Hl, Wl, f, N):
+    perm, st, ln, co = bsa.tile_order(T, Hl, Wl, *f, N)
+    rp, rs, rl, rc = ol.tile_order(T, Hl, Wl, *f, N)
+    assert np.array_equal(perm.numpy(), rp) and np.array_equal(st.numpy(), rs)
+    assert np.array_equal(ln.numpy(), rl) and np.array_equal(co.numpy(), rc)
+
+
+def test_tile_order_errors(lib):
+    perm = (ctypes.c_int32 * 256)()
+    st = (ctypes.c_int32 * 4)()
+    ln = (ctypes.c_int32 * 4)()
+    nb = ctypes.c_int(0)
+    args = [ctypes.cast(perm, ctypes.c_void_p), ctypes.cast(st, ctypes.c_void_p), ctypes.cast(ln, ctypes.c_void_p),
+            None, 4, ctypes.byref(nb)]
+    assert lib.bsa_tile_order(4, 8, 8, 2, 4, 4, 256, *args) == 3 and nb.value == 8       # ENOSPC
+    assert lib.bsa_tile_order(4, 8, 8, 0, 4, 4, 256, *args) == 1                         # EINVAL
+    assert lib.bsa_tile_order(4, 8, 8, 2, 4, 4, 255, *args) == 1                         # N too small
+    assert lib.bsa_tile_order(1, 8, 8, 1, 4, 4, 64, *args) == 0 and nb.value == 4
+
+
 def test_fractal_order_capacity(lib):
     perm = (ctypes.c_int32 * 256)()
     st = (ctypes.c_int32 * 4)()

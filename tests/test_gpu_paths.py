@@ -2,6 +2,8 @@
 
   * fractal flattening + CDF mask OR sliding-tile window + attention over
     variable-length patch blocks + inverse reorder (480p layer, 588 patches);
+  * per-head box orders (head-aware tiling) + CDF mask + attention over each
+    head's boxes + inverse reorder;
   * k-means of Q and K, cluster-contiguous order, centroid top-p mask,
     attention over variable-size cluster blocks, inverse permutation.
 
@@ -125,6 +127,48 @@ def test_window_only_mask_is_static_sta(gpu_lib):
     win = ol.window_blocks(coords, coords, *w.window)
     wc = win.sum(1)
     assert ((cnt[0] == wc[None]) | (cnt[0] == wc[None] + 1)).all()
+
+
+# ------------------------------------------------------------------ head-aware tiling
+
+def test_head_tiling_path(gpu_lib):
+    # each head has its own box factorisation, so its own order and blocks
+    # (588, 616 and 624 boxes, padded to 624 with empty blocks)
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_head_tiling"]
+    q, k, v = _wan480()
+    factors = [w.tilings[h % len(w.tilings)] for h in range(w.H)]
+    say(f"head-aware tiling path, 480p layer, factorisations {sorted(set(factors))}")
+    lay = pl.head_tiling_layout(w.T, w.Hl, w.Wl, factors, w.N, w.B, "cuda")
+    assert lay.nblocks[:3] == (588, 616, 624)
+    o, cnt, idx = pl.head_tiled_attention(q.cuda(), k.cuda(), v.cuda(), lay, w.thr, n_valid=w.n_valid,
+                                          return_mask=True)
+    torch.cuda.synchronize()
+    o, cnt, idx = _np(o), cnt.cpu().numpy(), idx.cpu().numpy()
+    assert (o[:, :, w.n_valid:] == 0).all()
+    nbp = lay.blocks.nblocks
+    rng = np.random.default_rng(1)
+    for h in (0, 1, 2, 7):
+        perm, st, ln, _ = ol.tile_order(w.T, w.Hl, w.Wl, *factors[h], w.N)
+        assert np.array_equal(lay.perm[0, h].cpu().numpy(), perm)
+        nb = len(st)
+        stp = np.concatenate([st, np.full(nbp - nb, w.n_valid)])
+        lnp = np.concatenate([ln, np.zeros(nbp - nb, np.int64)])
+        keep = keep_from_lists(cnt[0, h], idx[0, h], nbp)
+        assert not keep[nb:].any() and not keep[:, nb:].any(), "empty blocks take no part"
+        keep = keep[:nb, :nb]
+        qh, kh, vh = _np(q[0, h]), _np(k[0, h]), _np(v[0, h])
+        ref_keep, P = om.block_mask(qh[perm], kh[perm], stp, lnp, stp, lnp, w.thr)
+        assert not ref_keep[nb:].any() and not ref_keep[:, nb:].any()
+        ref_keep, P = ref_keep[:nb, :nb], P[:nb, :nb]
+        bad = mask_mismatches(P, w.thr, keep)
+        say(f"  head {h} {factors[h]}: kept {keep.sum()}/{keep.size}, differing bits "
+            f"{(keep != ref_keep).sum()}, sure-bit mismatches {bad}")
+        assert bad == 0
+        blocks = sorted(set(rng.choice(nb, 12, replace=False).tolist()) | {0, nb - 1})
+        ref = oa.permuted_attention(qh, kh, vh, perm, perm, st, ln, st, ln, keep, blocks=blocks)
+        rows = perm[np.concatenate([np.arange(st[b], st[b] + ln[b]) for b in blocks])]
+        _check_out(o[0, h], ref, rows, f"head {h} ({len(blocks)} box blocks)")
 
 
 # ------------------------------------------------------------------ semantic clustering
