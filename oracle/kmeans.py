@@ -14,7 +14,10 @@ Pins (tests/test_oracle_kmeans.py): well-separated hand-made clusters are
 recovered exactly; C = 1 gives the global mean; inertia never increases over
 Lloyd rounds; final centroids are the means of their members; every point is
 nearest to its own centroid; seeding follows the D^2 inverse-CDF rule
-(checked against a brute-force loop); the cluster order is a stable sort.
+(checked against a brute-force loop); the cluster order is a stable sort;
+``kmeans_warm`` -- a hand-worked 1-D case (tests/golden/kmeans_warm_cases.txt),
+a cold run equals a warm start from its seeds, converged centroids are a
+fixed point.
 """
 
 from __future__ import annotations
@@ -94,6 +97,38 @@ def kmeans(x: np.ndarray, C: int, iters: int, u: np.ndarray):
         cent, sizes = update(x, a, cent)
         hist.append(inertia(x, a, cent))
     return cent, a, sizes, seeds, hist
+
+
+def kmeans_warm(x: np.ndarray, cent0: np.ndarray, max_iters: int):
+    """Lloyd rounds started from given centroids, stopping at a fixed point.
+
+    Sparse VideoGen2 summary, Metodologia C.1 ("Cache dei Centroidi"): the
+    centroids of the previous denoising step initialise k-means at the next
+    step, so no seeding is done. Each round assigns every point to its nearest
+    centroid and moves the centroids to the cluster means (``assign`` and
+    ``update`` above). ``changes[t]`` is the number of points whose assignment
+    differs from round t - 1 (round 0 counts all points). A round that moves no
+    point leaves the centroids where they were, so every later round would
+    repeat it: the loop stops there and the remaining entries are 0.
+
+    Returns (centroids float64 [C, d], assignment int64 [n], sizes int64 [C],
+    changes int64 [max_iters]).
+    """
+    x = np.asarray(x, np.float64)
+    cent = np.array(cent0, dtype=np.float64, copy=True)
+    n = x.shape[0]
+    changes = np.zeros(max_iters, dtype=np.int64)
+    a_prev = None
+    a = np.zeros(n, dtype=np.int64)
+    sizes = np.zeros(cent.shape[0], dtype=np.int64)
+    for t in range(max_iters):
+        a = assign(x, cent)
+        changes[t] = n if a_prev is None else int((a != a_prev).sum())
+        cent, sizes = update(x, a, cent)
+        if changes[t] == 0:
+            break
+        a_prev = a
+    return cent, a, sizes, changes
 
 
 def cluster_order(a: np.ndarray, C: int, N: int | None = None):

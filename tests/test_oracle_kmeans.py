@@ -84,3 +84,48 @@ def test_cluster_order_is_stable_sort():
     for c in range(9):
         seg = perm[start[c]:start[c] + size[c]]
         assert (a[seg] == c).all() and (np.diff(seg) > 0).all()
+
+
+# ----------------------------------------------------------- warm start
+
+def _warm_cases():
+    with open(os.path.join(GOLDEN, "kmeans_warm_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                p, c, it, a, cf, ch = (s.split() for s in line.split("|"))
+                yield ([float(v) for v in p], [float(v) for v in c], int(it[0]), [int(v) for v in a],
+                       [float(v) for v in cf], [int(v) for v in ch])
+
+
+@pytest.mark.parametrize("pts,start,iters,a,cent,changes", list(_warm_cases()))
+def test_warm_start_golden(pts, start, iters, a, cent, changes):
+    x = np.array(pts)[:, None]
+    c, got_a, sizes, got_ch = ok.kmeans_warm(x, np.array(start)[:, None], iters)
+    assert got_a.tolist() == a and got_ch.tolist() == changes
+    np.testing.assert_allclose(c[:, 0], cent, rtol=0, atol=1e-12)
+    assert sizes.tolist() == np.bincount(a, minlength=len(start)).tolist()
+
+
+def test_cold_run_is_warm_start_from_its_seeds():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.normal(m, 1.0, size=(60, 3)) for m in (0.0, 4.0, 9.0, 15.0)])
+    u = rng.random(6)
+    for iters in (1, 3, 12):
+        c, a, s, seeds, _ = ok.kmeans(x, 6, iters, u)
+        cw, aw, sw, ch = ok.kmeans_warm(x, x[seeds], iters)
+        assert np.array_equal(a, aw) and np.array_equal(s, sw)
+        np.testing.assert_array_equal(c, cw)
+        assert ch[0] == len(x)
+
+
+def test_converged_centroids_are_a_fixed_point():
+    rng = np.random.default_rng(22)
+    x = rng.normal(size=(300, 4))
+    c, a, s, ch = ok.kmeans_warm(x, x[:8], 200)
+    stop = int(np.argmax(ch == 0))
+    assert ch[stop] == 0 and (ch[stop:] == 0).all() and (ch[1:stop] > 0).all()
+    c2, a2, s2, ch2 = ok.kmeans_warm(x, c, 5)
+    assert ch2.tolist() == [300, 0, 0, 0, 0]
+    np.testing.assert_array_equal(c2, c)
+    assert np.array_equal(a2, a) and np.array_equal(s2, s)
