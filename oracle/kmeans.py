@@ -99,17 +99,19 @@ def kmeans(x: np.ndarray, C: int, iters: int, u: np.ndarray):
     return cent, a, sizes, seeds, hist
 
 
-def kmeans_warm(x: np.ndarray, cent0: np.ndarray, max_iters: int):
-    """Lloyd rounds started from given centroids, stopping at a fixed point.
+def kmeans_warm(x: np.ndarray, cent0: np.ndarray, max_iters: int, tol_moves: int = 0):
+    """Lloyd rounds started from given centroids, stopping once (nearly) settled.
 
     Sparse VideoGen2 summary, Metodologia C.1 ("Cache dei Centroidi"): the
     centroids of the previous denoising step initialise k-means at the next
     step, so no seeding is done. Each round assigns every point to its nearest
     centroid and moves the centroids to the cluster means (``assign`` and
     ``update`` above). ``changes[t]`` is the number of points whose assignment
-    differs from round t - 1 (round 0 counts all points). A round that moves no
-    point leaves the centroids where they were, so every later round would
-    repeat it: the loop stops there and the remaining entries are 0.
+    differs from round t - 1 (round 0 counts all points). The loop stops after
+    the first round that moves at most ``tol_moves`` points (its update is
+    kept) and the remaining entries are 0. With tol_moves = 0 that round moved
+    nothing, so it left the centroids where they were and every later round
+    would repeat it: the result is the fixed point.
 
     Returns (centroids float64 [C, d], assignment int64 [n], sizes int64 [C],
     changes int64 [max_iters]).
@@ -125,7 +127,7 @@ def kmeans_warm(x: np.ndarray, cent0: np.ndarray, max_iters: int):
         a = assign(x, cent)
         changes[t] = n if a_prev is None else int((a != a_prev).sum())
         cent, sizes = update(x, a, cent)
-        if changes[t] == 0:
+        if changes[t] <= tol_moves:
             break
         a_prev = a
     return cent, a, sizes, changes

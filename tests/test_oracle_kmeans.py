@@ -93,15 +93,15 @@ def _warm_cases():
         for line in f:
             line = line.strip()
             if line and not line.startswith("#"):
-                p, c, it, a, cf, ch = (s.split() for s in line.split("|"))
-                yield ([float(v) for v in p], [float(v) for v in c], int(it[0]), [int(v) for v in a],
-                       [float(v) for v in cf], [int(v) for v in ch])
+                p, c, it, tol, a, cf, ch = (s.split() for s in line.split("|"))
+                yield ([float(v) for v in p], [float(v) for v in c], int(it[0]), int(tol[0]),
+                       [int(v) for v in a], [float(v) for v in cf], [int(v) for v in ch])
 
 
-@pytest.mark.parametrize("pts,start,iters,a,cent,changes", list(_warm_cases()))
-def test_warm_start_golden(pts, start, iters, a, cent, changes):
+@pytest.mark.parametrize("pts,start,iters,tol,a,cent,changes", list(_warm_cases()))
+def test_warm_start_golden(pts, start, iters, tol, a, cent, changes):
     x = np.array(pts)[:, None]
-    c, got_a, sizes, got_ch = ok.kmeans_warm(x, np.array(start)[:, None], iters)
+    c, got_a, sizes, got_ch = ok.kmeans_warm(x, np.array(start)[:, None], iters, tol)
     assert got_a.tolist() == a and got_ch.tolist() == changes
     np.testing.assert_allclose(c[:, 0], cent, rtol=0, atol=1e-12)
     assert sizes.tolist() == np.bincount(a, minlength=len(start)).tolist()
