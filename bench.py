@@ -320,6 +320,44 @@ def paths_bench(r: Runner, steps: int = 10, warmup: int = 3):
     st["clusters"] = [ws.Cq, ws.Ck]
     st["kmeans_iters"] = ws.kmeans_iters
     out["semantic"] = st
+
+    # the next denoising step: k-means warm-started from this step's centroids
+    from gen import next_step
+    q1 = next_step(r.q_cpu, 1, stream=0).to(dev)
+    k1 = next_step(r.k_cpu, 1, stream=1).to(dev)
+    cq0, ck0 = S["cq"], S["ck"]
+    cap = 100
+    tol = ws.n_valid // 100                     # stop once a round moves <= 1 % of the tokens
+
+    def rounds(ch):
+        c = ch.reshape(-1, ch.shape[-1]).cpu().numpy()
+        rr = [int(np.argmax(x <= tol)) + 1 if (x <= tol).any() else ch.shape[-1] for x in c]
+        return {"mean": round(float(np.mean(rr)), 2), "max": int(np.max(rr))}
+
+    def warm():
+        S["wq"] = bsa.kmeans_warm(q1, cq0, cap, ws.n_valid, tol)
+        S["wk"] = bsa.kmeans_warm(k1, ck0, cap, ws.n_valid, tol)
+    tw = run([("kmeans_qk_warm", warm)])
+    # cold start on the same step, run to convergence: seeding, then Lloyd
+    # rounds from the seeds until no token moves
+    sq0, _, _ = bsa.kmeans(q1, ws.Cq, 0, uq, ws.n_valid)
+    sk0, _, _ = bsa.kmeans(k1, ws.Ck, 0, uk, ws.n_valid)
+
+    def cold():
+        bsa.kmeans(q1, ws.Cq, 0, uq, ws.n_valid)
+        bsa.kmeans(k1, ws.Ck, 0, uk, ws.n_valid)
+        S["cq1"] = bsa.kmeans_warm(q1, sq0, cap, ws.n_valid, tol)
+        S["ck1"] = bsa.kmeans_warm(k1, sk0, cap, ws.n_valid, tol)
+    tc = run([("kmeans_qk_cold", cold)])
+    out["semantic_next_step"] = {
+        "what": "k-means of Q and K at the next denoising step (inputs drifted by 5 % RMS noise): warm start "
+                "from the previous step's centroids vs k-means++ seeding + Lloyd rounds, both run until a "
+                f"round moves at most {tol} tokens (1 %; at most {cap} rounds)",
+        "warm_ms": tw["kmeans_qk_warm"], "cold_ms": tc["kmeans_qk_cold"],
+        "speedup": round(tc["kmeans_qk_cold"] / tw["kmeans_qk_warm"], 2),
+        "warm_rounds_q": rounds(S["wq"][3]), "warm_rounds_k": rounds(S["wk"][3]),
+        "cold_rounds_q": rounds(S["cq1"][3]), "cold_rounds_k": rounds(S["ck1"][3]),
+    }
     return out
 
 

@@ -61,6 +61,7 @@ _SIGS = {
     "bsa_tile_order": ([_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_I)], _I),
     "bsa_kmeans_workspace": ([_I, _I, _I, _I, _I], _Z),
     "bsa_kmeans": ([_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "bsa_kmeans_warm": ([_P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
     "bsa_cluster_order_workspace": ([_I, _I, _I, _I], _Z),
     "bsa_cluster_order": ([_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
 }
@@ -437,6 +438,31 @@ def kmeans(x: torch.Tensor, C: int, iters: int, uniforms: torch.Tensor, n_valid:
                           assign.data_ptr(), sizes.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)),
            "kmeans")
     return cent, assign, sizes
+
+
+def kmeans_warm(x: torch.Tensor, centroids: torch.Tensor, max_iters: int, n_valid: Optional[int] = None,
+                tol_moves: int = 0):
+    """Lloyd rounds from the given centroids [B,H,C,d] (not modified), stopping
+    per head after the first round that moves at most tol_moves tokens.
+    Returns (centroids, assign, sizes, changes [B,H,max_iters])."""
+    B, H, N, d = _qkv(x, "x")
+    n_valid = N if n_valid is None else n_valid
+    _dev_tensor(centroids, torch.float32, "centroids")
+    if centroids.dim() != 4 or centroids.shape[:2] != (B, H) or centroids.shape[3] != d:
+        raise ValueError("centroids must be [B, H, C, d]")
+    C = centroids.shape[2]
+    cent = centroids.clone()
+    assign = torch.empty((B, H, N), dtype=torch.int32, device=x.device)
+    sizes = torch.empty((B, H, C), dtype=torch.int32, device=x.device)
+    changes = torch.empty((B, H, max(max_iters, 1)), dtype=torch.int32, device=x.device)
+    lib = load()
+    ws_bytes = lib.bsa_kmeans_workspace(B, H, N, C, d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.bsa_kmeans_warm(x.data_ptr(), B, H, N, d, n_valid, C, max_iters, tol_moves, cent.data_ptr(),
+                               assign.data_ptr(),
+                               sizes.data_ptr(), changes.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)),
+           "kmeans_warm")
+    return cent, assign, sizes, changes
 
 
 def cluster_order(assign: torch.Tensor, C: int, n_valid: Optional[int] = None):

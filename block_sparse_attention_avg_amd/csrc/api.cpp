@@ -355,8 +355,27 @@ int bsa_kmeans(const void* x, int B, int H, int N, int d, int n_valid, int C, in
   const size_t need = bsa_kmeans_workspace(B, H, N, C, d);
   if (ws == nullptr || ws_bytes < need) return fail(BSA_ENOSPC, "kmeans: workspace %zu bytes < %zu", ws_bytes, need);
   return hip_status(bsa::launch_kmeans(static_cast<const uint16_t*>(x), B * H, N, d, n_valid, C, iters, uniforms,
-                                       centroids, assign, sizes, ws, stream),
+                                       centroids, assign, sizes, nullptr, 0, ws, stream),
                     "kmeans");
+}
+
+int bsa_kmeans_warm(const void* x, int B, int H, int N, int d, int n_valid, int C, int max_iters, int tol_moves,
+                    float* centroids, int32_t* assign, int32_t* sizes, int32_t* changes, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (C < 1 || C > 1024) return fail(BSA_EUNSUPPORTED, "kmeans_warm: C must be in [1, 1024] (got %d)", C);
+  if (C > n_valid) return fail(BSA_EINVAL, "kmeans_warm: C=%d exceeds n_valid=%d", C, n_valid);
+  if (max_iters < 1) return fail(BSA_EINVAL, "kmeans_warm: max_iters must be >= 1");
+  if (tol_moves < 0) return fail(BSA_EINVAL, "kmeans_warm: tol_moves must be >= 0");
+  if (!x || !centroids || !assign || !sizes || !changes) return fail(BSA_EINVAL, "kmeans_warm: null pointer");
+  if (!aligned16(x)) return fail(BSA_EINVAL, "kmeans_warm: x must be 16-byte aligned");
+  const size_t need = bsa_kmeans_workspace(B, H, N, C, d);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(BSA_ENOSPC, "kmeans_warm: workspace %zu bytes < %zu", ws_bytes, need);
+  return hip_status(bsa::launch_kmeans(static_cast<const uint16_t*>(x), B * H, N, d, n_valid, C, max_iters,
+                                       nullptr, centroids, assign, sizes, changes, tol_moves, ws, stream),
+                    "kmeans_warm");
 }
 
 size_t bsa_cluster_order_workspace(int B, int H, int N, int C) {

@@ -134,7 +134,7 @@ hipError_t launch_permute(const uint16_t* x, uint16_t* y, const int32_t* perm, i
                           int d, int per_head, bool inverse, hipStream_t s);
 hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,
                          const float* uniforms, float* centroids, int32_t* assign,
-                         int32_t* sizes, void* ws, hipStream_t s);
+                         int32_t* sizes, int32_t* changes, int tol, void* ws, hipStream_t s);
 size_t kmeans_ws_bytes(int BH, int N, int C, int d);
 hipError_t launch_cluster_order(const int32_t* assign, int BH, int N, int n_valid, int C,
                                 int32_t* perm, int32_t* start, int32_t* len, void* ws,

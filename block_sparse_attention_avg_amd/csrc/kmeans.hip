@@ -9,6 +9,15 @@
 // in the same fixed order (no atomics, no grid barrier), the first workgroup
 // records the centre, and all update D^2 against it.
 //
+// Warm start (Sparse VideoGen2 summary, Metodologia C.1: the previous
+// denoising step's centroids initialise k-means): seeding is skipped and the
+// Lloyd rounds start from the caller's centroids. Each round counts the tokens
+// whose assignment changed (per head, integer atomics, so exact); after the
+// first round that moves at most `tol` tokens, every kernel of the later
+// rounds of that head returns at once. With tol = 0 that round moved nothing,
+// the clustering is a fixed point and the result is bit-identical to running
+// the remaining rounds.
+//
 // Lloyd rounds: assignment computes exact fp32 squared distances (centroids
 // are wave-uniform, so they are read through scalar loads); the update is a
 // stable counting sort by cluster (per-chunk histograms, a per-head scan, an
@@ -32,6 +41,16 @@ struct KmWs {
   int32_t* order;   // [BH][N]   tokens sorted by cluster
   int32_t* start;   // [BH][C]
   int32_t* size;    // [BH][C]
+};
+
+// Early exit of a warm-start round: head bh has stopped when the previous
+// round moved at most `tol` tokens (changes[bh][it-1] <= tol).
+struct Stop {
+  const int32_t* changes;   // null (cold start), or [BH][iters]
+  int it, iters, tol;
+  __device__ __forceinline__ bool operator()(int bh) const {
+    return changes && it >= 1 && changes[(size_t)bh * iters + it - 1] <= tol;
+  }
 };
 
 __device__ __forceinline__ float load_x(const uint16_t* row, int dd) {
@@ -136,8 +155,10 @@ __global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restri
 template <int D>
 __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict__ x, int N, int n,
                                                      int C, const float* __restrict__ cent,
-                                                     int32_t* __restrict__ assign) {
+                                                     int32_t* __restrict__ assign, Stop stop,
+                                                     int32_t* __restrict__ changes) {
   const int bh = blockIdx.y;
+  if (stop(bh)) return;
   const int i = blockIdx.x * kChunk + threadIdx.x;
   if (i >= N) return;
   if (i >= n) {
@@ -170,14 +191,25 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
       bi = c;
     }
   }
+  // rounds after the first count the tokens that moved
+  if (changes && stop.it >= 1 && assign[(size_t)bh * N + i] != bi)
+    atomicAdd(&changes[(size_t)bh * stop.iters + stop.it], 1);
   assign[(size_t)bh * N + i] = bi;
+}
+
+// changes[bh][0] = n (no earlier round to compare with), the rest 0.
+__global__ __launch_bounds__(256) void changes_init_kernel(int32_t* __restrict__ changes, size_t total, int iters,
+                                                           int n) {
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (size_t)gridDim.x * 256)
+    changes[u] = u % (size_t)iters == 0 ? n : 0;
 }
 
 // Per-chunk cluster histogram: cnt[bh][chunk][c].
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ assign, int N, int n,
-                                                   int C, int32_t* __restrict__ cnt) {
+                                                   int C, int32_t* __restrict__ cnt, Stop stop) {
   extern __shared__ int h[];
   const int bh = blockIdx.y, ch = blockIdx.x, nchunk = gridDim.x;
+  if (stop(bh)) return;
   for (int c = threadIdx.x; c < C; c += 256) h[c] = 0;
   __syncthreads();
   const int i = ch * kChunk + threadIdx.x;
@@ -191,9 +223,10 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ a
 // starts; off[bh][chunk][c] becomes the first output slot of chunk's members.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ off, int nchunk, int C,
                                                     int32_t* __restrict__ start,
-                                                    int32_t* __restrict__ size) {
+                                                    int32_t* __restrict__ size, Stop stop) {
   __shared__ int sz[1024];
   const int bh = blockIdx.x;
+  if (stop(bh)) return;
   const int c = threadIdx.x;
   int32_t* o = off + (size_t)bh * nchunk * C;
   int run = 0;
@@ -228,9 +261,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ off, i
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ assign, int N,
                                                       int n, int C,
                                                       const int32_t* __restrict__ off,
-                                                      int32_t* __restrict__ order) {
+                                                      int32_t* __restrict__ order, Stop stop) {
   __shared__ int ids[kChunk];
   const int bh = blockIdx.y, ch = blockIdx.x, nchunk = gridDim.x;
+  if (stop(bh)) return;
   const int i = ch * kChunk + threadIdx.x;
   ids[threadIdx.x] = i < n ? assign[(size_t)bh * N + i] : -1;
   __syncthreads();
@@ -252,10 +286,11 @@ __global__ __launch_bounds__(256) void mean_kernel(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ order,
                                                    const int32_t* __restrict__ start,
                                                    const int32_t* __restrict__ size,
-                                                   float* __restrict__ cent) {
+                                                   float* __restrict__ cent, Stop stop) {
   constexpr int G = 256 / D;   // token groups
   __shared__ float red[G][D];
   const int bh = blockIdx.y, c = blockIdx.x;
+  if (stop(bh)) return;
   const int sz = size[(size_t)bh * C + c];
   if (sz == 0) return;   // empty cluster keeps its centroid
   const int st = start[(size_t)bh * C + c];
@@ -312,31 +347,42 @@ size_t cluster_order_ws_bytes(int BH, int N, int C) {
 }
 
 static hipError_t sort_by_cluster(const int32_t* assign, int BH, int N, int n, int C, int32_t* off,
-                                  int32_t* order, int32_t* start, int32_t* size, hipStream_t s) {
+                                  int32_t* order, int32_t* start, int32_t* size, hipStream_t s,
+                                  Stop stop = Stop{nullptr, 0, 0, 0}) {
   const int nchunk = (N + kChunk - 1) / kChunk;
-  hist_kernel<<<dim3(nchunk, BH), 256, C * sizeof(int), s>>>(assign, N, n, C, off);
-  scan_kernel<<<BH, 1024, 0, s>>>(off, nchunk, C, start, size);
-  scatter_kernel<<<dim3(nchunk, BH), 256, 0, s>>>(assign, N, n, C, off, order);
+  hist_kernel<<<dim3(nchunk, BH), 256, C * sizeof(int), s>>>(assign, N, n, C, off, stop);
+  scan_kernel<<<BH, 1024, 0, s>>>(off, nchunk, C, start, size, stop);
+  scatter_kernel<<<dim3(nchunk, BH), 256, 0, s>>>(assign, N, n, C, off, order, stop);
   return hipGetLastError();
 }
 
+// uni != null: k-means++ seeding into cent first (cold start); otherwise cent
+// holds the initial centroids and changes ([BH][iters], iters >= 1) receives
+// the per-round move counts (warm start with early exit).
 template <int D>
 static hipError_t kmeans_t(const uint16_t* x, int BH, int N, int n, int C, int iters,
                            const float* uni, float* cent, int32_t* assign, int32_t* sizes,
-                           void* wsp, hipStream_t s) {
+                           int32_t* changes, int tol, void* wsp, hipStream_t s) {
   KmWs ws = carve(wsp, BH, N, C);
   const int nchunk_n = (n + kChunk - 1) / kChunk;
-  for (int r = 0; r < C; ++r)
-    kpp_round_kernel<D><<<dim3(nchunk_n, BH), 256, 0, s>>>(x, N, n, C, r, uni, cent, ws, BH);
+  if (uni)
+    for (int r = 0; r < C; ++r)
+      kpp_round_kernel<D><<<dim3(nchunk_n, BH), 256, 0, s>>>(x, N, n, C, r, uni, cent, ws, BH);
+  if (changes && iters > 0) {
+    const size_t total = (size_t)BH * iters;
+    changes_init_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(changes, total, iters, n);
+  }
   const int nchunk = (N + kChunk - 1) / kChunk;
   for (int it = 0; it < iters; ++it) {
-    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign);
-    hipError_t e = sort_by_cluster(assign, BH, N, n, C, ws.off, ws.order, ws.start, ws.size, s);
+    const Stop stop{changes, it, iters, tol};
+    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign, stop, changes);
+    hipError_t e = sort_by_cluster(assign, BH, N, n, C, ws.off, ws.order, ws.start, ws.size, s, stop);
     if (e != hipSuccess) return e;
-    mean_kernel<D><<<dim3(C, BH), 256, 0, s>>>(x, N, C, ws.order, ws.start, ws.size, cent);
+    mean_kernel<D><<<dim3(C, BH), 256, 0, s>>>(x, N, C, ws.order, ws.start, ws.size, cent, stop);
   }
   if (iters == 0) {
-    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign);
+    const Stop none{nullptr, 0, 0, 0};
+    assign_kernel<D><<<dim3(nchunk, BH), 256, 0, s>>>(x, N, n, C, cent, assign, none, nullptr);
     hipError_t e = sort_by_cluster(assign, BH, N, n, C, ws.off, ws.order, ws.start, ws.size, s);
     if (e != hipSuccess) return e;
   }
@@ -348,10 +394,11 @@ static hipError_t kmeans_t(const uint16_t* x, int BH, int N, int n, int C, int i
 
 hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,
                          const float* uniforms, float* centroids, int32_t* assign,
-                         int32_t* sizes, void* ws, hipStream_t s) {
+                         int32_t* sizes, int32_t* changes, int tol, void* ws, hipStream_t s) {
   if (BH == 0) return hipSuccess;
-  if (d == 128) return kmeans_t<128>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, ws, s);
-  return kmeans_t<64>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, ws, s);
+  if (d == 128)
+    return kmeans_t<128>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, changes, tol, ws, s);
+  return kmeans_t<64>(x, BH, N, n_valid, C, iters, uniforms, centroids, assign, sizes, changes, tol, ws, s);
 }
 
 hipError_t launch_cluster_order(const int32_t* assign, int BH, int N, int n_valid, int C,

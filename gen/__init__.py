@@ -5,4 +5,4 @@ method lives here.
 """
 
 from .configs import BY_INDEX, WORKLOADS, Workload  # noqa: F401
-from .fourier import generate, generate_head, kmeans_uniforms, token_coords  # noqa: F401
+from .fourier import generate, generate_head, kmeans_uniforms, next_step, token_coords  # noqa: F401

@@ -115,3 +115,20 @@ def kmeans_uniforms(B: int, H: int, C: int, seed: int = 0, stream: int = 0) -> n
     ss = np.random.SeedSequence([seed, 0x6B6D, stream])
     u = np.random.default_rng(ss).random((B, H, C), dtype=np.float32)
     return u
+
+
+def next_step(x: torch.Tensor, step: int, drift: float = 0.05, seed: int = 0, stream: int = 0) -> torch.Tensor:
+    """Stand-in for the same activation ``step`` denoising steps later.
+
+    Activations of a video DiT change slowly from one denoising step to the
+    next; this adds independent Gaussian noise of standard deviation
+    ``drift`` times the tensor's RMS to every element (bf16 [B, H, N, d] in,
+    same out), seeded by (seed, step, stream). All-zero rows (padding) stay
+    zero.
+    """
+    xf = x.float()
+    rms = float(xf.pow(2).mean().sqrt())
+    ss = np.random.SeedSequence([seed, 0x5354, step, stream])
+    eta = torch.from_numpy(np.random.default_rng(ss).standard_normal(tuple(x.shape), dtype=np.float32))
+    live = (xf != 0).any(-1, keepdim=True)
+    return torch.where(live, xf + drift * rms * eta, xf).to(x.dtype)

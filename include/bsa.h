@@ -370,6 +370,30 @@ int bsa_kmeans(const void* x, int B, int H, int N, int d, int n_valid, int C,
                int32_t* assign, int32_t* sizes, void* ws, size_t ws_bytes,
                hipStream_t stream);
 
+/*
+ * Warm-started k-means (Sparse VideoGen2 summary, Metodologia C.1 "Cache dei
+ * Centroidi": the centroids of the previous denoising step initialise the
+ * clustering of the next one). No seeding: up to max_iters rounds of the
+ * Lloyd step of bsa_kmeans (same assignment and update rules) start from the
+ * given centroids. A head stops after the first round that moves at most
+ * tol_moves tokens (that round's update included): its later rounds do
+ * nothing on the GPU. With tol_moves = 0 that round moved nothing, the
+ * clustering is a fixed point and the result equals running every round.
+ *   x          bf16 [B,H,N,d] (device), d in {64, 128}
+ *   centroids  fp32 [B,H,C,d] in: initial centroids; out: final
+ *   assign     int32 [B,H,N] out (-1 for padding rows); sizes int32 [B,H,C] out
+ *   changes    int32 [B,H,max_iters] out: tokens whose assignment changed in
+ *              each round (round 0 counts all n_valid tokens; 0 after the
+ *              stopping round)
+ *   ws         bsa_kmeans_workspace(...) bytes (device)
+ *   1 <= C <= 1024, C <= n_valid, max_iters >= 1, tol_moves >= 0
+ */
+int bsa_kmeans_warm(const void* x, int B, int H, int N, int d, int n_valid,
+                    int C, int max_iters, int tol_moves, float* centroids,
+                    int32_t* assign,
+                    int32_t* sizes, int32_t* changes, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by bsa_cluster_order. */
 size_t bsa_cluster_order_workspace(int B, int H, int N, int C);
 

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import block_sparse_attention_avg_amd.pipelines as pl
-from gen import WORKLOADS, generate, kmeans_uniforms, token_coords
+from gen import WORKLOADS, generate, kmeans_uniforms, next_step, token_coords
 from oracle import attention as oa
 from oracle import kmeans as ok
 from oracle import layout as ol
@@ -243,6 +243,76 @@ def test_kmeans_lloyd_invariants(gpu_lib, which):
                 np.testing.assert_allclose(c10[0, h, c], ref, rtol=1e-5, atol=1e-4 * np.abs(ref).max())
         say(f"  head {h}: sizes min {s10[0, h].min()} max {s10[0, h].max()}, "
             f"inertia {((xh - c10[0, h][ah]) ** 2).sum():.6e}")
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_kmeans_warm_start(gpu_lib, which):
+    # centroids of one step start the clustering of the next (a drifted copy)
+    bsa = gpu_lib
+    w, q, k, v, uq, uk = _semantic()
+    x, C, u = (q, w.Cq, uq) if which == "q" else (k, w.Ck, uk)
+    x1 = next_step(x, 1, stream=0 if which == "q" else 1)
+    say(f"k-means warm start on {which}, C={C}")
+    xd, x1d, ud = x.cuda(), x1.cuda(), u.cuda()
+    c0, _, _ = bsa.kmeans(xd, C, w.kmeans_iters, ud, n_valid=w.n_valid)
+    cw, aw, sw, ch = bsa.kmeans_warm(x1d, c0, 40, n_valid=w.n_valid)
+    cw2, aw2, sw2, ch2 = bsa.kmeans_warm(x1d, c0, 40, n_valid=w.n_valid)
+    assert torch.equal(cw, cw2) and torch.equal(aw, aw2) and torch.equal(ch, ch2), "deterministic"
+    ch = ch.cpu().numpy()
+    assert (ch[..., 0] == w.n_valid).all()
+    # once a round moves nothing, every later entry is 0
+    for row in ch.reshape(-1, 40):
+        z = np.nonzero(row == 0)[0]
+        if len(z):
+            assert (row[z[0]:] == 0).all()
+    say(f"  moves per round, head 0: {ch[0, 0].tolist()}")
+    # move counts: the assignments after t and t + 1 rounds differ in ch[t+1] tokens
+    for t in (1, 2):
+        _, a_t, _, _ = bsa.kmeans_warm(x1d, c0, t, n_valid=w.n_valid)
+        _, a_t1, _, c_t1 = bsa.kmeans_warm(x1d, c0, t + 1, n_valid=w.n_valid)
+        diff = (a_t != a_t1).sum(-1).cpu().numpy()
+        assert np.array_equal(diff, c_t1.cpu().numpy()[..., t]), t
+    # early exit is exact: a cold run of r rounds equals a warm start from its
+    # seeds (which stops as soon as nothing moves), for r past convergence too
+    seeds, _, _ = bsa.kmeans(xd, C, 0, ud, n_valid=w.n_valid)
+    for r in (3, 25):
+        cc, ac, sc = bsa.kmeans(xd, C, r, ud, n_valid=w.n_valid)
+        cs, as_, ss, _ = bsa.kmeans_warm(xd, seeds, r, n_valid=w.n_valid)
+        assert torch.equal(cc, cs) and torch.equal(ac, as_) and torch.equal(sc, ss), r
+    # a move tolerance: each head stops after its first round with at most tol
+    # moves, with the result of running exactly that many rounds
+    tol = int(ch[0, :, 4].max())                 # every head gets there by round 4
+    ct, at, _, cht = bsa.kmeans_warm(x1d, c0, 40, n_valid=w.n_valid, tol_moves=tol)
+    cht = cht.cpu().numpy()[0]
+    for h in (0, 5):
+        row = cht[h]
+        t_h = int(np.argmax(row <= tol))
+        assert row[t_h] <= tol and (row[:t_h] > tol).all() and (row[t_h + 1:] == 0).all()
+        cr, ar, _, _ = bsa.kmeans_warm(x1d, c0, t_h + 1, n_valid=w.n_valid)
+        assert torch.equal(ct[0, h], cr[0, h]) and torch.equal(at[0, h], ar[0, h]), h
+        say(f"  head {h}: tolerance {tol} moves reached after {t_h + 1} rounds")
+    # round 0 against the oracle's assignment rule, from the same fp32 centroids
+    c0n = c0.cpu().numpy().astype(np.float64)
+    _, a1, _, _ = bsa.kmeans_warm(x1d, c0, 1, n_valid=w.n_valid)
+    a1 = a1.cpu().numpy()
+    cwn, aw_n, sw_n = cw.cpu().numpy().astype(np.float64), aw.cpu().numpy(), sw.cpu().numpy()
+    for h in (0, 6):
+        xh = _np(x1[0, h])[:w.n_valid]
+        D = _d2(xh, c0n[0, h])
+        ref = ok.assign(xh, c0n[0, h])
+        mine = a1[0, h, :w.n_valid]
+        gap = D[np.arange(len(mine)), mine] - D[np.arange(len(ref)), ref]
+        bad = (mine != ref) & (gap > 2e-5 * D.min(1) + 1e-3)
+        say(f"  head {h}: round-0 assignments differing from the oracle {(mine != ref).sum()}, "
+            f"beyond fp32 ties {bad.sum()}")
+        assert not bad.any()
+        # the final centroids are the means of their members
+        ah = aw_n[0, h, :w.n_valid]
+        assert np.array_equal(np.bincount(ah, minlength=C), sw_n[0, h])
+        for c in range(C):
+            if sw_n[0, h, c]:
+                r_ = xh[ah == c].mean(0)
+                np.testing.assert_allclose(cwn[0, h, c], r_, rtol=1e-5, atol=1e-4 * np.abs(r_).max())
 
 
 def test_semantic_path(gpu_lib):
