@@ -349,6 +349,47 @@ def paths_bench(r: Runner, steps: int = 10, warmup: int = 3):
         S["cq1"] = bsa.kmeans_warm(q1, sq0, cap, ws.n_valid, tol)
         S["ck1"] = bsa.kmeans_warm(k1, sk0, cap, ws.n_valid, tol)
     tc = run([("kmeans_qk_cold", cold)])
+    # reuse of the raster mask across that step: the lists built at step 0
+    # applied at step 1, against the lists built at step 1
+    v1 = next_step(r.v_cpu, 1, stream=2).to(dev)
+    c0m, i0m = bsa.build_block_mask(q, k, w.thr, n_valid=w.n_valid)
+    c1m, i1m = bsa.build_block_mask(q1, k1, w.thr, n_valid=w.n_valid)
+    nb = c0m.shape[-1]
+
+    def dense(c, i):
+        # entries past each row's count go to a spare last column
+        m = torch.zeros((*c.shape, nb + 1), dtype=torch.bool, device=dev)
+        valid = torch.arange(i.shape[-1], device=dev) < c[..., None].long()
+        m.scatter_(3, torch.where(valid, i.long(), nb), True)
+        return m[..., :nb]
+    m0, m1 = dense(c0m, i0m), dense(c1m, i1m)
+    o_re = bsa.block_sparse_attn_fwd(q1, k1, v1, c0m, i0m, n_valid=w.n_valid).float()
+    o_fr = bsa.block_sparse_attn_fwd(q1, k1, v1, c1m, i1m, n_valid=w.n_valid).float()
+    dlt = (o_re - o_fr).abs()
+    out["mask_reuse_next_step"] = {
+        "what": "raster CDF mask of step 0 reused at the next step (5 % RMS drift of Q, K, V) vs the mask "
+                "rebuilt there: kept-tile overlap and the attention output difference",
+        "kept_step0": int(m0.sum()), "kept_step1": int(m1.sum()),
+        "jaccard": round(float((m0 & m1).sum()) / float((m0 | m1).sum()), 4),
+        "out_max_abs_diff": round(float(dlt.max()), 4), "out_mean_abs_diff": round(float(dlt.mean()), 5),
+        "out_rms": round(float(o_fr.pow(2).mean().sqrt()), 4),
+    }
+    # mask quality of this step's raster mask against the full attention
+    import block_sparse_attention_avg_amd.pipelines as pl2
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    mq = pl2.mask_quality(q, k, c0m, i0m, n_valid=w.n_valid)
+    ev[1].record()
+    torch.cuda.synchronize()
+    out["mask_quality"] = {
+        "what": "CDF mask of the 480p layer against the full attention's tile map (two passes: full forward "
+                "with row normalisers, then max/sum/min per 64x64 tile): recall of the equal-budget max-pooled "
+                "oracle mask and share of the attention mass kept, means over query blocks",
+        "oracle_recall": round(float(mq.oracle_recall.mean()), 4),
+        "mass_recall": round(float(mq.mass_recall.mean()), 4),
+        "mass_recall_p10": round(float(torch.quantile(mq.mass_recall.flatten(), 0.1)), 4),
+        "ms": round(ev[0].elapsed_time(ev[1]), 3),
+    }
     out["semantic_next_step"] = {
         "what": "k-means of Q and K at the next denoising step (inputs drifted by 5 % RMS noise): warm start "
                 "from the previous step's centroids vs k-means++ seeding + Lloyd rounds, both run until a "

@@ -61,6 +61,8 @@ _SIGS = {
     "bsa_tile_order": ([_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_I)], _I),
     "bsa_kmeans_workspace": ([_I, _I, _I, _I, _I], _Z),
     "bsa_kmeans": ([_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "bsa_attention_tile_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P], _I),
+    "bsa_mask_recall": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "bsa_kmeans_warm": ([_P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
     "bsa_cluster_order_workspace": ([_I, _I, _I, _I], _Z),
     "bsa_cluster_order": ([_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
@@ -354,6 +356,38 @@ def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
                                          dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                          _stream(q.device)), "block_sparse_attn_bwd")
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------ diagnostic
+
+def attention_tile_stats(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, n_valid: Optional[int] = None,
+                         scale: float = 0.0):
+    """Max, sum and min of the full attention per 64 x 64 tile: three fp32
+    [B,H,nb,nb] tensors. ``lse`` [B,H,N] holds the full rows' normalisers."""
+    B, H, N, d = _qkv(q, "q")
+    n_valid = N if n_valid is None else n_valid
+    _dev_tensor(lse, torch.float32, "lse")
+    nb = -(-n_valid // 64)
+    out = [torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device) for _ in range(3)]
+    _check(load().bsa_attention_tile_stats(q.data_ptr(), k.data_ptr(), lse.data_ptr(), B, H, N, d, n_valid, scale,
+                                           out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                           _stream(q.device)), "attention_tile_stats")
+    return tuple(out)
+
+
+def mask_recall(tile_max: torch.Tensor, tile_sum: torch.Tensor, kv_count: torch.Tensor, kv_index: torch.Tensor):
+    """Per query block: (oracle recall, mass recall) fp32 [B,H,nqb] each."""
+    _dev_tensor(tile_max, torch.float32, "tile_max")
+    _dev_tensor(tile_sum, torch.float32, "tile_sum")
+    _dev_tensor(kv_count, torch.int32, "kv_count")
+    _dev_tensor(kv_index, torch.int32, "kv_index")
+    B, H, nqb, nkb = tile_max.shape
+    rec = torch.empty((B, H, nqb), dtype=torch.float32, device=tile_max.device)
+    mass = torch.empty_like(rec)
+    _check(load().bsa_mask_recall(tile_max.data_ptr(), tile_sum.data_ptr(), kv_count.data_ptr(), kv_index.data_ptr(),
+                                  kv_index.shape[-1], B, H, nqb, nkb, rec.data_ptr(), mass.data_ptr(),
+                                  _stream(tile_max.device)), "mask_recall")
+    return rec, mass
 
 
 # ------------------------------------------------------------------ reorder

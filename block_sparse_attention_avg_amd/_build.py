@@ -22,7 +22,7 @@ PROBE = os.path.join(PKG, "mfma_probe")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_fwd_1w.hip", "attn_bwd.hip",
-           "permute.hip", "kmeans.hip"]
+           "diag.hip", "permute.hip", "kmeans.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -338,6 +338,34 @@ int bsa_fractal_order(int T, int Hl, int Wl, int P, int N, int32_t* perm, int32_
   return bsa_tile_order(T, Hl, Wl, 1, P, P, N, perm, blk_start, blk_len, blk_coords, max_blocks, nblocks);
 }
 
+int bsa_attention_tile_stats(const void* q, const void* k, const float* lse, int B, int H, int N, int d,
+                             int n_valid, float scale, float* tile_max, float* tile_sum, float* tile_min,
+                             hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "tile_stats: d must be 64 or 128");
+  if (!q || !k || !lse || !tile_max || !tile_sum || !tile_min) return fail(BSA_EINVAL, "tile_stats: null pointer");
+  if (!aligned16(q) || !aligned16(k)) return fail(BSA_EINVAL, "tile_stats: q, k must be 16-byte aligned");
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return hip_status(bsa::launch_tile_stats(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse,
+                                           B * H, N, d, n_valid, sc, tile_max, tile_sum, tile_min, stream),
+                    "tile_stats");
+}
+
+int bsa_mask_recall(const float* tile_max, const float* tile_sum, const int32_t* kv_count, const int32_t* kv_index,
+                    int kv_stride, int B, int H, int nqb, int nkb, float* oracle_recall, float* mass_recall,
+                    hipStream_t stream) {
+  g_msg[0] = 0;
+  if (B <= 0 || H <= 0 || nqb < 0 || nkb <= 0) return fail(BSA_EINVAL, "mask_recall: bad sizes");
+  if (nkb > 8192) return fail(BSA_EUNSUPPORTED, "mask_recall: at most 8192 key blocks (got %d)", nkb);
+  if (kv_stride < 1) return fail(BSA_EINVAL, "mask_recall: kv_stride must be >= 1");
+  if (!tile_max || !tile_sum || !kv_count || !kv_index || !oracle_recall || !mass_recall)
+    return fail(BSA_EINVAL, "mask_recall: null pointer");
+  return hip_status(bsa::launch_mask_recall(tile_max, tile_sum, kv_count, kv_index, kv_stride,
+                                            (size_t)B * H * nqb, nkb, oracle_recall, mass_recall, stream),
+                    "mask_recall");
+}
+
 size_t bsa_kmeans_workspace(int B, int H, int N, int C, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || C <= 0) return 0;
   return bsa::kmeans_ws_bytes(B * H, N, C, d);

@@ -132,6 +132,11 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
 size_t attn_bwd_workspace(int BH, int N, int nb);
 hipError_t launch_permute(const uint16_t* x, uint16_t* y, const int32_t* perm, int BH, int N,
                           int d, int per_head, bool inverse, hipStream_t s);
+hipError_t launch_tile_stats(const uint16_t* q, const uint16_t* k, const float* lse, int BH, int N, int d,
+                             int n_valid, float scale, float* tmax, float* tsum, float* tmin, hipStream_t s);
+hipError_t launch_mask_recall(const float* tmax, const float* tsum, const int32_t* kv_count,
+                              const int32_t* kv_index, int kv_stride, size_t rows, int nkb, float* oracle_recall,
+                              float* mass_recall, hipStream_t s);
 hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,
                          const float* uniforms, float* centroids, int32_t* assign,
                          int32_t* sizes, int32_t* changes, int tol, void* ws, hipStream_t s);

@@ -1,0 +1,152 @@
+// MFMA tile helpers shared by the attention-gradient and tile-statistics
+// kernels: 64-row bf16 tiles staged in LDS by direct-to-LDS buffer loads with
+// XOR-swizzled 16-byte pieces, the row operand read, the transposed operand
+// read (LDS transpose read, rows in the order of the 32 x 32 accumulator
+// layout), and the accumulator-to-rows store.
+#pragma once
+
+#include "attn.h"
+
+namespace bsa {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(4))) const int32_t cint;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Swizzle of the 16-byte piece index inside a tile row (as in the forward).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  else return (r >> 1) & 7;
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
+// Tile geometry shared by the two gradient kernels: 64 rows of D bf16,
+// row-major in LDS with swizzled 16-byte pieces; wave w of 2 loads rows
+// 32w .. 32w+31.
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int NI = BYTES / 1024 / 2;      // direct-to-LDS loads per wave
+  static constexpr int RPI = 1024 / ROWB;          // rows per load
+  static constexpr int PPR = ROWB / 16;            // 16-byte pieces per row
+};
+
+// Lane offsets of a wave's share of a 64-row tile load.
+template <int D>
+__device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int r = (wave * T::NI + i) * T::RPI + lane / T::PPR;
+    off[i] = r * T::ROWB + (((lane % T::PPR) ^ swz<D>(r & 15)) << 4);
+  }
+}
+// Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros.
+template <int D>
+__device__ __forceinline__ void tile_load(const uint16_t* head, int r0, int n, lds_u8* dst, int wave,
+                                          const uint32_t* off) {
+  using T = Tile<D>;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)max(n, 0) * T::ROWB);
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) dma16(rs, dst + (wave * T::NI + i) * 1024, off[i]);
+}
+// Row operand: lane supplies row (32 g + l32), channels 16 c + 8 half .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_read(const lds_u8* t, int g, int c, int l32, int half) {
+  const int off = (32 * g + l32) * Tile<D>::ROWB + (((2 * c + half) ^ swz<D>(l32 & 15)) << 4);
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off);
+}
+// Transposed operand through the LDS transpose read: lane receives channel
+// 32 dg + l32 of rows 32 g + 16 hh + (8 t + 4 half + 0..3, t = 0, 1): the row
+// order of the accumulator layout (see the forward).
+template <int D>
+struct TrOffsets {
+  int voff[D / 32][2];
+  __device__ __forceinline__ TrOffsets(int lane) {
+    const int half = lane >> 5, g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 8 * t + 4 * half + sj;
+        const int piece = 4 * dg + 2 * g16 + (sq >> 1);
+        voff[dg][t] = row * Tile<D>::ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
+      }
+  }
+};
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(const lds_u8* t, const TrOffsets<D>& o, int g, int hh, int dg) {
+  const lds_u8* b = t + (32 * g + 16 * hh) * Tile<D>::ROWB;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][0]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator element r of a 32 x 32 tile: row 8 (r / 4) + 4 half + (r & 3).
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// 64 x D accumulator tile (transposed: channels x rows, 32 rows per wave) ->
+// bf16 rows [r0, r0 + n) of `out`, staged through `stage` (a free tile).
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16* acc, float mul, lds_u8* stage, uint16_t* out, int r0,
+                                           int n, int wave, int lane) {
+  using T = Tile<D>;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int orow = 32 * wave + l32;
+  const int fo = swz<D>(orow & 15);
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const u32x2 w = {pack2(acc[dg][4 * j4 + 0] * mul, acc[dg][4 * j4 + 1] * mul),
+                       pack2(acc[dg][4 * j4 + 2] * mul, acc[dg][4 * j4 + 3] * mul)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + orow * T::ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
+    }
+  wg_barrier();
+#pragma unroll
+  for (int r = 0; r < T::BYTES / 16 / 128; ++r) {
+    const int u = threadIdx.x + 128 * r;
+    const int row = u / T::PPR, p = u % T::PPR;
+    if (row < n)
+      *reinterpret_cast<u32x4*>(out + (size_t)(r0 + row) * D + p * 8) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              stage + row * T::ROWB + ((p ^ swz<D>(row & 15)) << 4));
+  }
+}
+
+}  // namespace
+}  // namespace bsa

@@ -10,6 +10,12 @@ own p_t x p_h x p_w factorisation of the tile, so each head gets its own token
 order and its own box blocks; the CDF mask and the attention then run over
 each head's boxes and the output returns to raster order.
 
+``mask_quality`` -- Veda summary, sections 2.1 and 3: the full attention is
+max-pooled (and summed, min-pooled) over every 64 x 64 tile in two passes
+(row normalisers from the forward with every block kept, then the tile map),
+and a block mask is scored by its recall against the max-pooled oracle mask
+of the same budget and by the attention mass it keeps.
+
 ``semantic_attention`` -- Sparse VideoGen2 summary, Metodologia A-C: Q and K
 are clustered with k-means, tokens are permuted cluster-contiguously, the
 centroid top-p rule selects key clusters per query cluster, attention runs
@@ -26,8 +32,9 @@ from typing import Optional, Tuple
 
 import torch
 
-from . import (Blocks, block_sparse_attn_fwd, build_block_mask, build_centroid_mask,
-               cluster_order, fractal_order, kmeans, permute_tokens, tile_order, unpermute_tokens)
+from . import (Blocks, attention_tile_stats, block_sparse_attn_fwd, block_sparse_attn_fwd_lse,
+               build_block_mask, build_centroid_mask, cluster_order, fractal_order, kmeans, mask_recall,
+               permute_tokens, tile_order, unpermute_tokens)
 
 
 @dataclasses.dataclass
@@ -99,6 +106,29 @@ def head_tiled_attention(q, k, v, layout: HeadTiling, thr: float, n_valid: Optio
     op = block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=n_valid, qb=layout.blocks, kb=layout.blocks)
     o = unpermute_tokens(op, layout.perm)
     return (o, cnt, idx) if return_mask else o
+
+
+@dataclasses.dataclass
+class MaskQuality:
+    """Full-attention tile map and the recall of one mask against it (device)."""
+    tile_max: torch.Tensor       # fp32 [B,H,nb,nb]
+    tile_sum: torch.Tensor
+    tile_min: torch.Tensor
+    oracle_recall: torch.Tensor  # fp32 [B,H,nb]
+    mass_recall: torch.Tensor
+
+
+def mask_quality(q, k, kv_count, kv_index, n_valid: Optional[int] = None) -> MaskQuality:
+    """Two passes over the full attention of (q, k), then the mask's recall."""
+    B, H, N, _ = q.shape
+    n_valid = N if n_valid is None else n_valid
+    nb = -(-n_valid // 64)
+    full_c = torch.full((B, H, nb), nb, dtype=torch.int32, device=q.device)
+    full_i = torch.arange(nb, dtype=torch.int32, device=q.device).expand(B, H, nb, nb).contiguous()
+    _, lse = block_sparse_attn_fwd_lse(q, k, k, full_c, full_i, n_valid=n_valid)   # only lse is used
+    tmax, tsum, tmin = attention_tile_stats(q, k, lse, n_valid)
+    rec, mass = mask_recall(tmax, tsum, kv_count, kv_index)
+    return MaskQuality(tmax, tsum, tmin, rec, mass)
 
 
 @dataclasses.dataclass

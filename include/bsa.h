@@ -280,6 +280,52 @@ int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Mask-quality diagnostic
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Tile statistics of the full attention (Veda summary, section 2.1: the
+ * reference tile mask max-pools the full attention matrix over every
+ * query-tile x key-tile region; a tile is described by the mean, maximum and
+ * minimum of its values). Second of two passes: lse must hold the natural-log
+ * normaliser of every full attention row (bsa_block_sparse_attn_fwd_lse with
+ * every block kept). For uniform 64-token blocks, per tile (I, J):
+ *   tile_max = max, tile_sum = sum, tile_min = min of
+ *   P_ij = exp(scale q_i . k_j - lse_i) over its valid query rows i and keys j.
+ *   q, k     bf16 [B,H,N,d] (device), d in {64, 128}
+ *   lse      fp32 [B,H,N] (device)
+ *   scale    > 0, or 0 for 1/sqrt(d)
+ *   tile_max, tile_sum, tile_min  fp32 [B,H,nb,nb] out, nb = ceil(n_valid/64)
+ * Deterministic (fixed reduction orders).
+ */
+int bsa_attention_tile_stats(const void* q, const void* k, const float* lse,
+                             int B, int H, int N, int d, int n_valid,
+                             float scale, float* tile_max, float* tile_sum,
+                             float* tile_min, hipStream_t stream);
+
+/*
+ * Recall of a block mask against the full attention's tile map (Veda
+ * summary, sections 2.1 and 3: sparse-mask quality is its alignment with the
+ * tile geometry of the full attention). Per query block row with k kept key
+ * blocks (ids in range; others count as not kept):
+ *   oracle_recall = share of the k tiles with the largest tile_max (equal
+ *                   values: lower key-block id first) that the row keeps
+ *                   (0 for a row that keeps nothing);
+ *   mass_recall   = kept tiles' tile_sum / the row's total tile_sum (0 when
+ *                   the total is 0).
+ *   tile_max, tile_sum  fp32 [B,H,nqb,nkb] (device), from
+ *                       bsa_attention_tile_stats
+ *   kv_count, kv_index  the mask lists as in bsa_select_blocks
+ *   oracle_recall, mass_recall  fp32 [B,H,nqb] out
+ *   nkb <= 8192
+ */
+int bsa_mask_recall(const float* tile_max, const float* tile_sum,
+                    const int32_t* kv_count, const int32_t* kv_index,
+                    int kv_stride, int B, int H, int nqb, int nkb,
+                    float* oracle_recall, float* mass_recall,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Token reorder helpers
  * ------------------------------------------------------------------------ */
 
