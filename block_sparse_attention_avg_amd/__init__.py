@@ -29,7 +29,7 @@ class BsaError(RuntimeError):
 
 class _Blocks(ctypes.Structure):
     _fields_ = [("nblocks", ctypes.c_int32), ("per_head", ctypes.c_int32),
-                ("start", ctypes.c_void_p), ("len", ctypes.c_void_p)]
+                ("start", ctypes.c_void_p), ("len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
 
 
 class _Window(ctypes.Structure):
@@ -123,9 +123,11 @@ def _qkv(t: torch.Tensor, name: str):
 
 class Blocks:
     """Block descriptors: int32 device tensors ``start`` and ``length`` of shape
-    [nblocks] (shared by all heads) or [B, H, nblocks] (per head)."""
+    [nblocks] (shared by all heads) or [B, H, nblocks] (per head). ``max_len``
+    (1..64) is a bound on every length the caller vouches for; it lets the
+    attention take each block as one tile (0: any length)."""
 
-    def __init__(self, start: torch.Tensor, length: torch.Tensor):
+    def __init__(self, start: torch.Tensor, length: torch.Tensor, max_len: int = 0):
         if start.shape != length.shape:
             raise ValueError("start and length must have the same shape")
         _dev_tensor(start, torch.int32, "start")
@@ -133,9 +135,11 @@ class Blocks:
         self.start, self.length = start, length
         self.per_head = start.dim() > 1
         self.nblocks = start.shape[-1]
+        self.max_len = int(max_len)
 
     def _c(self):
-        return _Blocks(self.nblocks, 1 if self.per_head else 0, self.start.data_ptr(), self.length.data_ptr())
+        return _Blocks(self.nblocks, 1 if self.per_head else 0, self.start.data_ptr(), self.length.data_ptr(),
+                       self.max_len)
 
 
 def _blocks_ref(b: Optional[Blocks]):

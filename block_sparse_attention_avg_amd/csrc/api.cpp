@@ -41,6 +41,7 @@ int make_blocks(const bsa_blocks* in, int block, int n_valid, const char* what, 
     out.len = nullptr;
     out.nblocks = (n_valid + block - 1) / block;
     out.per_head = 0;
+    out.max_len = 0;
     return BSA_OK;
   }
   if (in->nblocks < 0) return fail(BSA_EINVAL, "%s: nblocks < 0", what);
@@ -50,6 +51,7 @@ int make_blocks(const bsa_blocks* in, int block, int n_valid, const char* what, 
   out.len = in->len;
   out.nblocks = in->nblocks;
   out.per_head = in->per_head ? 1 : 0;
+  out.max_len = in->max_len >= 1 && in->max_len <= 64 ? in->max_len : 0;
   // A non-null descriptor with no blocks is valid (nothing to do).
   if (out.start == nullptr) {
     // keep the device view distinguishable from uniform blocks

@@ -135,7 +135,11 @@ __device__ __forceinline__ float halves_sum(float x) {
 // Loads go through buffer descriptors that end at the chunk's last row:
 // rows past it (a partial last block, gathered rows past the chunk) read as
 // zeros, so no clamping is needed and padding never reaches P V.
-template <int D, bool KVAR>
+// Key blocks: KMODE 0 = uniform 64-token blocks, 1 = descriptor blocks of at
+// most 64 tokens (each one chunk, loaded like a uniform block from its own
+// start), 2 = descriptor blocks of any length (keys gathered row by row into
+// 64-key chunks).
+template <int D, int KMODE>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
                                           lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
   constexpr int ROWB = D * 2;                  // bytes per K/V row
@@ -145,6 +149,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   constexpr int PPR = ROWB / 16;               // 16-byte pieces per row
   constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
   constexpr uint32_t OOB = 0xFFFFFFF0u;        // lane offset past every descriptor: loads zeros
+  constexpr bool KVAR = KMODE == 2;            // gathered keys
+  // A chunk's length doubles as "the chunk exists" (> 0). A kept short block
+  // with no tokens is still a chunk: its length is coded as kEmpty (no rows
+  // loaded, every key masked).
+  constexpr int kEmpty = 1 << 16;
+  auto rows_of = [](int kl) { return KMODE == 1 ? kl & (kEmpty - 1) : kl; };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,7 +183,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // reference row max in log2 units; short blocks start from a finite floor
+  // so that a first chunk with every key masked (an empty block) gives
+  // exp2(-inf) = 0 rather than exp2(-inf + inf)
+  float m_run = KMODE == 1 ? -1e30f : -INFINITY, l_run = 0.f;
 
   const size_t qrow = (size_t)bh * a.nqb + I;
   const int cnt = ((const cint*)a.kv_count)[qrow];
@@ -213,7 +226,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   // (uniform blocks) or tk[r] (gathered); rows >= kl load zeros.
   auto issue_tile = [&](bool isv, int ks, int kl, const int* tk) {
     uint32_t off[NI];
-    const __amdgpu_buffer_rsrc_t rs = KVAR ? desc(isv ? vh : kh, 0, a.N) : desc(isv ? vh : kh, ks, kl);
+    const __amdgpu_buffer_rsrc_t rs = KVAR ? desc(isv ? vh : kh, 0, a.N) : desc(isv ? vh : kh, ks, rows_of(kl));
     if constexpr (KVAR) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -244,8 +257,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     if (c >= cnt) { ks = 0; kl = 0; return; }
     int J = slist[c];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;   // invalid ids stay in bounds
-    ks = J * 64;                       // uniform 64-token key blocks
-    kl = min(64, a.n_valid - ks);
+    if constexpr (KMODE == 1) {
+      a.kb.get(bh, J, ks, kl);         // a short block is one chunk
+      kl = kl > 0 ? min(kl, 64) : kEmpty;
+    } else {
+      ks = J * 64;                     // uniform 64-token key blocks
+      kl = min(64, a.n_valid - ks);
+    }
   };
   // Gathered blocks: wave 0 writes the token indices of chunk c to the ring
   // slot tok[c & 3] with a cursor (list entry e_cur, offset off_cur).
@@ -332,6 +350,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   };
   // keys >= kl of a chunk get -inf
   auto mask_tail = [&](f32x16* s, int kl_s) {
+    kl_s = rows_of(kl_s);
     if (kl_s < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -551,7 +570,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   }
 }
 
-template <int D, bool QVAR, bool KVAR>
+template <int D, bool QVAR, int KMODE>
 __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = 64 * D * 2;
   __shared__ __align__(16) unsigned char Ks[TILE];
@@ -578,7 +597,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   if (!QVAR) {
     if (tile >= a.nqb) return;
     I = a.order ? ((const cint*)a.order)[(size_t)bh * a.nqb + tile] : tile;
-    a.qb.get(bh, I, qs, ql);
+    a.qb.get(bh, I, qs, ql);          // uniform, or a short block: one tile
+    ql = min(ql, 64);
   } else {
     const cint* tb = (const cint*)a.tile_base + (size_t)bh * (a.nqb + 1);
     if (tile >= tb[a.nqb]) return;
@@ -595,7 +615,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
     ql = min(64, n0 - 64 * sub);
   }
   if (ql <= 0) return;
-  attn_tile<D, KVAR>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
+  attn_tile<D, KMODE>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
 }
 
 // Processing order of uniform query blocks: longest first. The query blocks
@@ -722,10 +742,14 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.kv_count = kv_count; a.kv_index = kv_index; a.kv_stride = kv_stride;
   a.sl2 = scale * 1.4426950408889634f;
   a.lse = lse;
-  // Uniform 64-token query blocks need no tiling table; key blocks that are not
-  // uniform 64-token blocks are gathered row by row.
-  const bool qvar = qb.start != nullptr;
-  const bool kvar = kb.start != nullptr;
+  // Uniform 64-token query blocks, and descriptor blocks the caller bounds to
+  // 64 tokens, are one tile each (longest first); longer query blocks are cut
+  // into 64-row tiles through a tiling table. Key blocks bounded to 64 tokens
+  // are one chunk each; others are gathered row by row.
+  const bool qvar = qb.start != nullptr && !(qb.max_len >= 1 && qb.max_len <= 64);
+  const bool kshort = kb.start != nullptr && kb.max_len >= 1 && kb.max_len <= 64;
+  const bool kvar = kb.start != nullptr && !kshort;
+  const int kmode = kvar ? 2 : kshort ? 1 : 0;
   a.tile_base = tile_ws;
   a.order = nullptr;
   if (qvar) {
@@ -747,20 +771,23 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   // traffic that mostly misses L2; there one wave per 64-row tile, which
   // shares each K/V operand read between both query halves, does better
   // (measured at 1857 key blocks: +8..11 %; at 512: -12 %).
-  if (d == 128 && !qvar && !kvar && a.order && kb.nblocks >= kOneWaveKeyBlocks)
+  if (d == 128 && !qvar && qb.start == nullptr && kmode == 0 && a.order && kb.nblocks >= kOneWaveKeyBlocks)
     return launch_attn_fwd_1w(a, (int)grid, s);
-#define BSA_ATTN(DD, QV, KV) attn_fwd_kernel<DD, QV, KV><<<(int)grid, 128, 0, s>>>(a)
+#define BSA_ATTN(DD, QV, KM) attn_fwd_kernel<DD, QV, KM><<<(int)grid, 128, 0, s>>>(a)
+#define BSA_ATTN_K(DD, QV)               \
+  do {                                   \
+    if (kmode == 2) BSA_ATTN(DD, QV, 2); \
+    else if (kmode == 1) BSA_ATTN(DD, QV, 1); \
+    else BSA_ATTN(DD, QV, 0);            \
+  } while (0)
   if (d == 128) {
-    if (qvar && kvar) BSA_ATTN(128, true, true);
-    else if (qvar) BSA_ATTN(128, true, false);
-    else if (kvar) BSA_ATTN(128, false, true);
-    else BSA_ATTN(128, false, false);
+    if (qvar) BSA_ATTN_K(128, true);
+    else BSA_ATTN_K(128, false);
   } else {
-    if (qvar && kvar) BSA_ATTN(64, true, true);
-    else if (qvar) BSA_ATTN(64, true, false);
-    else if (kvar) BSA_ATTN(64, false, true);
-    else BSA_ATTN(64, false, false);
+    if (qvar) BSA_ATTN_K(64, true);
+    else BSA_ATTN_K(64, false);
   }
+#undef BSA_ATTN_K
 #undef BSA_ATTN
   return hipGetLastError();
 }

@@ -35,6 +35,7 @@ struct Blocks {
   const int32_t* len;
   int32_t nblocks;
   int32_t per_head;
+  int32_t max_len;   // descriptors: 1..64 = no block is longer (caller's bound), else 0
   int32_t block;     // uniform block size
   int32_t n_valid;   // uniform: blocks cover [0, n_valid)
 

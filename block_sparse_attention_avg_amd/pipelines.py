@@ -46,10 +46,13 @@ class FractalLayout:
     coords: torch.Tensor        # int32 [nblocks, 3] (host)
 
 
-def fractal_layout(T: int, Hl: int, Wl: int, P: int, N: int, device) -> FractalLayout:
+def fractal_layout(T: int, Hl: int, Wl: int, P: int, N: int, device, bound_blocks: bool = True) -> FractalLayout:
+    """``bound_blocks``: pass the longest patch as the blocks' length bound
+    (when it is at most 64), so attention takes each patch as one tile."""
     perm, st, ln, co = fractal_order(T, Hl, Wl, P, N)
     grid = (T, -(-Hl // P), -(-Wl // P))
-    return FractalLayout(perm.to(device), Blocks(st.to(device), ln.to(device)), grid, co)
+    mx = int(ln.max()) if bound_blocks and len(ln) else 0
+    return FractalLayout(perm.to(device), Blocks(st.to(device), ln.to(device), mx if mx <= 64 else 0), grid, co)
 
 
 def fractal_sta_attention(q, k, v, layout: FractalLayout, thr: float,
@@ -77,9 +80,11 @@ class HeadTiling:
     nblocks: Tuple[int, ...]    # real boxes of each head
 
 
-def head_tiling_layout(T: int, Hl: int, Wl: int, factors, N: int, B: int, device) -> HeadTiling:
+def head_tiling_layout(T: int, Hl: int, Wl: int, factors, N: int, B: int, device,
+                       bound_blocks: bool = True) -> HeadTiling:
     """One ``tile_order`` per head; block lists are padded to a common count
-    with blocks of length 0 (they take no part in the mask)."""
+    with blocks of length 0 (they take no part in the mask). ``bound_blocks``
+    passes the longest box (when at most 64 tokens) as the length bound."""
     orders = [tile_order(T, Hl, Wl, *f, N) for f in factors]
     nb = max(len(o[1]) for o in orders)
     H = len(factors)
@@ -92,7 +97,8 @@ def head_tiling_layout(T: int, Hl: int, Wl: int, factors, N: int, B: int, device
 
     def dev(x):
         return x.unsqueeze(0).expand(B, *x.shape).contiguous().to(device)
-    return HeadTiling(dev(perm), Blocks(dev(st), dev(ln)), tuple(tuple(f) for f in factors),
+    mx = int(ln.max()) if bound_blocks else 0
+    return HeadTiling(dev(perm), Blocks(dev(st), dev(ln), mx if mx <= 64 else 0), tuple(tuple(f) for f in factors),
                       tuple(len(o[1]) for o in orders))
 
 

@@ -67,12 +67,18 @@ enum bsa_status {
  * side must not overlap. Passing NULL for a bsa_blocks* means uniform
  * blocks: block i = [block*i, min(block*(i+1), n_valid)),
  * nblocks = ceil(n_valid / block).
+ * `max_len` is an optional bound the caller vouches for: 1..64 means no block
+ * is longer (fractal patches, head-aware tiling boxes), and the attention
+ * then takes every block as one 64-row tile, longest rows first, with no
+ * gathering of key rows; a longer block would be cut to its first 64 tokens
+ * (unspecified output). 0 (or > 64) means any length.
  */
 typedef struct bsa_blocks {
   int32_t nblocks;
   int32_t per_head;
   const int32_t* start;
   const int32_t* len;
+  int32_t max_len;
 } bsa_blocks;
 
 /*

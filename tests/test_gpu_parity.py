@@ -384,20 +384,29 @@ def _random_partition(rng, n, lens=(0, 1, 7, 17, 33, 64, 65, 100, 150, 230)):
     return np.array(st, np.int32), np.array(ln, np.int32)
 
 
-@pytest.mark.parametrize("d,per_head", [(128, False), (64, True), (128, True)])
-def test_attn_variable_blocks_random(gpu_lib, d, per_head):
-    # query blocks of any length (tiled by 64 rows) and key blocks of any
-    # length (gathered into 64-row chunks), shared or per head
+@pytest.mark.parametrize("d,per_head,mode", [(128, False, "any"), (64, True, "any"), (128, True, "any"),
+                                             (128, False, "short"), (64, True, "short"), (128, True, "short"),
+                                             (128, True, "qshort")])
+def test_attn_variable_blocks_random(gpu_lib, d, per_head, mode):
+    # "any": query blocks of any length (tiled by 64 rows) and key blocks of
+    # any length (gathered into 64-row chunks), shared or per head; "short":
+    # blocks of at most 64 tokens declared as such (one tile / chunk each);
+    # "qshort": short query blocks with gathered key blocks
     bsa = gpu_lib
     H, N, nv = 3, 1100, 1037
-    rng = np.random.default_rng(d + per_head)
-    say(f"attention variable blocks d={d} per_head={per_head}")
+    rng = np.random.default_rng(d + per_head + 7 * len(mode))
+    say(f"attention variable blocks d={d} per_head={per_head} mode={mode}")
     x = rng.normal(size=(3, 1, H, N, d)).astype(np.float32)
     x[:, :, :, nv:] = 0
     q, k, v = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(3))
     heads = range(H) if per_head else [0]
-    parts_q = [_random_partition(rng, nv) for _ in heads]
-    parts_k = [_random_partition(rng, nv) for _ in heads]
+    short_lens = (0, 1, 7, 17, 33, 48, 64, 64, 64)
+    parts_q = [_random_partition(rng, nv, short_lens) if mode != "any" else _random_partition(rng, nv)
+               for _ in heads]
+    parts_k = [_random_partition(rng, nv, short_lens) if mode == "short" else _random_partition(rng, nv)
+               for _ in heads]
+    mq = 64 if mode != "any" else 0
+    mk = 64 if mode == "short" else 0
     nqb = max(len(p[0]) for p in parts_q)
     nkb = max(len(p[0]) for p in parts_k)
 
@@ -421,11 +430,11 @@ def test_attn_variable_blocks_random(gpu_lib, d, per_head):
             ids = np.nonzero(keep[h, i])[0]
             idx[h, i, :len(ids)] = ids
     if per_head:
-        qb = bsa.Blocks(torch.from_numpy(qst[None]).cuda(), torch.from_numpy(qln[None]).cuda())
-        kb = bsa.Blocks(torch.from_numpy(kst[None]).cuda(), torch.from_numpy(kln[None]).cuda())
+        qb = bsa.Blocks(torch.from_numpy(qst[None]).cuda(), torch.from_numpy(qln[None]).cuda(), mq)
+        kb = bsa.Blocks(torch.from_numpy(kst[None]).cuda(), torch.from_numpy(kln[None]).cuda(), mk)
     else:
-        qb = bsa.Blocks(torch.from_numpy(qst[0]).cuda(), torch.from_numpy(qln[0]).cuda())
-        kb = bsa.Blocks(torch.from_numpy(kst[0]).cuda(), torch.from_numpy(kln[0]).cuda())
+        qb = bsa.Blocks(torch.from_numpy(qst[0]).cuda(), torch.from_numpy(qln[0]).cuda(), mq)
+        kb = bsa.Blocks(torch.from_numpy(kst[0]).cuda(), torch.from_numpy(kln[0]).cuda(), mk)
     o = bsa.block_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(cnt[None]).cuda(),
                                   torch.from_numpy(idx[None]).cuda(), n_valid=nv, qb=qb, kb=kb)
     o = _np(o)

@@ -111,6 +111,26 @@ def test_fractal_sta_path(gpu_lib):
         _check_out(o[0, h], ref, rows, f"head {h} ({len(blocks)} patch blocks)")
 
 
+def test_fractal_patch_tiles_match_gathered_keys(gpu_lib):
+    # patches declared as at most 64 tokens run one tile per patch; the same
+    # attention with undeclared lengths gathers key rows into 64-row chunks
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_fractal_sta"]
+    q, k, v = _wan480()
+    heads = [0, 3]
+    lay = pl.fractal_layout(w.T, w.Hl, w.Wl, w.patch, w.N, "cuda")
+    assert lay.blocks.max_len == 64
+    gat = bsa.Blocks(lay.blocks.start, lay.blocks.length)
+    qp, kp, vp = (bsa.permute_tokens(t[:, heads].contiguous().cuda(), lay.perm) for t in (q, k, v))
+    cnt, idx = bsa.build_block_mask(qp, kp, w.thr, window=(*lay.grid, *w.window), n_valid=w.n_valid,
+                                    qb=lay.blocks, kb=lay.blocks)
+    o1 = bsa.block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=w.n_valid, qb=lay.blocks, kb=lay.blocks)
+    o2 = bsa.block_sparse_attn_fwd(qp, kp, vp, cnt, idx, n_valid=w.n_valid, qb=gat, kb=gat)
+    d = (o1.float() - o2.float()).abs()
+    say(f"  patch tiles vs gathered keys: max-abs {float(d.max()):.3e} mean-abs {float(d.mean()):.3e}")
+    assert float(d.max()) <= MAX_ABS and float(d.mean()) <= MEAN_ABS
+
+
 def test_window_only_mask_is_static_sta(gpu_lib):
     # thr = 0 with the window keeps everything; with thr = 1 the kept set is
     # the window plus each row's heaviest block.
