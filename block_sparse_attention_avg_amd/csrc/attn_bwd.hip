@@ -127,15 +127,18 @@ __global__ __launch_bounds__(256) void csc_list_kernel(BwdArgs a, size_t cols) {
   if (lane == 0) a.q_count[col] = base;
 }
 
-// dQ of one 64-row query tile (wave w owns query rows 32w .. 32w+31).
+// dQ of one 64-row query tile. Four waves: wave w owns query rows
+// 32 (w & 1) .. +31 and key rows 32 (w >> 1) .. +31 of every chunk, so each
+// wave holds half the per-chunk state and two waves share a SIMD.
 // Per kept key block, on double-buffered K / V tiles:
-//   S^T = K Q^T, dP^T = V dO^T      (Q^T, dO^T stay in registers)
+//   S^T = K Q^T, dP^T = V dO^T      (32 keys x 32 queries; Q^T, dO^T in registers)
 //   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)   (lane-local)
 //   dQ^T += K^T dS^T                (K^T through the transpose read)
+// The two key halves' partial dQ^T meet in LDS at the end (fixed order).
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
-  using T = Tile<D>;
-  constexpr int NS = D / 8;                        // MFMA steps per product
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using T = Tile<D, 4>;
+  constexpr int NC = D / 16;                       // MFMA k-steps over the channels
   __shared__ __align__(16) unsigned char K0[T::BYTES];
   __shared__ __align__(16) unsigned char V0[T::BYTES];
   __shared__ __align__(16) unsigned char K1[T::BYTES];
@@ -147,19 +150,20 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   if (ql <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = wave & 1, kw = wave >> 1;
   const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * a.N;
   const uint16_t* kh = a.k + head * D;
   const uint16_t* vh = a.v + head * D;
   const float sl2 = a.scale * kLog2e;
 
-  // Q^T and dO^T as MFMA B operands: lane supplies row 32w + l32,
+  // Q^T and dO^T as MFMA B operands: lane supplies row 32qw + l32,
   // channels 16 c + 8 half .. +7
-  const int qr = 32 * wave + l32;
+  const int qr = 32 * qw + l32;
   const bool qok = qr < ql;
-  bf16x8 qf[D / 16], gf[D / 16];
+  bf16x8 qf[NC], gf[NC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const size_t off = (head + qs + (qok ? qr : 0)) * D + 16 * c + 8 * half;
     qf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.q + off) : bf16x8{};
     gf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.dout + off) : bf16x8{};
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   const int cnt = min(max(((const cint*)a.kv_count)[lrow], 0), a.kv_stride);
   const cint* list = (const cint*)(a.kv_index + lrow * a.kv_stride);
   uint32_t off[T::NI];
-  tile_offsets<D>(wave, lane, off);
+  tile_offsets<D, 4>(wave, lane, off);
   const TrOffsets<D> tro(lane);
   auto block_of = [&](int c, int& ks, int& kl) {   // chunk c of the list (clamped into range)
     int J = list[c < cnt ? c : cnt - 1];
@@ -192,40 +196,34 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     int ks, kl, ks1, kl1;
     block_of(c, ks, kl);
     block_of(c + 1, ks1, kl1);
-    tile_load<D>(kh, ks1, kl1, Kn, wave, off);
-    tile_load<D>(vh, ks1, kl1, Vn, wave, off);
+    tile_load<D, 4>(kh, ks1, kl1, Kn, wave, off);
+    tile_load<D, 4>(vh, ks1, kl1, Vn, wave, off);
     wait_vm<2 * T::NI>();                          // this wave's share of chunk c landed
-    wg_barrier();                                  // and the other wave's
-    f32x16 s[2], dp[2];
+    wg_barrier();                                  // and the other waves'
+    f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int kb = j & 1, cc = j >> 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Kc, kb, cc, l32, half), qf[cc], s[kb], 0, 0, 0);
-      dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Vc, kb, cc, l32, half), gf[cc], dp[kb], 0, 0, 0);
+    for (int cc = 0; cc < NC; ++cc) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Kc, kw, cc, l32, half), qf[cc], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Vc, kw, cc, l32, half), gf[cc], dp, 0, 0, 0);
     }
-    uint32_t pw[2][2][4];
+    uint32_t pw[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 16; r += 2) {
+      float d2[2];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float d2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int key = 32 * kb + acc_row(r + u, half);
-          const float p = key < kl ? __builtin_amdgcn_exp2f(fmaf(s[kb][r + u], sl2, -lse2)) : 0.f;
-          d2[u] = p * (dp[kb][r + u] - drow);
-        }
-        pw[kb][r >> 3][(r & 7) >> 1] = pack2(d2[0], d2[1]);
+      for (int u = 0; u < 2; ++u) {
+        const int key = 32 * kw + acc_row(r + u, half);
+        const float p = key < kl ? __builtin_amdgcn_exp2f(fmaf(s[r + u], sl2, -lse2)) : 0.f;
+        d2[u] = p * (dp[r + u] - drow);
       }
+      pw[r >> 3][(r & 7) >> 1] = pack2(d2[0], d2[1]);
+    }
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
-      const bf16x8 ds = __builtin_bit_cast(bf16x8, (u32x4){pw[kb][hh][0], pw[kb][hh][1], pw[kb][hh][2], pw[kb][hh][3]});
-      dq[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Kc, tro, kb, hh, dg), ds, dq[dg], 0, 0, 0);
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 ds = __builtin_bit_cast(bf16x8, (u32x4){pw[hh][0], pw[hh][1], pw[hh][2], pw[hh][3]});
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+        dq[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Kc, tro, kw, hh, dg), ds, dq[dg], 0, 0, 0);
     }
     wg_barrier();                                  // (Kc, Vc) free for chunk c+2
   };
@@ -233,8 +231,8 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   if (cnt > 0) {
     int ks0, kl0;
     block_of(0, ks0, kl0);
-    tile_load<D>(kh, ks0, kl0, (lds_u8*)K0, wave, off);
-    tile_load<D>(vh, ks0, kl0, (lds_u8*)V0, wave, off);
+    tile_load<D, 4>(kh, ks0, kl0, (lds_u8*)K0, wave, off);
+    tile_load<D, 4>(vh, ks0, kl0, (lds_u8*)V0, wave, off);
     for (int c = 0;;) {
       step(c, (const lds_u8*)K0, (const lds_u8*)V0, (lds_u8*)K1, (lds_u8*)V1);
       if (++c >= cnt) break;
@@ -243,8 +241,23 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   wait_vm<0>();                                    // no load of this wave targets LDS
-  wg_barrier();                                    // nor one of the other wave
-  store_rows<D>(dq, a.scale, (lds_u8*)K0, a.dq + head * D, qs, ql, wave, lane);
+  wg_barrier();                                    // nor one of the other waves
+  // the second key half's partial dQ^T joins the first's: 16 KiB per wave
+  lds_f32* park = (lds_f32*)(qw ? V0 : K0);
+  if (kw == 1) {
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) park[(dg * 16 + r) * 64 + lane] = dq[dg][r];
+  }
+  wg_barrier();
+  if (kw == 0) {
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[dg][r] += park[(dg * 16 + r) * 64 + lane];
+  }
+  store_rows<D, 256>(dq, a.scale, (lds_u8*)K1, a.dq + head * D, qs, ql, qw, lane, kw == 0);
 }
 
 // dK, dV of one 64-key tile (wave w owns keys 32w .. 32w+31). Per query block
@@ -448,10 +461,10 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.order_k = launch_qorder(a.q_count, BH, nb, nb, ok, s) ? ok : nullptr;
   const int tiles = (int)lrows;
   if (d == 128) {
-    bwd_dq_kernel<128><<<tiles, 128, 0, s>>>(a);
+    bwd_dq_kernel<128><<<tiles, 256, 0, s>>>(a);
     bwd_dkdv_kernel<128><<<tiles, 128, 0, s>>>(a);
   } else {
-    bwd_dq_kernel<64><<<tiles, 128, 0, s>>>(a);
+    bwd_dq_kernel<64><<<tiles, 256, 0, s>>>(a);
     bwd_dkdv_kernel<64><<<tiles, 128, 0, s>>>(a);
   }
   return hipGetLastError();

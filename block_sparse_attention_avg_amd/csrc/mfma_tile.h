@@ -52,22 +52,22 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
 
-// Tile geometry shared by the two gradient kernels: 64 rows of D bf16,
-// row-major in LDS with swizzled 16-byte pieces; wave w of 2 loads rows
-// 32w .. 32w+31.
-template <int D>
+// Tile geometry: 64 rows of D bf16, row-major in LDS with swizzled 16-byte
+// pieces; the NW waves of a workgroup share its loads (wave w loads rows
+// 64w/NW .. 64(w+1)/NW - 1).
+template <int D, int NW = 2>
 struct Tile {
   static constexpr int ROWB = D * 2;
   static constexpr int BYTES = 64 * ROWB;
-  static constexpr int NI = BYTES / 1024 / 2;      // direct-to-LDS loads per wave
+  static constexpr int NI = BYTES / 1024 / NW;     // direct-to-LDS loads per wave
   static constexpr int RPI = 1024 / ROWB;          // rows per load
   static constexpr int PPR = ROWB / 16;            // 16-byte pieces per row
 };
 
 // Lane offsets of a wave's share of a 64-row tile load.
-template <int D>
+template <int D, int NW = 2>
 __device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) {
-  using T = Tile<D>;
+  using T = Tile<D, NW>;
 #pragma unroll
   for (int i = 0; i < T::NI; ++i) {
     const int r = (wave * T::NI + i) * T::RPI + lane / T::PPR;
@@ -75,10 +75,10 @@ __device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) 
   }
 }
 // Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros.
-template <int D>
+template <int D, int NW = 2>
 __device__ __forceinline__ void tile_load(const uint16_t* head, int r0, int n, lds_u8* dst, int wave,
                                           const uint32_t* off) {
-  using T = Tile<D>;
+  using T = Tile<D, NW>;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)max(n, 0) * T::ROWB);
 #pragma unroll
   for (int i = 0; i < T::NI; ++i) dma16(rs, dst + (wave * T::NI + i) * 1024, off[i]);
@@ -119,27 +119,31 @@ __device__ __forceinline__ bf16x8 tr_read(const lds_u8* t, const TrOffsets<D>& o
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 // 64 x D accumulator tile (transposed: channels x rows, 32 rows per wave) ->
-// bf16 rows [r0, r0 + n) of `out`, staged through `stage` (a free tile).
-template <int D>
+// bf16 rows [r0, r0 + n) of `out`, staged through `stage` (a free tile). All
+// NT threads of the workgroup take part; only waves with `active` hold rows
+// (row half `wave`).
+template <int D, int NT = 128>
 __device__ __forceinline__ void store_rows(const f32x16* acc, float mul, lds_u8* stage, uint16_t* out, int r0,
-                                           int n, int wave, int lane) {
+                                           int n, int wave, int lane, bool active = true) {
   using T = Tile<D>;
   const int half = lane >> 5, l32 = lane & 31;
   const int orow = 32 * wave + l32;
   const int fo = swz<D>(orow & 15);
+  if (active) {
 #pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
+    for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const u32x2 w = {pack2(acc[dg][4 * j4 + 0] * mul, acc[dg][4 * j4 + 1] * mul),
-                       pack2(acc[dg][4 * j4 + 2] * mul, acc[dg][4 * j4 + 3] * mul)};
-      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-          stage + orow * T::ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
-    }
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const u32x2 w = {pack2(acc[dg][4 * j4 + 0] * mul, acc[dg][4 * j4 + 1] * mul),
+                         pack2(acc[dg][4 * j4 + 2] * mul, acc[dg][4 * j4 + 3] * mul)};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+            stage + orow * T::ROWB + (((4 * dg + j4) ^ fo) << 4) + 8 * half) = w;
+      }
+  }
   wg_barrier();
 #pragma unroll
-  for (int r = 0; r < T::BYTES / 16 / 128; ++r) {
-    const int u = threadIdx.x + 128 * r;
+  for (int r = 0; r < T::BYTES / 16 / NT; ++r) {
+    const int u = threadIdx.x + NT * r;
     const int row = u / T::PPR, p = u % T::PPR;
     if (row < n)
       *reinterpret_cast<u32x4*>(out + (size_t)(r0 + row) * D + p * 8) =
