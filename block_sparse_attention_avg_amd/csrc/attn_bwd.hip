@@ -260,14 +260,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   store_rows<D, 256>(dq, a.scale, (lds_u8*)K1, a.dq + head * D, qs, ql, qw, lane, kw == 0);
 }
 
-// dK, dV of one 64-key tile (wave w owns keys 32w .. 32w+31). Per query block
-// that kept it, on double-buffered Q / dO tiles, for each 32-row query half g:
-//   S = Q K^T, dP = dO V^T          (K^T, V^T stay in registers)
+// dK, dV of one 64-key tile. Four waves: wave w owns keys 32 (w & 1) .. +31
+// and query rows 32 (w >> 1) .. +31 of every chunk. Per query block that kept
+// the tile, on double-buffered Q / dO tiles:
+//   S = Q K^T, dP = dO V^T          (32 queries x 32 keys; K^T, V^T in registers)
 //   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)
 //   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through the transpose read)
+// The two query halves' partial dK^T, dV^T meet in LDS at the end (fixed order).
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
-  using T = Tile<D>;
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = Tile<D, 4>;
+  constexpr int NC = D / 16;                       // MFMA k-steps over the channels
   __shared__ __align__(16) unsigned char Q0[T::BYTES];
   __shared__ __align__(16) unsigned char G0[T::BYTES];
   __shared__ __align__(16) unsigned char Q1[T::BYTES];
@@ -283,19 +286,20 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
   if (kl <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 1, g = wave >> 1;
   const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * a.N;
   const uint16_t* qh = a.q + head * D;
   const uint16_t* gh = a.dout + head * D;
   const float sl2 = a.scale * kLog2e;
 
-  // K^T and V^T as MFMA B operands: lane supplies key 32w + l32, channels
+  // K^T and V^T as MFMA B operands: lane supplies key 32kw + l32, channels
   // 16 c + 8 half .. +7
-  const int kr = 32 * wave + l32;
+  const int kr = 32 * kw + l32;
   const bool kok = kr < kl;
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[NC], vf[NC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const size_t o = (head + ks + (kok ? kr : 0)) * D + 16 * c + 8 * half;
     kf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.k + o) : bf16x8{};
     vf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.v + o) : bf16x8{};
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
   const int cnt = ((const cint*)a.q_count)[lcol];
   const cint* list = (const cint*)(a.q_index + lcol * a.nqb);
   uint32_t off[T::NI];
-  tile_offsets<D>(wave, lane, off);
+  tile_offsets<D, 4>(wave, lane, off);
   const TrOffsets<D> tro(lane);
 
   // rows, lse and Dr of chunk c (clamped into range); lane l of each wave
@@ -321,12 +325,12 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
     const bool ok = lane < ql;
     lv = INFINITY;
     rv = 0.f;
-    if (ok) {                                      // both waves: equal load counts
+    if (ok) {                                      // every wave: equal load counts
       lv = a.lse[head + qs + lane];
       rv = a.dr[head + qs + lane];
     }
-    tile_load<D>(qh, qs, ql, Qn, wave, off);
-    tile_load<D>(gh, qs, ql, Gn, wave, off);
+    tile_load<D, 4>(qh, qs, ql, Qn, wave, off);
+    tile_load<D, 4>(gh, qs, ql, Gn, wave, off);
   };
   // one chunk: chunk c+1 (or a reload of c) goes out first; chunk c's tiles
   // must have landed and its lse / Dr are in registers lv, rv (wave 0)
@@ -339,42 +343,39 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
     issue(c + 1, Qn, Gn, lv_n, rv_n);
     wait_vm<2 * T::NI + 2>();                      // chunk c landed (and its lse / Dr before it)
     wg_barrier();
+    f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {                  // 32-row query half
-      f32x16 s = {}, dp = {};
+    for (int cc = 0; cc < NC; ++cc) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Qc, g, cc, l32, half), kf[cc], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Gc, g, cc, l32, half), vf[cc], dp, 0, 0, 0);
+    }
+    uint32_t pp[2][4], pd[2][4];
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Qc, g, cc, l32, half), kf[cc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(Gc, g, cc, l32, half), vf[cc], dp, 0, 0, 0);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      // rows 32g + 8 r4 + 4 half + 0..3 of the chunk
+      const int row0 = 32 * g + 8 * r4 + 4 * half;
+      const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Lc + row0);
+      const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Rc + row0);
+      float p[4], d[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * r4 + u;
+        p[u] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[u]));
+        d[u] = p[u] * (dp[r] - d4[u]);
       }
-      uint32_t pp[2][4], pd[2][4];
+      pp[r4 >> 1][2 * (r4 & 1) + 0] = pack2(p[0], p[1]);
+      pp[r4 >> 1][2 * (r4 & 1) + 1] = pack2(p[2], p[3]);
+      pd[r4 >> 1][2 * (r4 & 1) + 0] = pack2(d[0], d[1]);
+      pd[r4 >> 1][2 * (r4 & 1) + 1] = pack2(d[2], d[3]);
+    }
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        // rows 32g + 8 r4 + 4 half + 0..3 of the chunk
-        const int row0 = 32 * g + 8 * r4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Lc + row0);
-        const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Rc + row0);
-        float p[4], d[4];
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
+      const bf16x8 db = __builtin_bit_cast(bf16x8, (u32x4){pd[hh][0], pd[hh][1], pd[hh][2], pd[hh][3]});
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * r4 + u;
-          p[u] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[u]));
-          d[u] = p[u] * (dp[r] - d4[u]);
-        }
-        pp[r4 >> 1][2 * (r4 & 1) + 0] = pack2(p[0], p[1]);
-        pp[r4 >> 1][2 * (r4 & 1) + 1] = pack2(p[2], p[3]);
-        pd[r4 >> 1][2 * (r4 & 1) + 0] = pack2(d[0], d[1]);
-        pd[r4 >> 1][2 * (r4 & 1) + 1] = pack2(d[2], d[3]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
-        const bf16x8 db = __builtin_bit_cast(bf16x8, (u32x4){pd[hh][0], pd[hh][1], pd[hh][2], pd[hh][3]});
-#pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg) {
-          dv[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Gc, tro, g, hh, dg), pb, dv[dg], 0, 0, 0);
-          dk[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Qc, tro, g, hh, dg), db, dk[dg], 0, 0, 0);
-        }
+      for (int dg = 0; dg < D / 32; ++dg) {
+        dv[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Gc, tro, g, hh, dg), pb, dv[dg], 0, 0, 0);
+        dk[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Qc, tro, g, hh, dg), db, dk[dg], 0, 0, 0);
       }
     }
     wg_barrier();                                  // chunk c's buffers free for chunk c+2
@@ -394,9 +395,32 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vm<0>();
   wg_barrier();
-  store_rows<D>(dk, a.scale, (lds_u8*)Q0, a.dk + head * D, ks, kl, wave, lane);
+  // the second query half's partial dK^T, dV^T join the first's (16 KiB each)
+  lds_f32* park_k = (lds_f32*)(kw ? G0 : Q0);
+  lds_f32* park_v = (lds_f32*)(kw ? G1 : Q1);
+  if (g == 1) {
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        park_k[(dg * 16 + r) * 64 + lane] = dk[dg][r];
+        park_v[(dg * 16 + r) * 64 + lane] = dv[dg][r];
+      }
+  }
   wg_barrier();
-  store_rows<D>(dv, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, wave, lane);
+  if (g == 0) {
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[dg][r] += park_k[(dg * 16 + r) * 64 + lane];
+        dv[dg][r] += park_v[(dg * 16 + r) * 64 + lane];
+      }
+  }
+  wg_barrier();                                    // the parks are read before staging reuses them
+  store_rows<D, 256>(dk, a.scale, (lds_u8*)Q0, a.dk + head * D, ks, kl, kw, lane, g == 0);
+  wg_barrier();
+  store_rows<D, 256>(dv, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, kw, lane, g == 0);
 }
 
 // Pad rows n_valid .. N-1 of dq, dk, dv are zero.
@@ -462,10 +486,10 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int tiles = (int)lrows;
   if (d == 128) {
     bwd_dq_kernel<128><<<tiles, 256, 0, s>>>(a);
-    bwd_dkdv_kernel<128><<<tiles, 128, 0, s>>>(a);
+    bwd_dkdv_kernel<128><<<tiles, 256, 0, s>>>(a);
   } else {
     bwd_dq_kernel<64><<<tiles, 256, 0, s>>>(a);
-    bwd_dkdv_kernel<64><<<tiles, 128, 0, s>>>(a);
+    bwd_dkdv_kernel<64><<<tiles, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
