@@ -94,24 +94,28 @@ __device__ __forceinline__ bf16x8 row_read(const lds_u8* t, int g, int c, int l3
 // order of the accumulator layout (see the forward).
 template <int D>
 struct TrOffsets {
-  int voff[D / 32][2];
+  // offset of channel group dg = 0, row half t = 0; the others follow from
+  // it: channel group dg flips the piece bits 4 dg (byte bits dg << 6), and
+  // the row half t = 1 lies 8 rows further with swizzle bit 8 (D = 128) or
+  // 4 (D = 64) flipped
+  int base;
   __device__ __forceinline__ TrOffsets(int lane) {
     const int half = lane >> 5, g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 8 * t + 4 * half + sj;
-        const int piece = 4 * dg + 2 * g16 + (sq >> 1);
-        voff[dg][t] = row * Tile<D>::ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
-      }
+    const int row = 4 * half + sj;
+    const int piece = 2 * g16 + (sq >> 1);
+    base = row * Tile<D>::ROWB + ((piece ^ swz<D>(row)) << 4) + ((sq & 1) << 3);
+  }
+  __device__ __forceinline__ int at(int dg, int t) const {
+    constexpr int kFlip = D == 128 ? 128 : 64;
+    const int o = base ^ (dg << 6);
+    return t ? (o ^ kFlip) + 8 * Tile<D>::ROWB : o;
   }
 };
 template <int D>
 __device__ __forceinline__ bf16x8 tr_read(const lds_u8* t, const TrOffsets<D>& o, int g, int hh, int dg) {
   const lds_u8* b = t + (32 * g + 16 * hh) * Tile<D>::ROWB;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][0]));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.voff[dg][1]));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.at(dg, 0)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.at(dg, 1)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
