@@ -570,7 +570,7 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
             lines.append(f"{k} (mean per dispatch): " + " ".join(vals))
     elif kind == "traffic":
         fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-        kern = "bsa::attn_fwd_kernel<128, false, false>"
+        kern = "bsa::attn_fwd_kernel<128, false, 0>"
         copy = "bsa::permute_kernel<16>"
         f_att, n1 = rocprof_counter(fetch_dir, "FETCH_SIZE", kern)
         w_att, n2 = rocprof_counter(write_dir, "WRITE_SIZE", kern)
