@@ -167,8 +167,10 @@ int bsa_build_block_mask(const void* q, const void* k, int B, int H, int N, int 
   float* kbar = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                          round256(sizeof(float) * (size_t)B * H * bq.nblocks * d));
   const int BH = B * H;
-  if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(q), BH, N, d, bq, qbar, stream), "pool q")) return e;
-  if (int e = hip_status(bsa::launch_pool(static_cast<const uint16_t*>(k), BH, N, d, bk, kbar, stream), "pool k")) return e;
+  if (int e = hip_status(bsa::launch_pool2(static_cast<const uint16_t*>(q), bq, qbar, static_cast<const uint16_t*>(k),
+                                           bk, kbar, BH, N, d, stream),
+                         "pool q, k"))
+    return e;
   const float sc = 1.f / sqrtf((float)d);
   // descriptor blocks: a block with no tokens takes no part (lengths, no bias)
   const bsa::Sizes sz{bq.start ? bq.len : nullptr, bk.start ? bk.len : nullptr, bq.per_head, bk.per_head, 0};

@@ -623,13 +623,23 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
 // blocks, so the long tiles start early and do not finish last; together with
 // the contiguous per-XCD ranges this keeps the XCDs busy until the end.
 // Affects scheduling only: every tile computes the same bits in any order.
+// With `o` given, the workgroup of head bh also zeroes that head's padding
+// rows [n_valid, N) of O (cpr 16-byte pieces per row) and sets their lse to
+// -inf, which spares the attention call a launch.
 __global__ __launch_bounds__(256) void qorder_kernel(const int32_t* __restrict__ kv_count, int nqb, int nkb,
-                                                     int32_t* __restrict__ order) {
+                                                     int32_t* __restrict__ order, uint4* __restrict__ o,
+                                                     float* __restrict__ lse, int N, int n_valid, int cpr) {
   extern __shared__ int sm[];
   int* cnt = sm;              // [nkb + 1] bucket counts, then cursors
   int* key = sm + nkb + 1;    // [nqb]
   __shared__ int part[257];
   const int bh = blockIdx.x;
+  if (o) {
+    const size_t base = ((size_t)bh * N + n_valid) * cpr;
+    for (int u = threadIdx.x; u < (N - n_valid) * cpr; u += 256) o[base + u] = make_uint4(0, 0, 0, 0);
+    if (lse)
+      for (int r = n_valid + threadIdx.x; r < N; r += 256) lse[(size_t)bh * N + r] = -INFINITY;
+  }
   for (int b = threadIdx.x; b <= nkb; b += 256) cnt[b] = 0;
   __syncthreads();
   for (int I = threadIdx.x; I < nqb; I += 256) {
@@ -715,7 +725,7 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(uint4* __restrict__ o, f
 bool launch_qorder(const int32_t* counts, int BH, int n, int cap, int32_t* order, hipStream_t s) {
   const size_t lds = sizeof(int) * ((size_t)cap + 1 + n);
   if (lds > 64 * 1024) return false;
-  qorder_kernel<<<BH, 256, lds, s>>>(counts, n, cap, order);
+  qorder_kernel<<<BH, 256, lds, s>>>(counts, n, cap, order, nullptr, nullptr, 0, 0, 0);
   return true;
 }
 
@@ -727,14 +737,21 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
                            float scale, int32_t* tile_ws, float* lse, hipStream_t s) {
   if (BH == 0) return hipSuccess;
-  if (n_valid < N) {
+  // padding rows of O are zero (and their lse -inf): folded into the ordering
+  // launch when there is one, else a launch of their own
+  bool pad_done = n_valid >= N;
+  auto zero_pad = [&]() {
     const int cpr = d / 8;
     const size_t total = (size_t)BH * (N - n_valid) * cpr;
     const size_t want = (total + 255) / 256;
     const int grid = (int)(want < 4096 ? want : 4096);
     zero_rows_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<uint4*>(o), lse, N, n_valid, cpr, total);
+    pad_done = true;
+  };
+  if (qb.nblocks == 0) {
+    if (!pad_done) zero_pad();
+    return hipGetLastError();
   }
-  if (qb.nblocks == 0) return hipGetLastError();
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.N = N; a.n_valid = n_valid; a.nqb = qb.nblocks; a.nkb = kb.nblocks;
@@ -760,10 +777,14 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
     const size_t lds = sizeof(int) * ((size_t)kb.nblocks + 1 + qb.nblocks);
     if (lds <= 64 * 1024) {
       int32_t* order = tile_ws;
-      qorder_kernel<<<BH, 256, lds, s>>>(kv_count, qb.nblocks, kb.nblocks, order);
+      qorder_kernel<<<BH, 256, lds, s>>>(kv_count, qb.nblocks, kb.nblocks, order,
+                                         pad_done ? nullptr : reinterpret_cast<uint4*>(o), lse, N, n_valid,
+                                         d / 8);
       a.order = order;
+      pad_done = true;
     }
   }
+  if (!pad_done) zero_pad();
   a.bh = BH;
   const long long grid = 8LL * (((long long)BH * a.tiles + 7) / 8);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;

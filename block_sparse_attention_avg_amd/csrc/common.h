@@ -118,6 +118,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 namespace bsa {
 hipError_t launch_pool(const uint16_t* x, int BH, int N, int d, const Blocks& blk, float* out,
                        hipStream_t s);
+// Q and K pooled in one launch (x1 == nullptr: x0 only).
+hipError_t launch_pool2(const uint16_t* x0, const Blocks& blk0, float* out0, const uint16_t* x1,
+                        const Blocks& blk1, float* out1, int BH, int N, int d, hipStream_t s);
 hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, int nkb, int d,
                          const Sizes& sizes, float thr, float scale,
                          const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,

@@ -12,14 +12,22 @@
 
 namespace bsa {
 
+// One tensor per grid z-slice: z = 0 pools (x0, blk0) into out0, z = 1 (when
+// given) pools (x1, blk1) into out1, so Q and K take one launch.
 template <int D>
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x,
-                                                   float* __restrict__ out, int N, Blocks blk) {
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x0, float* __restrict__ out0,
+                                                   Blocks blk0, const uint16_t* __restrict__ x1,
+                                                   float* __restrict__ out1, Blocks blk1, int N) {
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int RL = 256 / CH;     // row lanes
   __shared__ float red[RL][D + 4];
 
+  const bool second = blockIdx.z == 1;
+  const uint16_t* __restrict__ x = second ? x1 : x0;
+  float* __restrict__ out = second ? out1 : out0;
+  const Blocks& blk = second ? blk1 : blk0;
   const int i = blockIdx.x;
+  if (i >= blk.nblocks) return;
   const int bh = blockIdx.y;
   int s, n;
   blk.get(bh, i, s, n);
@@ -72,12 +80,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
 
 hipError_t launch_pool(const uint16_t* x, int BH, int N, int d, const Blocks& blk, float* out,
                        hipStream_t s) {
-  if (blk.nblocks == 0 || BH == 0) return hipSuccess;
-  dim3 grid(blk.nblocks, BH);
+  return launch_pool2(x, blk, out, nullptr, blk, nullptr, BH, N, d, s);
+}
+
+hipError_t launch_pool2(const uint16_t* x0, const Blocks& blk0, float* out0, const uint16_t* x1,
+                        const Blocks& blk1, float* out1, int BH, int N, int d, hipStream_t s) {
+  const int nb = x1 ? (blk0.nblocks > blk1.nblocks ? blk0.nblocks : blk1.nblocks) : blk0.nblocks;
+  if (nb == 0 || BH == 0) return hipSuccess;
+  dim3 grid(nb, BH, x1 ? 2 : 1);
   if (d == 128)
-    pool_kernel<128><<<grid, 256, 0, s>>>(x, out, N, blk);
+    pool_kernel<128><<<grid, 256, 0, s>>>(x0, out0, blk0, x1, out1, blk1, N);
   else
-    pool_kernel<64><<<grid, 256, 0, s>>>(x, out, N, blk);
+    pool_kernel<64><<<grid, 256, 0, s>>>(x0, out0, blk0, x1, out1, blk1, N);
   return hipGetLastError();
 }
 
