@@ -125,3 +125,45 @@ def test_bwd_mask_stage_lists(gpu_lib):
         do = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
         cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), w.thr, n_valid=nv)
         _run_case(bsa, q, k, v, do, cnt.cpu().numpy()[0], idx.cpu().numpy()[0], nv)
+
+
+def test_bwd_wan480_full_layer_sampled(gpu_lib):
+    # the whole 480p layer (12 heads, 32,760 tokens, the mask stage's lists) in
+    # the launch the bench times; sampled query blocks' dQ and sampled key
+    # blocks' dK, dV against the oracle (each from every query block that
+    # kept that key block), on two heads
+    bsa = gpu_lib
+    w = WORKLOADS["wan480"]
+    q, k, v = generate(w)
+    nv = w.n_valid
+    say("backward, full 480p layer, sampled blocks")
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    do[:, :, nv:] = 0
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    cnt, idx = bsa.build_block_mask(qd, kd, w.thr, n_valid=nv)
+    o, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cnt, idx, n_valid=nv)
+    dq, dk, dv = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cnt, idx, n_valid=nv)
+    torch.cuda.synchronize()
+    cnt, idx = cnt.cpu().numpy()[0], idx.cpu().numpy()[0]
+    dq, dk, dv = (_np(t)[0] for t in (dq, dk, dv))
+    for t in (dq, dk, dv):
+        assert (t[:, nv:] == 0).all()
+    st, ln = ol.raster_blocks(nv)
+    nb = len(st)
+    rng = np.random.default_rng(9)
+    for h in (2, 9):
+        keep = keep_from_lists(cnt[h], idx[h], nb)
+        args = [_np(t[0, h]) for t in (q, k, v, do)]
+        qi = sorted(set(rng.choice(nb, 3, replace=False).tolist()) | {nb - 1})
+        rq, _, _ = oa.masked_attention_bwd(*args, st[qi], ln[qi], st, ln, keep[qi])
+        rows = np.concatenate([np.arange(st[i], st[i] + ln[i]) for i in qi])
+        _check_grad(dq[h], rq, rows, f"head {h} dq (query blocks {qi})")
+        # key blocks: a well-kept one and the last (ragged) one
+        for J in (int(np.argmax(keep.sum(0))), nb - 1):
+            users = np.nonzero(keep[:, J])[0]
+            if len(users) == 0:
+                continue
+            _, rk, rv = oa.masked_attention_bwd(*args, st[users], ln[users], st, ln, keep[users])
+            krows = np.arange(st[J], st[J] + ln[J])
+            _check_grad(dk[h], rk, krows, f"head {h} dk (key block {J}, {len(users)} query blocks)")
+            _check_grad(dv[h], rv, krows, f"head {h} dv (key block {J})")

@@ -91,3 +91,35 @@ def test_tile_stats_mask_stage_lists(gpu_lib):
     say("tile statistics on mask-stage lists, 480p layer, 4096 tokens")
     cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), w.thr, n_valid=4096)
     _check(q, k, cnt.cpu(), idx.cpu(), 4096, [0, 1])
+
+
+def test_tile_stats_wan480_full_layer_sampled(gpu_lib):
+    # the whole 480p layer: sampled query-block rows of the tile map against
+    # the oracle's full-attention rows, and their recall
+    bsa = gpu_lib
+    w = WORKLOADS["wan480"]
+    q, k, _ = generate(w)
+    nv = w.n_valid
+    say("tile statistics, full 480p layer, sampled rows")
+    cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), w.thr, n_valid=nv)
+    mq = pl.mask_quality(q.cuda(), k.cuda(), cnt, idx, n_valid=nv)
+    torch.cuda.synchronize()
+    gmax, gsum, gmin = (_np(t)[0] for t in (mq.tile_max, mq.tile_sum, mq.tile_min))
+    grec, gmass = _np(mq.oracle_recall)[0], _np(mq.mass_recall)[0]
+    cnt, idx = cnt.cpu().numpy()[0], idx.cpu().numpy()[0]
+    st, ln = ol.raster_blocks(nv)
+    nb = len(st)
+    rng = np.random.default_rng(4)
+    for h in (1, 10):
+        kh = _np(k[0, h])[:nv]
+        keep = keep_from_lists(cnt[h], idx[h], nb)
+        for I in sorted(set(rng.choice(nb, 3, replace=False).tolist()) | {nb - 1}):
+            qh = _np(q[0, h])[st[I]:st[I] + ln[I]]
+            rmax, rsum, rmin = od.tile_stats(qh, kh, [0], [ln[I]], st, ln)
+            for g, r, what in ((gmax[h, I], rmax[0], "max"), (gsum[h, I], rsum[0], "sum"),
+                               (gmin[h, I], rmin[0], "min")):
+                np.testing.assert_allclose(g, r, rtol=1e-3, atol=1e-7, err_msg=f"head {h} row {I} tile {what}")
+            rrec, rmass = od.mask_recall(keep[I:I + 1], gmax[h, I:I + 1], gsum[h, I:I + 1])
+            np.testing.assert_allclose(grec[h, I], rrec[0], rtol=0, atol=1e-6)
+            np.testing.assert_allclose(gmass[h, I], rmass[0], rtol=1e-5, atol=1e-7)
+            say(f"  head {h} row {I}: oracle recall {grec[h, I]:.3f} mass recall {gmass[h, I]:.3f}")
