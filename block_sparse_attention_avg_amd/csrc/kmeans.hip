@@ -6,8 +6,10 @@
 // One launch per seeding round: every workgroup owns 256 tokens, keeps their
 // D^2 in a double buffer and publishes its partial sum; at the start of the
 // next round every workgroup re-derives the drawn index from those partials
-// in the same fixed order (no atomics, no grid barrier), the first workgroup
-// records the centre, and all update D^2 against it.
+// with the same fixed-order workgroup scans (over the chunk partials, then
+// over the chosen chunk's D^2; no grid barrier), the first workgroup records
+// the centre, and all update D^2 against it, reading token rows in 16-byte
+// pieces and the centre through scalar loads.
 //
 // Warm start (Sparse VideoGen2 summary, Metodologia C.1: the previous
 // denoising step's centroids initialise k-means): seeding is skipped and the
@@ -72,21 +74,29 @@ __device__ float block_sum_256(float v, float* red) {
 
 }  // namespace
 
-// D^2 of the tokens of this chunk to centre `cidx`; min with the previous D^2
-// unless first. Writes the chunk's partial sum.
+// D^2 of the tokens of this chunk to centre `cidx` (wave-uniform: read with
+// scalar loads); min with the previous D^2 unless first. Each thread reads its
+// token row in 16-byte pieces. Writes the chunk's partial sum.
 template <int D>
 __device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_prev,
                            float* d2_next, float* part_next, bool first, float* red) {
   const int i = blockIdx.x * kChunk + threadIdx.x;
   float v = 0.f;
   if (i < n) {
-    const uint16_t* xr = xh + (size_t)i * D;
-    const uint16_t* cr = xh + (size_t)cidx * D;
+    const uint4* xr = reinterpret_cast<const uint4*>(xh + (size_t)i * D);
+    const uint4* cr = reinterpret_cast<const uint4*>(xh + (size_t)cidx * D);
     float acc = 0.f;
-#pragma unroll 8
-    for (int dd = 0; dd < D; ++dd) {
-      const float t = load_x(xr, dd) - load_x(cr, dd);
-      acc = fmaf(t, t, acc);
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const uint4 w = xr[c8], c = cr[c8];
+      const uint32_t xs[4] = {w.x, w.y, w.z, w.w}, cs[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t0 = bf16_lo(xs[e]) - bf16_lo(cs[e]);
+        const float t1 = bf16_hi(xs[e]) - bf16_hi(cs[e]);
+        acc = fmaf(t0, t0, acc);
+        acc = fmaf(t1, t1, acc);
+      }
     }
     v = first ? acc : fminf(acc, d2_prev[i]);
     d2_next[i] = v;
@@ -95,6 +105,89 @@ __device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_
   if (threadIdx.x == 0) part_next[blockIdx.x] = s;
 }
 
+namespace {
+
+// Inclusive scan of one value per thread over the 256 threads (Hillis-Steele
+// in LDS, fixed order: every workgroup computes the same sums). Returns the
+// thread's inclusive and exclusive sums and the segment total.
+struct ScanOut {
+  float incl, excl, seg;
+};
+__device__ ScanOut block_scan_256(float v, float* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const float add = t >= o ? buf[t - o] : 0.f;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const ScanOut r{buf[t], t ? buf[t - 1] : 0.f, buf[255]};
+  __syncthreads();
+  return r;
+}
+
+// Inverse-CDF draw of the next centre by the whole workgroup: the first token
+// whose running sum of D^2 (chunk partials in order, then the chunk's tokens)
+// exceeds u * total. Rounding can leave the target past the last sum: then the
+// last chunk is taken, and in the chunk the last token with positive D^2.
+// Every thread returns the same token.
+__device__ int kpp_draw(const float* pp, const float* d2p, int nchunk, int n, float u, float* buf, int* flag,
+                        float* fsh) {
+  const int t = threadIdx.x;
+  float total = 0.f;
+  for (int c0 = 0; c0 < nchunk; c0 += 256) {
+    const int c = c0 + t;
+    total += block_scan_256(c < nchunk ? pp[c] : 0.f, buf).seg;
+  }
+  if (!(total > 0.f)) return min((int)floor((double)u * (double)n), n - 1);
+  const float target = u * total;
+  // the chunk: first one whose running sum passes the target
+  int ch = -1;
+  float before = 0.f, carry = 0.f;
+  for (int c0 = 0; c0 < nchunk; c0 += 256) {
+    const int c = c0 + t;
+    const ScanOut sc = block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
+    if (t == 0) flag[0] = 256;
+    __syncthreads();
+    if (c < nchunk && carry + sc.incl > target) atomicMin(&flag[0], t);
+    if (c == nchunk - 1) fsh[0] = carry + sc.excl;            // the fallback's running sum
+    __syncthreads();
+    const int f = flag[0];
+    if (f == t) fsh[1] = carry + sc.excl;
+    __syncthreads();
+    if (f < 256) {
+      ch = c0 + f;
+      before = fsh[1];
+      break;
+    }
+    carry += sc.seg;
+  }
+  if (ch < 0) {
+    ch = nchunk - 1;
+    before = fsh[0];
+  }
+  // the token inside the chunk
+  const int i = ch * kChunk + t;
+  const float v = i < n ? d2p[i] : 0.f;
+  const ScanOut sc = block_scan_256(v, buf);
+  if (t == 0) {
+    flag[0] = 256;
+    flag[1] = -1;
+  }
+  __syncthreads();
+  if (i < n && before + sc.incl > target) atomicMin(&flag[0], t);
+  if (i < n && v > 0.f) atomicMax(&flag[1], t);
+  __syncthreads();
+  const int idx = flag[0] < 256 ? ch * kChunk + flag[0]
+                                : (flag[1] >= 0 ? ch * kChunk + flag[1] : min(n, (ch + 1) * kChunk) - 1);
+  __syncthreads();
+  return idx;
+}
+
+}  // namespace
+
 template <int D>
 __global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restrict__ x, int N,
                                                         int n, int C, int r,
@@ -102,7 +195,8 @@ __global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restri
                                                         float* __restrict__ cent, KmWs ws,
                                                         int BH) {
   __shared__ float red[256];
-  __shared__ int chosen;
+  __shared__ int flag[2];
+  __shared__ float fsh[2];
   const int bh = blockIdx.y;
   const int nchunk = gridDim.x;
   const uint16_t* xh = x + (size_t)bh * N * D;
@@ -113,40 +207,9 @@ __global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restri
   const float* pp = ws.part + ((size_t)prev * BH + bh) * nchunk;
   float* pn = ws.part + ((size_t)next * BH + bh) * nchunk;
 
-  if (threadIdx.x == 0) {
-    int idx;
-    if (r == 0) {
-      idx = (int)floor((double)u * (double)n);
-    } else {
-      float total = 0.f;
-      for (int c = 0; c < nchunk; ++c) total += pp[c];
-      if (!(total > 0.f)) {
-        idx = (int)floor((double)u * (double)n);
-      } else {
-        const float target = u * total;
-        float run = 0.f;
-        int ch = 0;
-        for (; ch < nchunk - 1; ++ch) {
-          if (run + pp[ch] > target) break;
-          run += pp[ch];
-        }
-        // Rounding can leave the in-chunk running sum just short of the
-        // target; then take the chunk's last token with positive D^2.
-        idx = -1;
-        int last_pos = min(n, (ch + 1) * kChunk) - 1;
-        for (int i = ch * kChunk; i < min(n, (ch + 1) * kChunk); ++i) {
-          const float v = d2p[i];
-          if (v > 0.f) last_pos = i;
-          run += v;
-          if (run > target) { idx = i; break; }
-        }
-        if (idx < 0) idx = last_pos;
-      }
-    }
-    chosen = min(max(idx, 0), n - 1);
-  }
-  __syncthreads();
-  const int cidx = chosen;
+  const int idx = r == 0 ? min((int)floor((double)u * (double)n), n - 1)
+                         : kpp_draw(pp, d2p, nchunk, n, u, red, flag, fsh);
+  const int cidx = __builtin_amdgcn_readfirstlane(min(max(idx, 0), n - 1));
   if (blockIdx.x == 0 && threadIdx.x < D)
     cent[((size_t)bh * C + r) * D + threadIdx.x] = load_x(xh + (size_t)cidx * D, threadIdx.x);
   kpp_update<D>(xh, n, cidx, d2p, d2n, pn, r == 0, red);
