@@ -20,8 +20,9 @@
 // the clustering is a fixed point and the result is bit-identical to running
 // the remaining rounds.
 //
-// Lloyd rounds: assignment computes exact fp32 squared distances (centroids
-// are wave-uniform, so they are read through scalar loads); the update is a
+// Lloyd rounds: assignment computes fp32 squared distances (centroids are
+// wave-uniform, so they are read through scalar loads; even and odd channels
+// summed separately, two centroids at a time, for independent FMA chains); the update is a
 // stable counting sort by cluster (per-chunk histograms, a per-head scan, an
 // in-chunk stable rank) followed by a per-cluster mean over the cluster's
 // tokens in ascending token order. Every reduction has a fixed order, so
@@ -107,25 +108,29 @@ __device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_
 
 namespace {
 
-// Inclusive scan of one value per thread over the 256 threads (Hillis-Steele
-// in LDS, fixed order: every workgroup computes the same sums). Returns the
-// thread's inclusive and exclusive sums and the segment total.
+// Inclusive scan of one value per thread over the 256 threads: a shuffle scan
+// inside each wave, then the wave totals added in wave order (fixed order:
+// every workgroup computes the same sums). Returns the thread's inclusive and
+// exclusive sums and the segment total.
 struct ScanOut {
   float incl, excl, seg;
 };
 __device__ ScanOut block_scan_256(float v, float* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const float add = t >= o ? buf[t - o] : 0.f;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float up = __shfl_up(incl, o);
+    if (lane >= o) incl += up;
   }
-  const ScanOut r{buf[t], t ? buf[t - 1] : 0.f, buf[255]};
+  const float prev = __shfl_up(incl, 1);
+  if (lane == 63) buf[w] = incl;
   __syncthreads();
-  return r;
+  float off = 0.f;
+  for (int j = 0; j < w; ++j) off += buf[j];
+  const float seg = ((buf[0] + buf[1]) + buf[2]) + buf[3];
+  __syncthreads();
+  return ScanOut{incl + off, lane ? prev + off : off, seg};
 }
 
 // Inverse-CDF draw of the next centre by the whole workgroup: the first token
@@ -241,18 +246,29 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
   const float* cb = cent + (size_t)bh * C * D;
   float best = INFINITY;
   int bi = 0;
-  for (int c = 0; c < C; ++c) {
-    const float* cr = cb + (size_t)c * D;
-    float acc = 0.f;
+  // two centroids per step, each over even and odd channels: four independent
+  // FMA chains; the distance is (even + odd), compared in centroid order
+  auto dist = [&](const float* cr, float& ea, float& oa) {
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd) {
-      const float t = xv[dd] - cr[dd];
-      acc = fmaf(t, t, acc);
+    for (int dd = 0; dd < D; dd += 2) {
+      const float t0 = xv[dd] - cr[dd], t1 = xv[dd + 1] - cr[dd + 1];
+      ea = fmaf(t0, t0, ea);
+      oa = fmaf(t1, t1, oa);
     }
-    if (acc < best) {
-      best = acc;
-      bi = c;
-    }
+  };
+  int c = 0;
+  for (; c + 1 < C; c += 2) {
+    float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
+    dist(cb + (size_t)c * D, e0, o0);
+    dist(cb + (size_t)(c + 1) * D, e1, o1);
+    const float a0 = e0 + o0, a1 = e1 + o1;
+    if (a0 < best) { best = a0; bi = c; }
+    if (a1 < best) { best = a1; bi = c + 1; }
+  }
+  if (c < C) {
+    float e0 = 0.f, o0 = 0.f;
+    dist(cb + (size_t)c * D, e0, o0);
+    if (e0 + o0 < best) { best = e0 + o0; bi = c; }
   }
   // rounds after the first count the tokens that moved
   if (changes && stop.it >= 1 && assign[(size_t)bh * N + i] != bi)
