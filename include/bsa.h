@@ -17,7 +17,12 @@
  * plus the token reorder helpers and the semantic-clustering variant of the
  * Sparse VideoGen2 summary (Metodologia A-C): fractal flattening (NABLA
  * section 1), k-means of Q and K, cluster-contiguous permutation and its
- * inverse, centroid top-p selection and attention over variable-size blocks.
+ * inverse, centroid top-p selection and attention over variable-size blocks;
+ * and around them: the attention backward over the same kept tiles (NABLA
+ * summary, training), k-means warm-started from the previous step's
+ * centroids (Sparse VideoGen2 summary, Metodologia C.1), per-head box
+ * layouts (head-aware tiling, Veda summary 2.2) and a mask-quality
+ * diagnostic against the full attention's tile map (Veda summary 2.1).
  *
  * Conventions for every entry point
  * ---------------------------------
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2   /* 2: bsa_blocks.max_len */
 
 enum bsa_status {
   BSA_OK = 0,

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
     for code in range(5):
         assert lib.bsa_strerror(code).decode()
     assert lib.bsa_strerror(99).decode() == "unknown status"
