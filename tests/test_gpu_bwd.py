@@ -167,3 +167,39 @@ def test_bwd_wan480_full_layer_sampled(gpu_lib):
             krows = np.arange(st[J], st[J] + ln[J])
             _check_grad(dk[h], rk, krows, f"head {h} dk (key block {J}, {len(users)} query blocks)")
             _check_grad(dv[h], rv, krows, f"head {h} dv (key block {J})")
+
+
+def test_bwd_hunyuan720_sampled(gpu_lib):
+    # the 720p layer (24 heads, 118,800 tokens, 1857 key blocks): the
+    # transposed lists over 59 bit-words per row, sampled blocks of one head
+    bsa = gpu_lib
+    w = WORKLOADS["hunyuan720"]
+    q, k, v = generate(w)
+    nv = w.n_valid
+    say("backward, 720p layer, sampled blocks of head 13")
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    do[:, :, nv:] = 0
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    cnt, idx = bsa.build_block_mask(qd, kd, w.thr, n_valid=nv)
+    o, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cnt, idx, n_valid=nv)
+    dq, dk, dv = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cnt, idx, n_valid=nv)
+    torch.cuda.synchronize()
+    h = 13
+    cnt, idx = cnt[0, h].cpu().numpy(), idx[0, h].cpu().numpy()
+    dq, dk, dv = (_np(t[0, h]) for t in (dq, dk, dv))
+    assert (dq[nv:] == 0).all() and (dk[nv:] == 0).all() and (dv[nv:] == 0).all()
+    st, ln = ol.raster_blocks(nv)
+    nb = len(st)
+    keep = keep_from_lists(cnt, idx, nb)
+    args = [_np(t[0, h]) for t in (q, k, v, do)]
+    qi = [int(np.argmax(cnt)), nb - 1]
+    rq, _, _ = oa.masked_attention_bwd(*args, st[qi], ln[qi], st, ln, keep[qi])
+    rows = np.concatenate([np.arange(st[i], st[i] + ln[i]) for i in qi])
+    _check_grad(dq, rq, rows, f"dq (query blocks {qi}, {cnt[qi].tolist()} kept)")
+    J = nb - 1
+    users = np.nonzero(keep[:, J])[0]
+    if len(users):
+        _, rk, rv = oa.masked_attention_bwd(*args, st[users], ln[users], st, ln, keep[users])
+        krows = np.arange(st[J], st[J] + ln[J])
+        _check_grad(dk, rk, krows, f"dk (key block {J}, {len(users)} query blocks)")
+        _check_grad(dv, rv, krows, f"dv (key block {J})")
