@@ -38,11 +38,9 @@
 
 namespace bsa {
 
-
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -81,14 +79,6 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
-  const bf16x2 a = __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2);
-  const bf16x2 b = __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2);
-  const bf16x2 c = __builtin_convertvector((f32x2){p[4], p[5]}, bf16x2);
-  const bf16x2 d = __builtin_convertvector((f32x2){p[6], p[7]}, bf16x2);
-  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
