@@ -136,16 +136,13 @@ __global__ __launch_bounds__(256) void csc_list_kernel(BwdArgs a, size_t cols) {
 //   dQ^T += K^T dS^T                (K^T through the transpose read)
 // The two key halves' partial dQ^T meet in LDS at the end (fixed order).
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, unsigned char* K0, unsigned char* V0,
+                                            unsigned char* K1, unsigned char* V1) {
   using T = Tile<D, 4>;
   constexpr int NC = D / 16;                       // MFMA k-steps over the channels
-  __shared__ __align__(16) unsigned char K0[T::BYTES];
-  __shared__ __align__(16) unsigned char V0[T::BYTES];
-  __shared__ __align__(16) unsigned char K1[T::BYTES];
-  __shared__ __align__(16) unsigned char V1[T::BYTES];
 
   int bh, I;
-  tile_of(blockIdx.x, a.nqb, (int)(gridDim.x / a.nqb), a.order_q, bh, I);
+  tile_of(L, a.nqb, BH, a.order_q, bh, I);
   const int qs = 64 * I, ql = min(64, a.n_valid - qs);
   if (ql <= 0) return;
   const int tid = threadIdx.x;
@@ -268,20 +265,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 //   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through the transpose read)
 // The two query halves' partial dK^T, dV^T meet in LDS at the end (fixed order).
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, unsigned char* Q0, unsigned char* G0,
+                                              unsigned char* Q1, unsigned char* G1, float* L0, float* R0, float* L1,
+                                              float* R1) {
   using T = Tile<D, 4>;
   constexpr int NC = D / 16;                       // MFMA k-steps over the channels
-  __shared__ __align__(16) unsigned char Q0[T::BYTES];
-  __shared__ __align__(16) unsigned char G0[T::BYTES];
-  __shared__ __align__(16) unsigned char Q1[T::BYTES];
-  __shared__ __align__(16) unsigned char G1[T::BYTES];
-  __shared__ __align__(16) float L0[64];           // lse * log2e of the chunk's rows (+inf on pads)
-  __shared__ __align__(16) float R0[64];           // Dr of the chunk's rows (0 on pads)
-  __shared__ __align__(16) float L1[64];
-  __shared__ __align__(16) float R1[64];
 
   int bh, J;
-  tile_of(blockIdx.x, a.nkb, (int)(gridDim.x / a.nkb), a.order_k, bh, J);
+  tile_of(L, a.nkb, BH, a.order_k, bh, J);
   const int ks = 64 * J, kl = min(64, a.n_valid - ks);
   if (kl <= 0) return;
   const int tid = threadIdx.x;
@@ -423,6 +414,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   store_rows<D, 256>(dv, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, kw, lane, g == 0);
 }
 
+// One launch for both gradients: workgroups [0, nkv) take key tiles (dK, dV;
+// the longer work, dispatched first), the rest query tiles (dQ), which fill
+// in as the key tiles drain. nkv is the key-tile count rounded up to a
+// multiple of 8, so each part keeps its own per-XCD ranges; the LDS buffers
+// are shared by the two roles.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a, int BH, int nkv) {
+  __shared__ __align__(16) unsigned char B0[Tile<D>::BYTES];
+  __shared__ __align__(16) unsigned char B1[Tile<D>::BYTES];
+  __shared__ __align__(16) unsigned char B2[Tile<D>::BYTES];
+  __shared__ __align__(16) unsigned char B3[Tile<D>::BYTES];
+  __shared__ __align__(16) float L0[64];           // lse * log2e of the chunk's rows (+inf on pads)
+  __shared__ __align__(16) float R0[64];           // Dr of the chunk's rows (0 on pads)
+  __shared__ __align__(16) float L1[64];
+  __shared__ __align__(16) float R1[64];
+  const int G = blockIdx.x;
+  if (G < nkv) {
+    if (G >= BH * a.nkb) return;                  // padding of the key-tile range
+    bwd_dkdv_tile<D>(a, G, BH, B0, B1, B2, B3, L0, R0, L1, R1);
+  } else {
+    bwd_dq_tile<D>(a, G - nkv, BH, B0, B1, B2, B3);
+  }
+}
+
 // Pad rows n_valid .. N-1 of dq, dk, dv are zero.
 __global__ __launch_bounds__(256) void bwd_zero_pad_kernel(uint4* dq, uint4* dk, uint4* dv, int N, int n_valid,
                                                            int cpr, size_t total) {
@@ -484,13 +499,11 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.order_q = launch_qorder(kv_count, BH, nb, nb, oq, s) ? oq : nullptr;
   a.order_k = launch_qorder(a.q_count, BH, nb, nb, ok, s) ? ok : nullptr;
   const int tiles = (int)lrows;
-  if (d == 128) {
-    bwd_dq_kernel<128><<<tiles, 256, 0, s>>>(a);
-    bwd_dkdv_kernel<128><<<tiles, 256, 0, s>>>(a);
-  } else {
-    bwd_dq_kernel<64><<<tiles, 256, 0, s>>>(a);
-    bwd_dkdv_kernel<64><<<tiles, 256, 0, s>>>(a);
-  }
+  const int nkv = (tiles + 7) & ~7;
+  if (d == 128)
+    bwd_grad_kernel<128><<<nkv + tiles, 256, 0, s>>>(a, BH, nkv);
+  else
+    bwd_grad_kernel<64><<<nkv + tiles, 256, 0, s>>>(a, BH, nkv);
   return hipGetLastError();
 }
 
