@@ -8,13 +8,16 @@
 //   S  = scale Q_I K_J^T,   P = exp(S - lse_I)     (lse from the forward)
 //   dP = dO_I V_J^T,        dS = P * (dP - Dr_I)   (Dr_i = dO_i . O_i)
 //   dQ_I += scale dS K_J,   dK_J += scale dS^T Q_I,   dV_J += P^T dO_I
-// Three kernels, each deterministic (no atomics on the gradients):
+// Every kernel is deterministic (no atomics on the gradients):
 //   bwd_dot_kernel   Dr = rowsum(dO * O), fp32;
-//   bwd_dq_kernel    one 64-row query tile per workgroup (2 waves x 32 rows),
-//                    walks the tile's kept key blocks (the forward's lists);
-//   bwd_dkdv_kernel  one 64-key tile per workgroup (2 waves x 32 keys), walks
-//                    the query blocks that kept it: the lists transposed by
-//                    the csc_* kernels (a bit matrix, then ascending lists).
+//   csc_*_kernel     the lists transposed (key block -> query blocks that
+//                    kept it): a bit matrix, then ascending lists;
+//   bwd_grad_kernel  one launch with two roles, 4 waves per workgroup:
+//                    key tiles (dK, dV) walk the query blocks that kept them,
+//                    query tiles (dQ) walk their kept key blocks (the
+//                    forward's lists); each wave takes a 32 x 32 quarter of
+//                    every 64 x 64 chunk and the two partial sums of a tile
+//                    meet in LDS at the end.
 // The MFMA layouts are those of the forward: a 32 x 32 accumulator whose
 // lane holds one column (query, resp. key) and 16 rows; the second product of
 // each pair takes its bf16 B operand straight from that accumulator, and the
