@@ -83,6 +83,32 @@ def test_argument_validation_before_launch(lib):
     assert lib.bsa_permute_tokens(P, P, P, 1, 1, 8, 64, 0, None) == 1
 
 
+def test_argument_validation_newer_entry_points(lib):
+    P = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    # forward with row normaliser: lse is required; variable blocks are not supported there
+    assert lib.bsa_block_sparse_attn_fwd_lse(P, P, P, P, None, 1, 1, 128, 64, 128, 64, None, None, P, P, 2,
+                                             0.0, P, 1 << 20, None) == 1
+    # backward: uniform 64-token blocks only, pointers, workspace
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 32, P, P, 2, 0.0, P, P, P, P,
+                                         1 << 30, None) == 2
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, None, P, 1, 1, 128, 64, 128, 64, P, P, 2, 0.0, P, P, P, P,
+                                         1 << 30, None) == 1
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 64, P, P, 2, 0.0, P, P, P, P,
+                                         16, None) == 3
+    assert "workspace" in _err(lib)
+    # warm-started k-means: rounds, tolerance, the move counts are required
+    assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 0, 0, P, P, P, P, P, 1 << 30, None) == 1
+    assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 5, -1, P, P, P, P, P, 1 << 30, None) == 1
+    assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 5, 0, P, P, P, None, P, 1 << 30, None) == 1
+    assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 5, 0, P, P, P, P, None, 0, None) == 3
+    # tile statistics and recall
+    assert lib.bsa_attention_tile_stats(P, P, P, 1, 1, 128, 96, 128, 0.0, P, P, P, None) == 2
+    assert lib.bsa_attention_tile_stats(P, P, None, 1, 1, 128, 64, 128, 0.0, P, P, P, None) == 1
+    assert lib.bsa_mask_recall(P, P, P, P, 9000, 1, 1, 4, 9000, P, P, None) == 2
+    assert lib.bsa_mask_recall(P, P, P, P, 0, 1, 1, 4, 4, P, P, None) == 1
+    assert lib.bsa_mask_recall(P, None, P, P, 4, 1, 1, 4, 4, P, P, None) == 1
+
+
 def test_workspace_queries(lib):
     assert lib.bsa_build_block_mask_workspace(1, 12, 512, 512, 128) == 2 * 12 * 512 * 128 * 4
     assert lib.bsa_block_sparse_attn_fwd_workspace(1, 12, 512, None) >= 12 * 513 * 4
