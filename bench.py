@@ -136,7 +136,7 @@ class Runner:
         o, lse = bsa.block_sparse_attn_fwd_lse(self.q, self.k, self.v, self.cnt, self.idx, n_valid=self.w.n_valid)
         grads = tuple(torch.empty_like(self.q) for _ in range(3))
         lib = bsa.load()
-        ws = torch.empty(lib.bsa_block_sparse_attn_bwd_workspace(self.w.B, self.w.H, self.w.N),
+        ws = torch.empty(lib.bsa_block_sparse_attn_bwd_workspace(self.w.B, self.w.H, self.w.N, None, None),
                          dtype=torch.uint8, device=self.q.device)
 
         def fwd():
@@ -273,6 +273,21 @@ def paths_bench(r: Runner, steps: int = 10, warmup: int = 3):
         st["attn_tflops"] = round(f / (st["attention"] * 1e-3) / 1e12, 3)
         st["step_tflops"] = round(f / (st["total"] * 1e-3) / 1e12, 3)
         st["kept_blocks"] = int(cnt.sum())
+        if blocks.max_len:
+            # the backward over the same lists and blocks (seeded upstream gradient)
+            g = torch.randn(q.shape, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(dev)
+            o_l = [None, None]
+
+            def fwd_lse():
+                o_l[0], o_l[1] = bsa.block_sparse_attn_fwd_lse(buf[0], buf[1], buf[2], cnt, idx, n_valid=w.n_valid,
+                                                               qb=blocks, kb=blocks)
+
+            def bwd():
+                bsa.block_sparse_attn_bwd(buf[0], buf[1], buf[2], o_l[0], g, o_l[1], cnt, idx, n_valid=w.n_valid,
+                                          qb=blocks, kb=blocks)
+            tb = run([("fwd_lse", fwd_lse), ("backward", bwd)])
+            st["backward_ms"] = tb["backward"]
+            st["backward_tflops_eff"] = round(2.5 * f / (tb["backward"] * 1e-3) / 1e12, 3)
         out[key] = st
 
     wf = WORKLOADS["wan480_fractal_sta"]

@@ -52,8 +52,9 @@ _SIGS = {
     "bsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z, _P], _I),
     "bsa_block_sparse_attn_fwd_lse": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z,
                                        _P], _I),
-    "bsa_block_sparse_attn_bwd_workspace": ([_I, _I, _I], _Z),
-    "bsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _F, _P, _P, _P, _P,
+    "bsa_block_sparse_attn_bwd_workspace": ([_I, _I, _I, ctypes.POINTER(_Blocks), ctypes.POINTER(_Blocks)], _Z),
+    "bsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_Blocks),
+                                   ctypes.POINTER(_Blocks), _P, _P, _I, _F, _P, _P, _P, _P,
                                    _Z, _P], _I),
     "bsa_permute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "bsa_unpermute_tokens": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
@@ -327,9 +328,11 @@ def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
                           dout: torch.Tensor, lse: torch.Tensor, kv_count: torch.Tensor,
                           kv_index: torch.Tensor, n_valid: Optional[int] = None, block: int = 64,
                           scale: float = 0.0, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-                          workspace: Optional[torch.Tensor] = None
+                          workspace: Optional[torch.Tensor] = None, qb: Optional[Blocks] = None,
+                          kb: Optional[Blocks] = None
                           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Gradients (dq, dk, dv) of the block-sparse attention (uniform blocks)."""
+    """Gradients (dq, dk, dv) of the block-sparse attention: uniform blocks, or
+    descriptors (``qb``, ``kb``) bounded to 64 tokens (``max_len``)."""
     B, H, N, d = _qkv(q, "q")
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         if _qkv(t, n) != q.shape:
@@ -340,7 +343,7 @@ def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
     _dev_tensor(kv_count, torch.int32, "kv_count")
     _dev_tensor(kv_index, torch.int32, "kv_index")
     n_valid = N if n_valid is None else n_valid
-    nqb = -(-n_valid // block)
+    nqb = _nblocks(qb, n_valid, block)
     if kv_count.numel() != B * H * nqb:
         raise ValueError("kv_count must have B*H*nqb entries")
     kv_stride = kv_index.shape[-1]
@@ -351,11 +354,12 @@ def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
         if _qkv(t, n) != q.shape:
             raise ValueError(f"{n} must have the shape of q")
     lib = load()
-    ws_bytes = lib.bsa_block_sparse_attn_bwd_workspace(B, H, N)
+    qr, kr = _blocks_ref(qb), _blocks_ref(kb)
+    ws_bytes = lib.bsa_block_sparse_attn_bwd_workspace(B, H, N, qr, kr)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     _check(lib.bsa_block_sparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                                         lse.data_ptr(), B, H, N, d, n_valid, block, kv_count.data_ptr(),
+                                         lse.data_ptr(), B, H, N, d, n_valid, block, qr, kr, kv_count.data_ptr(),
                                          kv_index.data_ptr(), kv_stride, scale, dq.data_ptr(), dk.data_ptr(),
                                          dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                          _stream(q.device)), "block_sparse_attn_bwd")

@@ -240,15 +240,18 @@ int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, v
                        ws, ws_bytes, stream);
 }
 
-size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N) {
+size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N, const bsa_blocks* qb, const bsa_blocks* kb) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return bsa::attn_bwd_workspace(B * H, N, (N + 63) / 64);
+  const int nqb = qb ? qb->nblocks : (N + 63) / 64, nkb = kb ? kb->nblocks : (N + 63) / 64;
+  if (nqb < 0 || nkb < 0) return 0;
+  return bsa::attn_bwd_workspace(B * H, N, nqb, nkb);
 }
 
 int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, int B, int H, int N, int d, int n_valid, int block,
-                              const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
-                              void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+                              const bsa_blocks* qb, const bsa_blocks* kb, const int32_t* kv_count,
+                              const int32_t* kv_index, int kv_stride, float scale, void* dq, void* dk, void* dv,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
   g_msg[0] = 0;
   if (int e = check_shape(B, H, N, d, n_valid)) return e;
   if (!q || !k || !v || !o || !dout || !lse || !kv_count || !kv_index || !dq || !dk || !dv)
@@ -256,20 +259,23 @@ int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(BSA_EINVAL, "attn_bwd: tensors must be 16-byte aligned");
-  if (block != 64) return fail(BSA_EUNSUPPORTED, "attn_bwd: block must be 64");
   if ((long long)N * d * 2 > 0xFFFFFFFFLL)
     return fail(BSA_EUNSUPPORTED, "attn_bwd: one head (N*d*2 bytes) must be below 4 GiB");
-  const int nb = (n_valid + 63) / 64;
-  if (kv_stride < 0 || (nb > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_bwd: bad kv_stride");
-  const size_t need = bsa_block_sparse_attn_bwd_workspace(B, H, N);
+  bsa::Blocks bq, bk;
+  if (int e = make_blocks(qb, block, n_valid, "attn_bwd query blocks", bq)) return e;
+  if (int e = make_blocks(kb, block, n_valid, "attn_bwd key blocks", bk)) return e;
+  if ((qb && bq.max_len == 0) || (kb && bk.max_len == 0))
+    return fail(BSA_EUNSUPPORTED, "attn_bwd: block descriptors need a length bound max_len in 1..64");
+  if (kv_stride < 0 || (bk.nblocks > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_bwd: bad kv_stride");
+  const size_t need = bsa::attn_bwd_workspace(B * H, N, bq.nblocks, bk.nblocks);
   if (ws == nullptr || ws_bytes < need)
     return fail(BSA_ENOSPC, "attn_bwd: workspace %zu bytes < %zu", ws_bytes, need);
   if (!aligned16(ws)) return fail(BSA_EINVAL, "attn_bwd: workspace must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return hip_status(bsa::launch_attn_bwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
-                                         static_cast<const uint16_t*>(dout), lse, B * H, N, d, n_valid, kv_count,
-                                         kv_index, kv_stride, sc, static_cast<uint16_t*>(dq),
+                                         static_cast<const uint16_t*>(dout), lse, B * H, N, d, n_valid, bq, bk,
+                                         kv_count, kv_index, kv_stride, sc, static_cast<uint16_t*>(dq),
                                          static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), ws, stream),
                     "attn_bwd");
 }

@@ -40,6 +40,7 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   int N, n_valid, nqb, nkb;
+  Blocks qb, kb;              // query / key blocks: uniform 64-token, or descriptors of at most 64 tokens
   const int32_t* kv_count;    // [BH][nqb] kept key blocks per query block
   const int32_t* kv_index;    // [BH][nqb][kv_stride]
   int kv_stride;
@@ -146,7 +147,9 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
 
   int bh, I;
   tile_of(L, a.nqb, BH, a.order_q, bh, I);
-  const int qs = 64 * I, ql = min(64, a.n_valid - qs);
+  int qs, ql;
+  a.qb.get(bh, I, qs, ql);
+  ql = min(ql, 64);
   if (ql <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,8 +189,8 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
   auto block_of = [&](int c, int& ks, int& kl) {   // chunk c of the list (clamped into range)
     int J = list[c < cnt ? c : cnt - 1];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;
-    ks = 64 * J;
-    kl = min(64, a.n_valid - ks);
+    a.kb.get(bh, J, ks, kl);
+    kl = min(max(kl, 0), 64);
   };
 
   // one chunk: loads of chunk c+1 (or a reload of c) into (Kn, Vn) go out
@@ -276,7 +279,9 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
 
   int bh, J;
   tile_of(L, a.nkb, BH, a.order_k, bh, J);
-  const int ks = 64 * J, kl = min(64, a.n_valid - ks);
+  int ks, kl;
+  a.kb.get(bh, J, ks, kl);
+  kl = min(kl, 64);
   if (kl <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,7 +320,9 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
   // fetches row l's lse and Dr into registers (wave 0 stores them to LDS)
   auto issue = [&](int c, lds_u8* Qn, lds_u8* Gn, float& lv, float& rv) {
     const int I = list[c < cnt ? c : cnt - 1];
-    const int qs = 64 * I, ql = min(64, a.n_valid - qs);
+    int qs, ql;
+    a.qb.get(bh, I, qs, ql);
+    ql = min(max(ql, 0), 64);
     const bool ok = lane < ql;
     lv = INFINITY;
     rv = 0.f;
@@ -454,16 +461,18 @@ __global__ __launch_bounds__(256) void bwd_zero_pad_kernel(uint4* dq, uint4* dk,
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const uint16_t* dout, const float* lse, int BH, int N, int d, int n_valid,
-                           const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+                           const Blocks& qb, const Blocks& kb, const int32_t* kv_count, const int32_t* kv_index,
+                           int kv_stride, float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
+                           hipStream_t s) {
   if (BH == 0) return hipSuccess;
-  const int nb = (n_valid + 63) / 64;
+  const int nqb = qb.nblocks, nkb = kb.nblocks;
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.N = N; a.n_valid = n_valid; a.nqb = nb; a.nkb = nb;
+  a.N = N; a.n_valid = n_valid; a.nqb = nqb; a.nkb = nkb;
+  a.qb = qb; a.kb = kb;
   a.kv_count = kv_count; a.kv_index = kv_index; a.kv_stride = kv_stride;
-  a.W = (nb + 31) / 32;
+  a.W = (nqb + 31) / 32;
   a.scale = scale;
   // workspace: Dr [BH][N] fp32 | q_count [BH][nkb] | q_index [BH][nkb][nqb] | bits [BH][nkb][W]
   char* p = static_cast<char*>(ws);
@@ -473,11 +482,11 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
     return r;
   };
   a.dr = reinterpret_cast<float*>(take(sizeof(float) * (size_t)BH * N));
-  a.q_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
-  a.q_index = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb * nb));
-  a.bits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)BH * nb * a.W));
-  int32_t* oq = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
-  int32_t* ok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nb));
+  a.q_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nkb));
+  a.q_index = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nkb * nqb));
+  a.bits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)BH * nkb * a.W));
+  int32_t* oq = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nqb));
+  int32_t* ok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nkb));
 
   if (n_valid < N) {
     const int cpr = d / 8;
@@ -487,35 +496,34 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
         reinterpret_cast<uint4*>(dq), reinterpret_cast<uint4*>(dk), reinterpret_cast<uint4*>(dv), N, n_valid, cpr,
         total);
   }
-  if (nb == 0) return hipGetLastError();
+  if (nqb == 0 || nkb == 0) return hipGetLastError();
   const size_t rows = (size_t)BH * N;
   const size_t lanes = rows * (d / 8);
   if (d == 128)
     bwd_dot_kernel<128><<<(int)((lanes + 255) / 256), 256, 0, s>>>(a, rows);
   else
     bwd_dot_kernel<64><<<(int)((lanes + 255) / 256), 256, 0, s>>>(a, rows);
-  const size_t nbits = (size_t)BH * nb * a.W;
+  const size_t nbits = (size_t)BH * nkb * a.W;
   csc_clear_kernel<<<(int)((nbits + 255) / 256 < 4096 ? (nbits + 255) / 256 : 4096), 256, 0, s>>>(a.bits, nbits);
-  const size_t lrows = (size_t)BH * nb;
-  csc_set_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
-  csc_list_kernel<<<(int)((lrows + 3) / 4), 256, 0, s>>>(a, lrows);
-  a.order_q = launch_qorder(kv_count, BH, nb, nb, oq, s) ? oq : nullptr;
-  a.order_k = launch_qorder(a.q_count, BH, nb, nb, ok, s) ? ok : nullptr;
-  const int tiles = (int)lrows;
-  const int nkv = (tiles + 7) & ~7;
+  const size_t qrows = (size_t)BH * nqb, kcols = (size_t)BH * nkb;
+  csc_set_kernel<<<(int)((qrows + 3) / 4), 256, 0, s>>>(a, qrows);
+  csc_list_kernel<<<(int)((kcols + 3) / 4), 256, 0, s>>>(a, kcols);
+  a.order_q = launch_qorder(kv_count, BH, nqb, nkb, oq, s) ? oq : nullptr;
+  a.order_k = launch_qorder(a.q_count, BH, nkb, nqb, ok, s) ? ok : nullptr;
+  const int nkv = ((int)kcols + 7) & ~7;
   if (d == 128)
-    bwd_grad_kernel<128><<<nkv + tiles, 256, 0, s>>>(a, BH, nkv);
+    bwd_grad_kernel<128><<<nkv + (int)qrows, 256, 0, s>>>(a, BH, nkv);
   else
-    bwd_grad_kernel<64><<<nkv + tiles, 256, 0, s>>>(a, BH, nkv);
+    bwd_grad_kernel<64><<<nkv + (int)qrows, 256, 0, s>>>(a, BH, nkv);
   return hipGetLastError();
 }
 
-size_t attn_bwd_workspace(int BH, int N, int nb) {
+size_t attn_bwd_workspace(int BH, int N, int nqb, int nkb) {
   auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  const size_t W = ((size_t)nb + 31) / 32;
-  return r(sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nb) +
-         r(sizeof(int32_t) * (size_t)BH * nb * nb) + r(sizeof(uint32_t) * (size_t)BH * nb * W) +
-         2 * r(sizeof(int32_t) * (size_t)BH * nb);
+  const size_t W = ((size_t)nqb + 31) / 32;
+  return r(sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nkb) +
+         r(sizeof(int32_t) * (size_t)BH * nkb * nqb) + r(sizeof(uint32_t) * (size_t)BH * nkb * W) +
+         r(sizeof(int32_t) * (size_t)BH * nqb) + r(sizeof(int32_t) * (size_t)BH * nkb);
 }
 
 }  // namespace bsa

@@ -120,9 +120,10 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float scale, int32_t* tile_ws, float* lse, hipStream_t s);
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const uint16_t* dout, const float* lse, int BH, int N, int d, int n_valid,
-                           const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
-size_t attn_bwd_workspace(int BH, int N, int nb);
+                           const Blocks& qb, const Blocks& kb, const int32_t* kv_count, const int32_t* kv_index,
+                           int kv_stride, float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
+                           hipStream_t s);
+size_t attn_bwd_workspace(int BH, int N, int nqb, int nkb);
 hipError_t launch_permute(const uint16_t* x, uint16_t* y, const int32_t* perm, int BH, int N,
                           int d, int per_head, bool inverse, hipStream_t s);
 hipError_t launch_tile_stats(const uint16_t* q, const uint16_t* k, const float* lse, int BH, int N, int d,

@@ -250,9 +250,12 @@ int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v,
                                   hipStream_t stream);
 
 /* Workspace bytes needed by bsa_block_sparse_attn_bwd: fp32 row terms
- * [B,H,N] plus the transposed block lists (int32 [B,H,nb] counts,
- * [B,H,nb,nb] ids, and a [B,H,nb,ceil(nb/32)] bit matrix; nb = ceil(N/64)). */
-size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N);
+ * [B,H,N] plus the transposed block lists (int32 [B,H,nkb] counts,
+ * [B,H,nkb,nqb] ids, a [B,H,nkb,ceil(nqb/32)] bit matrix) and two
+ * processing orders; nqb, nkb from the descriptors, ceil(N/64) for NULL. */
+size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N,
+                                           const bsa_blocks* qb,
+                                           const bsa_blocks* kb);
 
 /*
  * Block-sparse attention backward (NABLA summary, Contributi Chiave,
@@ -264,7 +267,10 @@ size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N);
  *   dS = P (dP - Dr),  dQ_I += scale dS K_J,  dK_J += scale dS^T Q_I,
  *   dV_J += P^T dO_I
  * MFMA bf16 products with fp32 accumulation; deterministic (no atomics on
- * the gradients). Uniform `block`-token blocks only (block = 64).
+ * the gradients). Blocks: uniform (qb / kb NULL, block = 64), or descriptors
+ * bounded to 64 tokens (max_len in 1..64: fractal patches, head-aware
+ * boxes) that cover [0, n_valid) once each (every valid token in exactly
+ * one query block and one key block; rows of no block are not written).
  *
  *   q, k, v, o, dout  bf16 [B,H,N,d] (device), d in {64, 128}; o is the
  *             forward's output
@@ -276,16 +282,19 @@ size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N);
  *   dq, dk, dv  bf16 [B,H,N,d] (device), fully written: rows n_valid..N-1,
  *             query rows with no kept key block and key rows no query block
  *             kept are zero
- *   ws        workspace of bsa_block_sparse_attn_bwd_workspace(B, H, N)
- *             bytes (device, 16-byte aligned; contents are overwritten)
+ *   qb, kb    query / key block descriptors as in the forward (NULL =
+ *             uniform); the lists index them
+ *   ws        workspace of bsa_block_sparse_attn_bwd_workspace(B, H, N, qb,
+ *             kb) bytes (device, 16-byte aligned; contents are overwritten)
  * All pointers 16-byte aligned. Errors: BSA_EINVAL (null or misaligned
- * pointers, bad kv_stride), BSA_EUNSUPPORTED (d, block, 4 GiB head limit),
- * BSA_ENOSPC (workspace).
+ * pointers, bad kv_stride), BSA_EUNSUPPORTED (d, block, descriptors without
+ * a length bound, 4 GiB head limit), BSA_ENOSPC (workspace).
  */
 int bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v,
                               const void* o, const void* dout,
                               const float* lse, int B, int H, int N, int d,
-                              int n_valid, int block, const int32_t* kv_count,
+                              int n_valid, int block, const bsa_blocks* qb,
+                              const bsa_blocks* kb, const int32_t* kv_count,
                               const int32_t* kv_index, int kv_stride,
                               float scale, void* dq, void* dk, void* dv,
                               void* ws, size_t ws_bytes, hipStream_t stream);

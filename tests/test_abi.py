@@ -89,13 +89,18 @@ def test_argument_validation_newer_entry_points(lib):
     assert lib.bsa_block_sparse_attn_fwd_lse(P, P, P, P, None, 1, 1, 128, 64, 128, 64, None, None, P, P, 2,
                                              0.0, P, 1 << 20, None) == 1
     # backward: uniform 64-token blocks only, pointers, workspace
-    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 32, P, P, 2, 0.0, P, P, P, P,
-                                         1 << 30, None) == 2
-    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, None, P, 1, 1, 128, 64, 128, 64, P, P, 2, 0.0, P, P, P, P,
-                                         1 << 30, None) == 1
-    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 64, P, P, 2, 0.0, P, P, P, P,
-                                         16, None) == 3
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 32, None, None, P, P, 2, 0.0, P, P,
+                                         P, P, 1 << 30, None) == 2
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, None, P, 1, 1, 128, 64, 128, 64, None, None, P, P, 2, 0.0, P,
+                                         P, P, P, 1 << 30, None) == 1
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 64, None, None, P, P, 2, 0.0, P, P,
+                                         P, P, 16, None) == 3
     assert "workspace" in _err(lib)
+    # block descriptors without a length bound are refused
+    blk = bsa._Blocks(2, 0, 16, 16, 0)
+    assert lib.bsa_block_sparse_attn_bwd(P, P, P, P, P, P, 1, 1, 128, 64, 128, 64, ctypes.byref(blk),
+                                         ctypes.byref(blk), P, P, 2, 0.0, P, P, P, P, 1 << 30, None) == 2
+    assert "max_len" in _err(lib)
     # warm-started k-means: rounds, tolerance, the move counts are required
     assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 0, 0, P, P, P, P, P, 1 << 30, None) == 1
     assert lib.bsa_kmeans_warm(P, 1, 1, 128, 64, 128, 8, 5, -1, P, P, P, P, P, 1 << 30, None) == 1

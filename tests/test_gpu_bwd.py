@@ -203,3 +203,107 @@ def test_bwd_hunyuan720_sampled(gpu_lib):
         krows = np.arange(st[J], st[J] + ln[J])
         _check_grad(dk, rk, krows, f"dk (key block {J}, {len(users)} query blocks)")
         _check_grad(dv, rv, krows, f"dv (key block {J})")
+
+
+def _short_partition(rng, n, lens=(0, 1, 7, 17, 33, 48, 64, 64, 64)):
+    st, ln, pos = [], [], 0
+    while pos < n:
+        L = int(min(rng.choice(lens), n - pos))
+        st.append(pos)
+        ln.append(L)
+        pos += L
+    return np.array(st, np.int32), np.array(ln, np.int32)
+
+
+@pytest.mark.parametrize("H,N,nv,d", [(2, 704, 650, 128), (2, 320, 300, 64)])
+def test_bwd_bounded_blocks_random(gpu_lib, H, N, nv, d):
+    # query and key blocks of at most 64 tokens (empty, ragged and full ones)
+    # that partition the valid tokens, per head
+    bsa = gpu_lib
+    say(f"backward over bounded blocks H={H} N={N} n_valid={nv} d={d}")
+    rng = np.random.default_rng(N * 3 + d)
+    x = rng.normal(size=(4, 1, H, N, d)).astype(np.float32)
+    x[:, :, :, nv:] = 0
+    q, k, v, do = (torch.from_numpy(x[i] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16) for i in range(4))
+    parts_q = [_short_partition(rng, nv) for _ in range(H)]
+    parts_k = [_short_partition(rng, nv) for _ in range(H)]
+    nqb, nkb = max(len(p[0]) for p in parts_q), max(len(p[0]) for p in parts_k)
+
+    def pad(parts, nb):
+        st = np.full((H, nb), nv, np.int32)
+        ln = np.zeros((H, nb), np.int32)
+        for h, (s_, l_) in enumerate(parts):
+            st[h, :len(s_)], ln[h, :len(l_)] = s_, l_
+        return st, ln
+
+    qst, qln = pad(parts_q, nqb)
+    kst, kln = pad(parts_k, nkb)
+    keep = rng.random((H, nqb, nkb)) < 0.3
+    keep[:, :, 0] |= ~keep.any(2)
+    cnt = keep.sum(2).astype(np.int32)
+    idx = np.full((H, nqb, nkb), -1, np.int32)
+    for h in range(H):
+        for i in range(nqb):
+            ids = np.nonzero(keep[h, i])[0]
+            idx[h, i, :len(ids)] = ids
+    qb = bsa.Blocks(torch.from_numpy(qst[None]).cuda(), torch.from_numpy(qln[None]).cuda(), 64)
+    kb = bsa.Blocks(torch.from_numpy(kst[None]).cuda(), torch.from_numpy(kln[None]).cuda(), 64)
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    cd, id_ = torch.from_numpy(cnt[None]).cuda(), torch.from_numpy(idx[None]).cuda()
+    o, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cd, id_, n_valid=nv, qb=qb, kb=kb)
+    dq, dk, dv = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv, qb=qb, kb=kb)
+    dq2, dk2, dv2 = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv, qb=qb, kb=kb)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    lse_g, dq, dk, dv = (_np(t)[0] for t in (lse, dq, dk, dv))
+    rows = np.arange(nv)
+    for h in range(H):
+        args = [_np(t[0, h]) for t in (q, k, v, do)]
+        ref_l = oa.masked_attention_lse(args[0], args[1], qst[h], qln[h], kst[h], kln[h], keep[h])
+        fin = np.isfinite(ref_l[rows])
+        assert np.array_equal(np.isfinite(lse_g[h][rows]), fin)
+        assert np.abs(lse_g[h][rows][fin] - ref_l[rows][fin]).max() <= LSE_ABS
+        rq, rk, rv = oa.masked_attention_bwd(*args, qst[h], qln[h], kst[h], kln[h], keep[h])
+        _check_grad(dq[h], rq, rows, f"head {h} dq")
+        _check_grad(dk[h], rk, rows, f"head {h} dk")
+        _check_grad(dv[h], rv, rows, f"head {h} dv")
+    for t in (dq, dk, dv):
+        assert (t[:, nv:] == 0).all()
+
+
+def test_bwd_fractal_patches_wan480_sampled(gpu_lib):
+    # the hybrid layout: fractal patches (588 blocks of 24..64 tokens), the CDF
+    # mask OR the sliding-tile window, on the permuted 480p layer
+    import block_sparse_attention_avg_amd.pipelines as pl
+    bsa = gpu_lib
+    w = WORKLOADS["wan480_fractal_sta"]
+    q, k, v = generate(w, heads=[0, 5])
+    nv = w.n_valid
+    say("backward over fractal patches, 480p layer, sampled blocks")
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16)
+    do[:, :, nv:] = 0
+    lay = pl.fractal_layout(w.T, w.Hl, w.Wl, w.patch, w.N, "cuda")
+    qp, kp, vp, gp = (bsa.permute_tokens(t.cuda(), lay.perm) for t in (q, k, v, do))
+    cnt, idx = bsa.build_block_mask(qp, kp, w.thr, window=(*lay.grid, *w.window), n_valid=nv,
+                                    qb=lay.blocks, kb=lay.blocks)
+    o, lse = bsa.block_sparse_attn_fwd_lse(qp, kp, vp, cnt, idx, n_valid=nv, qb=lay.blocks, kb=lay.blocks)
+    dq, dk, dv = bsa.block_sparse_attn_bwd(qp, kp, vp, o, gp, lse, cnt, idx, n_valid=nv, qb=lay.blocks,
+                                           kb=lay.blocks)
+    torch.cuda.synchronize()
+    perm, st, ln, _ = ol.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
+    nb = len(st)
+    cnt, idx = cnt.cpu().numpy()[0], idx.cpu().numpy()[0]
+    dq, dk, dv = (_np(t)[0] for t in (dq, dk, dv))
+    rng = np.random.default_rng(12)
+    for h in range(2):
+        keep = keep_from_lists(cnt[h], idx[h], nb)
+        args = [_np(t[0, h])[perm] for t in (q, k, v, do)]
+        qi = sorted(set(rng.choice(nb, 3, replace=False).tolist()) | {nb - 1})
+        rq, _, _ = oa.masked_attention_bwd(*args, st[qi], ln[qi], st, ln, keep[qi])
+        rows = np.concatenate([np.arange(st[i], st[i] + ln[i]) for i in qi])
+        _check_grad(dq[h], rq, rows, f"head {h} dq (patches {qi})")
+        J = int(np.argmin(ln))                       # a short edge patch
+        users = np.nonzero(keep[:, J])[0]
+        _, rk, rv = oa.masked_attention_bwd(*args, st[users], ln[users], st, ln, keep[users])
+        krows = np.arange(st[J], st[J] + ln[J])
+        _check_grad(dk[h], rk, krows, f"head {h} dk (patch {J} of {ln[J]} tokens, {len(users)} query patches)")
+        _check_grad(dv[h], rv, krows, f"head {h} dv (patch {J})")
