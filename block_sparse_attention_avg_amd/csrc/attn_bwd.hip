@@ -65,6 +65,19 @@ __device__ __forceinline__ void tile_of(int L, int n, int BH, const int32_t* ord
   t = order ? ((const __attribute__((address_space(4))) int32_t*)order)[(size_t)bh * n + pos] : pos;
 }
 
+// Block i of head bh: uniform 64-token blocks (geometry known at compile
+// time) or a descriptor bounded to 64 tokens.
+template <bool DESC>
+__device__ __forceinline__ void block_at(const Blocks& b, int bh, int i, int n_valid, int& s, int& n) {
+  if constexpr (DESC) {
+    b.get(bh, i, s, n);
+    n = min(max(n, 0), 64);
+  } else {
+    s = 64 * i;
+    n = min(64, n_valid - s);
+  }
+}
+
 // Dr[row] = sum_c dO[row, c] O[row, c] (fp32), 0 on pad rows.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a, size_t rows) {
@@ -139,7 +152,7 @@ __global__ __launch_bounds__(256) void csc_list_kernel(BwdArgs a, size_t cols) {
 //   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)   (lane-local)
 //   dQ^T += K^T dS^T                (K^T through the transpose read)
 // The two key halves' partial dQ^T meet in LDS at the end (fixed order).
-template <int D>
+template <int D, bool DESC>
 __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, unsigned char* K0, unsigned char* V0,
                                             unsigned char* K1, unsigned char* V1) {
   using T = Tile<D, 4>;
@@ -148,8 +161,7 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
   int bh, I;
   tile_of(L, a.nqb, BH, a.order_q, bh, I);
   int qs, ql;
-  a.qb.get(bh, I, qs, ql);
-  ql = min(ql, 64);
+  block_at<DESC>(a.qb, bh, I, a.n_valid, qs, ql);
   if (ql <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,8 +201,7 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
   auto block_of = [&](int c, int& ks, int& kl) {   // chunk c of the list (clamped into range)
     int J = list[c < cnt ? c : cnt - 1];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;
-    a.kb.get(bh, J, ks, kl);
-    kl = min(max(kl, 0), 64);
+    block_at<DESC>(a.kb, bh, J, a.n_valid, ks, kl);
   };
 
   // one chunk: loads of chunk c+1 (or a reload of c) into (Kn, Vn) go out
@@ -270,7 +281,7 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
 //   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)
 //   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through the transpose read)
 // The two query halves' partial dK^T, dV^T meet in LDS at the end (fixed order).
-template <int D>
+template <int D, bool DESC>
 __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, unsigned char* Q0, unsigned char* G0,
                                               unsigned char* Q1, unsigned char* G1, float* L0, float* R0, float* L1,
                                               float* R1) {
@@ -280,8 +291,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
   int bh, J;
   tile_of(L, a.nkb, BH, a.order_k, bh, J);
   int ks, kl;
-  a.kb.get(bh, J, ks, kl);
-  kl = min(kl, 64);
+  block_at<DESC>(a.kb, bh, J, a.n_valid, ks, kl);
   if (kl <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -321,8 +331,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
   auto issue = [&](int c, lds_u8* Qn, lds_u8* Gn, float& lv, float& rv) {
     const int I = list[c < cnt ? c : cnt - 1];
     int qs, ql;
-    a.qb.get(bh, I, qs, ql);
-    ql = min(max(ql, 0), 64);
+    block_at<DESC>(a.qb, bh, I, a.n_valid, qs, ql);
     const bool ok = lane < ql;
     lv = INFINITY;
     rv = 0.f;
@@ -429,7 +438,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
 // in as the key tiles drain. nkv is the key-tile count rounded up to a
 // multiple of 8, so each part keeps its own per-XCD ranges; the LDS buffers
 // are shared by the two roles.
-template <int D>
+template <int D, bool DESC>
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a, int BH, int nkv) {
   __shared__ __align__(16) unsigned char B0[Tile<D>::BYTES];
   __shared__ __align__(16) unsigned char B1[Tile<D>::BYTES];
@@ -442,9 +451,9 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a, int BH, int
   const int G = blockIdx.x;
   if (G < nkv) {
     if (G >= BH * a.nkb) return;                  // padding of the key-tile range
-    bwd_dkdv_tile<D>(a, G, BH, B0, B1, B2, B3, L0, R0, L1, R1);
+    bwd_dkdv_tile<D, DESC>(a, G, BH, B0, B1, B2, B3, L0, R0, L1, R1);
   } else {
-    bwd_dq_tile<D>(a, G - nkv, BH, B0, B1, B2, B3);
+    bwd_dq_tile<D, DESC>(a, G - nkv, BH, B0, B1, B2, B3);
   }
 }
 
@@ -511,10 +520,15 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.order_q = launch_qorder(kv_count, BH, nqb, nkb, oq, s) ? oq : nullptr;
   a.order_k = launch_qorder(a.q_count, BH, nkb, nqb, ok, s) ? ok : nullptr;
   const int nkv = ((int)kcols + 7) & ~7;
-  if (d == 128)
-    bwd_grad_kernel<128><<<nkv + (int)qrows, 256, 0, s>>>(a, BH, nkv);
-  else
-    bwd_grad_kernel<64><<<nkv + (int)qrows, 256, 0, s>>>(a, BH, nkv);
+  const int grid = nkv + (int)qrows;
+  const bool desc = qb.start != nullptr || kb.start != nullptr;
+  if (d == 128) {
+    if (desc) bwd_grad_kernel<128, true><<<grid, 256, 0, s>>>(a, BH, nkv);
+    else bwd_grad_kernel<128, false><<<grid, 256, 0, s>>>(a, BH, nkv);
+  } else {
+    if (desc) bwd_grad_kernel<64, true><<<grid, 256, 0, s>>>(a, BH, nkv);
+    else bwd_grad_kernel<64, false><<<grid, 256, 0, s>>>(a, BH, nkv);
+  }
   return hipGetLastError();
 }
 
