@@ -15,6 +15,16 @@ mask stage), then the block-sparse attention forward. Prints ONE JSON line.
   cpu_baseline  the float64 CPU reference timed on a bounded sample of the
              same workload and extrapolated to one step
 
+Beside the step, on the same inputs (each switchable off):
+  backward   forward with row normalisers + dQ/dK/dV over the step's lists
+  paths      the reorder-based layouts on the 480p layer (fractal patches +
+             window with its backward, per-head box tilings, semantic
+             clusters), mask reuse and warm-started k-means at a drifted next
+             step, and the mask's recall against the full attention
+  cold_cache the step with Q, K, V flushed from the caches
+  mfma_probe / dense_gemm_ref  what the MFMA pipe and the vendor GEMM reach
+             on the same box (context for the roofline fraction)
+
 A second workload (the 118,800-token 720p layer) is measured after the main
 one and reported under "also", with its mask-stage / attention time ratio.
 """
