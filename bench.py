@@ -771,6 +771,11 @@ def main():
             "mask_gbs": round(s2["mask_gbs"], 1),
             "sparsity_blocks": round(s2["sparsity_blocks"], 4),
         }}
+        if a.bwd_steps > 0:
+            tf2, tb2 = r2.backward(max(2, a.bwd_steps // 10), warmup=1)
+            fb2 = 2.5 * s2["flops_eff"]
+            line["also"][w2.key]["backward"] = {"ms": round(tb2, 3), "tflops_eff": round(fb2 / (tb2 * 1e-3) / 1e12, 3),
+                                                "fwd_with_lse_ms": round(tf2, 3)}
     print(json.dumps(line), flush=True)
 
 
