@@ -20,15 +20,15 @@
 // the clustering is a fixed point and the result is bit-identical to running
 // the remaining rounds.
 //
-// Lloyd rounds: assignment computes fp32 squared distances (centroids are
-// wave-uniform, so they are read through scalar loads; even and odd channels
-// summed separately, two centroids at a time, for independent FMA chains); the update is a
+// Lloyd rounds: assignment on the matrix cores (the nearest centroid by
+// |c|^2 - 2 x.c, x.c from an exact three-way bf16 split of the centroids,
+// see assign_kernel); the update is a
 // stable counting sort by cluster (per-chunk histograms, a per-head scan, an
 // in-chunk stable rank) followed by a per-cluster mean over the cluster's
 // tokens in ascending token order. Every reduction has a fixed order, so
 // results are bit-reproducible. The same sort produces the
 // cluster-contiguous permutation.
-#include "common.h"
+#include "mfma_tile.h"
 
 #include <math.h>
 
@@ -60,15 +60,15 @@ __device__ __forceinline__ float load_x(const uint16_t* row, int dd) {
   return __uint_as_float((uint32_t)row[dd] << 16);
 }
 
-// Fixed-order block sum over 256 threads (result valid in thread 0).
+// Fixed-order block sum over 256 threads (result valid in thread 0): a
+// butterfly inside each wave (every lane ends with the same sum), then the
+// four wave totals in wave order.
 __device__ float block_sum_256(float v, float* red) {
-  red[threadIdx.x] = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  const float r = red[0];
+  const float r = ((red[0] + red[1]) + red[2]) + red[3];
   __syncthreads();
   return r;
 }
@@ -142,9 +142,12 @@ __device__ int kpp_draw(const float* pp, const float* d2p, int nchunk, int n, fl
                         float* fsh) {
   const int t = threadIdx.x;
   float total = 0.f;
+  ScanOut first{0.f, 0.f, 0.f};                    // the first 256 partials' scan, reused below
   for (int c0 = 0; c0 < nchunk; c0 += 256) {
     const int c = c0 + t;
-    total += block_scan_256(c < nchunk ? pp[c] : 0.f, buf).seg;
+    const ScanOut sc = block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
+    if (c0 == 0) first = sc;
+    total += sc.seg;
   }
   if (!(total > 0.f)) return min((int)floor((double)u * (double)n), n - 1);
   const float target = u * total;
@@ -153,7 +156,7 @@ __device__ int kpp_draw(const float* pp, const float* d2p, int nchunk, int n, fl
   float before = 0.f, carry = 0.f;
   for (int c0 = 0; c0 < nchunk; c0 += 256) {
     const int c = c0 + t;
-    const ScanOut sc = block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
+    const ScanOut sc = c0 == 0 ? first : block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
     if (t == 0) flag[0] = 256;
     __syncthreads();
     if (c < nchunk && carry + sc.incl > target) atomicMin(&flag[0], t);
@@ -220,60 +223,139 @@ __global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restri
   kpp_update<D>(xh, n, cidx, d2p, d2n, pn, r == 0, red);
 }
 
+// Assignment on the matrix cores. The nearest centroid minimises
+// |c|^2 - 2 x.c (|x|^2 is common to all centroids). Tokens are bf16, so each
+// x.c is computed exactly up to fp32 accumulation from a three-way bf16 split
+// c = c1 + c2 + c3 of the fp32 centroid (each remainder is exact in fp32 and
+// the last fits bf16): three bf16 MFMA 32x32x16 products into one fp32
+// accumulator, smallest part first.
+//
+// A workgroup of 4 waves owns 256 tokens, 64 per wave as two 32-token groups
+// whose rows stay in registers as the B operand. Centroids go through LDS in
+// chunks of 32: the workgroup reads the fp32 rows, splits them, stores the
+// three bf16 parts in swizzled 32-row tiles and |c|^2 (fixed-order sums, the
+// same in every workgroup); the parts are the A operand, shared by both
+// token groups. A lane holds 16 centroid scores of one token; it keeps the
+// first minimum in centroid order, and the two lane halves merge at the end
+// (equal scores go to the lower index).
 template <int D>
 __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict__ x, int N, int n,
                                                      int C, const float* __restrict__ cent,
                                                      int32_t* __restrict__ assign, Stop stop,
                                                      int32_t* __restrict__ changes) {
+  constexpr int ROWB = D * 2, PART = 32 * ROWB;
+  constexpr int CPT = D / 8;                       // channels per thread in the chunk load
+  __shared__ __align__(16) unsigned char parts[3 * PART];
+  __shared__ __align__(16) float nrm[32];
   const int bh = blockIdx.y;
   if (stop(bh)) return;
-  const int i = blockIdx.x * kChunk + threadIdx.x;
-  if (i >= N) return;
-  if (i >= n) {
-    assign[(size_t)bh * N + i] = -1;
-    return;
-  }
-  const uint16_t* xr = x + ((size_t)bh * N + i) * D;
-  float xv[D];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tok0 = blockIdx.x * kChunk + 64 * wave;
+
+  bf16x8 xf[2][D / 16];
 #pragma unroll
-  for (int c8 = 0; c8 < D / 8; ++c8) {
-    const uint4 w = *reinterpret_cast<const uint4*>(xr + 8 * c8);
-    xv[8 * c8 + 0] = bf16_lo(w.x); xv[8 * c8 + 1] = bf16_hi(w.x);
-    xv[8 * c8 + 2] = bf16_lo(w.y); xv[8 * c8 + 3] = bf16_hi(w.y);
-    xv[8 * c8 + 4] = bf16_lo(w.z); xv[8 * c8 + 5] = bf16_hi(w.z);
-    xv[8 * c8 + 6] = bf16_lo(w.w); xv[8 * c8 + 7] = bf16_hi(w.w);
+  for (int g = 0; g < 2; ++g) {
+    const int i = tok0 + 32 * g + l32;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      xf[g][c] = i < n ? *reinterpret_cast<const bf16x8*>(x + ((size_t)bh * N + i) * D + 16 * c + 8 * half)
+                       : bf16x8{};
   }
+
+  // chunk loader: thread t takes centroid row t / 8, channels CPT * (t % 8) ..
+  const int lr = tid >> 3, ls = tid & 7;
   const float* cb = cent + (size_t)bh * C * D;
-  float best = INFINITY;
-  int bi = 0;
-  // two centroids per step, each over even and odd channels: four independent
-  // FMA chains; the distance is (even + odd), compared in centroid order
-  auto dist = [&](const float* cr, float& ea, float& oa) {
+  float cv[CPT];
+  auto fetch = [&](int c0) {
+    const bool ok = c0 + lr < C;
+    const float4* src = reinterpret_cast<const float4*>(cb + (size_t)(ok ? c0 + lr : 0) * D + CPT * ls);
 #pragma unroll
-    for (int dd = 0; dd < D; dd += 2) {
-      const float t0 = xv[dd] - cr[dd], t1 = xv[dd + 1] - cr[dd + 1];
-      ea = fmaf(t0, t0, ea);
-      oa = fmaf(t1, t1, oa);
+    for (int j = 0; j < CPT / 4; ++j) {
+      const float4 w = ok ? src[j] : float4{0.f, 0.f, 0.f, 0.f};
+      cv[4 * j + 0] = w.x; cv[4 * j + 1] = w.y; cv[4 * j + 2] = w.z; cv[4 * j + 3] = w.w;
     }
   };
-  int c = 0;
-  for (; c + 1 < C; c += 2) {
-    float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
-    dist(cb + (size_t)c * D, e0, o0);
-    dist(cb + (size_t)(c + 1) * D, e1, o1);
-    const float a0 = e0 + o0, a1 = e1 + o1;
-    if (a0 < best) { best = a0; bi = c; }
-    if (a1 < best) { best = a1; bi = c + 1; }
+  auto stage = [&](int c0) {
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) sq = fmaf(cv[j], cv[j], sq);
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    sq += __shfl_xor(sq, 4);
+    if (ls == 0) nrm[lr] = c0 + lr < C ? sq : INFINITY;
+#pragma unroll
+    for (int pc = 0; pc < CPT / 8; ++pc) {
+      u32x4 w[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float r0 = cv[8 * pc + 2 * e], r1 = cv[8 * pc + 2 * e + 1];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const uint32_t b = pack2(r0, r1);
+          w[p][e] = b;
+          r0 -= __uint_as_float(b << 16);
+          r1 -= __uint_as_float(b & 0xffff0000u);
+        }
+      }
+      const int piece = (CPT / 8) * ls + pc;
+      const int off = lr * ROWB + ((piece ^ swz<D>(lr & 15)) << 4);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((lds_u8*)parts + p * PART + off) = w[p];
+    }
+  };
+
+  float best[2] = {INFINITY, INFINITY};
+  int bi[2] = {0, 0};
+  fetch(0);
+  for (int c0 = 0; c0 < C; c0 += 32) {
+    __syncthreads();                               // the previous chunk's reads are done
+    stage(c0);
+    __syncthreads();
+    if (c0 + 32 < C) fetch(c0 + 32);
+    f32x16 acc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+#pragma unroll
+    for (int p = 2; p >= 0; --p)
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 a = row_read<D>((const lds_u8*)parts + p * PART, 0, c, l32, half);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[g][c], acc[g], 0, 0, 0);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 nr = *reinterpret_cast<const float4*>(nrm + 8 * j + 4 * half);
+      const float nv[4] = {nr.x, nr.y, nr.z, nr.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float sc = fmaf(-2.f, acc[g][4 * j + e], nv[e]);
+          if (sc < best[g]) { best[g] = sc; bi[g] = c0 + 8 * j + 4 * half + e; }
+        }
+    }
   }
-  if (c < C) {
-    float e0 = 0.f, o0 = 0.f;
-    dist(cb + (size_t)c * D, e0, o0);
-    if (e0 + o0 < best) { best = e0 + o0; bi = c; }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float ob = __shfl_xor(best[g], 32);
+    const int oi = __shfl_xor(bi[g], 32);
+    if (ob < best[g] || (ob == best[g] && oi < bi[g])) bi[g] = oi;
+    const int i = tok0 + 32 * g + l32;
+    if (half == 0 && i < N) {
+      int32_t* dst = assign + (size_t)bh * N + i;
+      if (i >= n) {
+        *dst = -1;
+        continue;
+      }
+      // rounds after the first count the tokens that moved
+      if (changes && stop.it >= 1 && *dst != bi[g]) atomicAdd(&changes[(size_t)bh * stop.iters + stop.it], 1);
+      *dst = bi[g];
+    }
   }
-  // rounds after the first count the tokens that moved
-  if (changes && stop.it >= 1 && assign[(size_t)bh * N + i] != bi)
-    atomicAdd(&changes[(size_t)bh * stop.iters + stop.it], 1);
-  assign[(size_t)bh * N + i] = bi;
 }
 
 // changes[bh][0] = n (no earlier round to compare with), the rest 0.
@@ -300,38 +382,52 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ a
 
 // Per head: running offsets over chunks for every cluster, cluster sizes and
 // starts; off[bh][chunk][c] becomes the first output slot of chunk's members.
+// Thread c walks cluster c's column in batches of 16 loads (so their
+// latencies overlap); the starts are an exclusive scan of the sizes over the
+// workgroup (integer sums: exact in any order).
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ off, int nchunk, int C,
                                                     int32_t* __restrict__ start,
                                                     int32_t* __restrict__ size, Stop stop) {
-  __shared__ int sz[1024];
+  constexpr int kB = 16;
+  __shared__ int wsum[16];
   const int bh = blockIdx.x;
   if (stop(bh)) return;
-  const int c = threadIdx.x;
+  const int c = threadIdx.x, lane = c & 63, w = c >> 6;
   int32_t* o = off + (size_t)bh * nchunk * C;
   int run = 0;
-  if (c < C) {
-    for (int ch = 0; ch < nchunk; ++ch) {
-      const int t = o[(size_t)ch * C + c];
-      o[(size_t)ch * C + c] = run;
-      run += t;
+  if (c < C)
+    for (int ch0 = 0; ch0 < nchunk; ch0 += kB) {
+      int t[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) t[j] = ch0 + j < nchunk ? o[(size_t)(ch0 + j) * C + c] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) run += t[j];
     }
+  int incl = c < C ? run : 0;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
   }
-  sz[c] = c < C ? run : 0;
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  if (c == 0) {
-    int acc = 0;
-    for (int j = 0; j < C; ++j) {
-      const int v = sz[j];
-      sz[j] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
+  int st = incl - (c < C ? run : 0);
+  for (int j = 0; j < w; ++j) st += wsum[j];
   if (c < C) {
-    const int st = sz[c];
     start[(size_t)bh * C + c] = st;
     size[(size_t)bh * C + c] = run;
-    for (int ch = 0; ch < nchunk; ++ch) o[(size_t)ch * C + c] += st;
+    int acc = st;
+    for (int ch0 = 0; ch0 < nchunk; ch0 += kB) {
+      int t[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) t[j] = ch0 + j < nchunk ? o[(size_t)(ch0 + j) * C + c] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (ch0 + j < nchunk) {
+          o[(size_t)(ch0 + j) * C + c] = acc;
+          acc += t[j];
+        }
+    }
   }
 }
 
@@ -359,35 +455,49 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // Cluster means: token p of a cluster (ascending token order) goes to group
-// p % G, groups are combined in a fixed order.
+// p % G; each group reads its tokens' rows in 16-byte pieces (D / 8 threads
+// per row), and the groups are combined in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void mean_kernel(const uint16_t* __restrict__ x, int N, int C,
                                                    const int32_t* __restrict__ order,
                                                    const int32_t* __restrict__ start,
                                                    const int32_t* __restrict__ size,
                                                    float* __restrict__ cent, Stop stop) {
-  constexpr int G = 256 / D;   // token groups
+  constexpr int TPR = D / 8;     // threads per token row
+  constexpr int G = 256 / TPR;   // token groups
   __shared__ float red[G][D];
   const int bh = blockIdx.y, c = blockIdx.x;
   if (stop(bh)) return;
   const int sz = size[(size_t)bh * C + c];
   if (sz == 0) return;   // empty cluster keeps its centroid
   const int st = start[(size_t)bh * C + c];
-  const int dd = threadIdx.x % D, g = threadIdx.x / D;
+  const int pc = threadIdx.x % TPR, g = threadIdx.x / TPR;
   const int32_t* ord = order + (size_t)bh * N + st;
-  const uint16_t* xh = x + (size_t)bh * N * D;
-  float acc = 0.f;
+  const uint16_t* xh = x + (size_t)bh * N * D + 8 * pc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const uint4& w) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_lo(ws[e]);
+      acc[2 * e + 1] += bf16_hi(ws[e]);
+    }
+  };
   int p = g;
   for (; p + 3 * G < sz; p += 4 * G) {
     const int i0 = ord[p], i1 = ord[p + G], i2 = ord[p + 2 * G], i3 = ord[p + 3 * G];
-    const float a0 = load_x(xh + (size_t)i0 * D, dd), a1 = load_x(xh + (size_t)i1 * D, dd);
-    const float a2 = load_x(xh + (size_t)i2 * D, dd), a3 = load_x(xh + (size_t)i3 * D, dd);
-    acc += a0; acc += a1; acc += a2; acc += a3;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(xh + (size_t)i0 * D);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(xh + (size_t)i1 * D);
+    const uint4 w2 = *reinterpret_cast<const uint4*>(xh + (size_t)i2 * D);
+    const uint4 w3 = *reinterpret_cast<const uint4*>(xh + (size_t)i3 * D);
+    add(w0); add(w1); add(w2); add(w3);
   }
-  for (; p < sz; p += G) acc += load_x(xh + (size_t)ord[p] * D, dd);
-  red[g][dd] = acc;
+  for (; p < sz; p += G) add(*reinterpret_cast<const uint4*>(xh + (size_t)ord[p] * D));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[g][8 * pc + e] = acc[e];
   __syncthreads();
-  if (g == 0) {
+  if (threadIdx.x < D) {
+    const int dd = threadIdx.x;
     float s = red[0][dd];
     for (int k = 1; k < G; ++k) s += red[k][dd];
     cent[((size_t)bh * C + c) * D + dd] = s / (float)sz;
