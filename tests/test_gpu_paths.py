@@ -206,6 +206,40 @@ def _d2(x, c):
     return ok.sq_dists(x, c)
 
 
+def _check_seeding(xh, cent_h, uh, n):
+    """Every seed is a token vector drawn by the D^2 inverse-CDF rule."""
+    d2 = None
+    for r in range(cent_h.shape[0]):
+        hits = np.nonzero((xh == cent_h[r]).all(1))[0]
+        assert len(hits) >= 1, r
+        if r == 0:
+            assert min(int(np.floor(uh[0] * n)), n - 1) in hits
+            d2 = ((xh - cent_h[0]) ** 2).sum(1)
+            continue
+        cs = np.cumsum(d2)
+        target = uh[r] * cs[-1]
+        tol = 1e-5 * cs[-1]
+        ok_idx = [i for i in hits if cs[i] - d2[i] <= target + tol and cs[i] >= target - tol]
+        assert ok_idx, r
+        d2 = np.minimum(d2, ((xh - cent_h[r]) ** 2).sum(1))
+
+
+def _check_lloyd(xh, prev_h, cent_h, a_h, s_h):
+    """The assignment is nearest w.r.t. the previous centroids (fp32 ties
+    allowed), sizes count it, and centroids are their members' means."""
+    C = cent_h.shape[0]
+    assert np.array_equal(np.bincount(a_h, minlength=C), s_h)
+    D = _d2(xh, prev_h)
+    mine = D[np.arange(len(a_h)), a_h]
+    assert (mine <= D.min(1) * (1 + 2e-5) + 1e-3).all()
+    for c in range(C):
+        if s_h[c]:
+            ref = xh[a_h == c].mean(0)
+            np.testing.assert_allclose(cent_h[c], ref, rtol=1e-5, atol=1e-4 * np.abs(ref).max())
+        else:
+            np.testing.assert_array_equal(cent_h[c], prev_h[c])
+
+
 @pytest.mark.parametrize("which", ["q", "k"])
 def test_kmeans_seeding_rule(gpu_lib, which):
     bsa = gpu_lib
@@ -215,23 +249,36 @@ def test_kmeans_seeding_rule(gpu_lib, which):
     cent, a, sizes = bsa.kmeans(x.cuda(), C, 0, u.cuda(), n_valid=w.n_valid)
     cent = cent.cpu().numpy().astype(np.float64)
     for h in (0, 9):
-        xh = _np(x[0, h])[:w.n_valid]
-        uh = u[0, h].numpy().astype(np.float64)
-        # every seed is a token vector; recover it and check the D^2 draw
-        d2 = None
-        for r in range(C):
-            hits = np.nonzero((xh == cent[0, h, r]).all(1))[0]
-            assert len(hits) >= 1, (h, r)
-            if r == 0:
-                assert min(int(np.floor(uh[0] * w.n_valid)), w.n_valid - 1) in hits
-                d2 = ((xh - cent[0, h, 0]) ** 2).sum(1)
-                continue
-            cs = np.cumsum(d2)
-            target = uh[r] * cs[-1]
-            tol = 1e-5 * cs[-1]
-            ok_idx = [i for i in hits if cs[i] - d2[i] <= target + tol and cs[i] >= target - tol]
-            assert ok_idx, (h, r)
-            d2 = np.minimum(d2, ((xh - cent[0, h, r]) ** 2).sum(1))
+        _check_seeding(_np(x[0, h])[:w.n_valid], cent[0, h], u[0, h].numpy().astype(np.float64), w.n_valid)
+
+
+@pytest.mark.parametrize("d,C,n,N,H", [(64, 5, 650, 704, 2), (64, 40, 650, 704, 2), (128, 100, 1000, 1024, 1),
+                                       (128, 1, 300, 320, 1), (64, 33, 2100, 2112, 3), (128, 37, 64, 64, 1)])
+def test_kmeans_small_shapes(gpu_lib, d, C, n, N, H):
+    """Head dims 64 and 128, cluster counts off the 32-centroid chunk of the
+    assignment kernel, ragged token tails and a single cluster: the seeding
+    rule, then four Lloyd rounds checked against the third's centroids."""
+    bsa = gpu_lib
+    g = torch.Generator().manual_seed(1000 + d + C + n)
+    centres = torch.randn((H, 8, d), generator=g) * 3.0
+    pick = torch.randint(0, 8, (H, N), generator=g)
+    x = (torch.gather(centres, 1, pick[..., None].expand(H, N, d)) + torch.randn((H, N, d), generator=g))
+    x[:, n:] = 0.0
+    x = x[None].to(torch.bfloat16)
+    u = torch.rand((1, H, C), generator=g, dtype=torch.float64).float()
+    say(f"k-means d={d} C={C} n={n} N={N} H={H}")
+    xd, ud = x.cuda(), u.cuda()
+    seeds, _, _ = bsa.kmeans(xd, C, 0, ud, n_valid=n)
+    c3, _, _ = bsa.kmeans(xd, C, 3, ud, n_valid=n)
+    c4, a4, s4 = bsa.kmeans(xd, C, 4, ud, n_valid=n)
+    torch.cuda.synchronize()
+    seeds, c3, c4 = (t.cpu().numpy().astype(np.float64) for t in (seeds, c3, c4))
+    a4, s4 = a4.cpu().numpy(), s4.cpu().numpy()
+    assert (a4[:, :, n:] == -1).all()
+    for h in range(H):
+        xh = _np(x[0, h])[:n]
+        _check_seeding(xh, seeds[0, h], u[0, h].numpy().astype(np.float64), n)
+        _check_lloyd(xh, c3[0, h], c4[0, h], a4[0, h, :n], s4[0, h])
 
 
 @pytest.mark.parametrize("which", ["q", "k"])
