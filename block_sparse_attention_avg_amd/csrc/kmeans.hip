@@ -5,11 +5,11 @@
 // to D^2, by inverse CDF over token order with a caller-supplied uniform).
 // One launch per seeding round: every workgroup owns 256 tokens, keeps their
 // D^2 in a double buffer and publishes its partial sum; at the start of the
-// next round every workgroup re-derives the drawn index from those partials
-// with the same fixed-order workgroup scans (over the chunk partials, then
-// over the chosen chunk's D^2; no grid barrier), the first workgroup records
-// the centre, and all update D^2 against it, reading token rows in 16-byte
-// pieces and the centre through scalar loads.
+// next round one wave of every workgroup re-derives the drawn index from
+// those partials with the same fixed-order wave scans (over the chunk
+// partials, then over the chosen chunk's D^2; no grid barrier) while the
+// other four start reading their token rows; the first workgroup records the
+// centre, and all update D^2 against it (centre through scalar loads).
 //
 // Warm start (Sparse VideoGen2 summary, Metodologia C.1: the previous
 // denoising step's centroids initialise k-means): seeding is skipped and the
@@ -60,36 +60,145 @@ __device__ __forceinline__ float load_x(const uint16_t* row, int dd) {
   return __uint_as_float((uint32_t)row[dd] << 16);
 }
 
-// Fixed-order block sum over 256 threads (result valid in thread 0): a
-// butterfly inside each wave (every lane ends with the same sum), then the
-// four wave totals in wave order.
-__device__ float block_sum_256(float v, float* red) {
+// Inclusive scan of one value per lane over the wave (fixed order).
+__device__ __forceinline__ float wave_scan(float v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = ((red[0] + red[1]) + red[2]) + red[3];
-  __syncthreads();
-  return r;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float up = __shfl_up(v, o);
+    if (lane >= o) v += up;
+  }
+  return v;
+}
+
+// Inverse-CDF draw of the next centre by one wave: the first token whose
+// running sum of D^2 (chunk partials in order, then the chunk's tokens)
+// exceeds u * total, every sum a fixed-order wave scan. Rounding can leave
+// the target past the last sum: then the last chunk is taken, and in the
+// chunk the last token with positive D^2 (the last token if none). With
+// no positive D^2 at all the draw is floor(u * n). Every lane returns the
+// same token.
+__device__ int kpp_draw_wave(const float* pp, const float* d2p, int nchunk, int n, float u) {
+  constexpr int kCache = 8;                        // chunk partials held in registers: 512 chunks
+  const int lane = threadIdx.x & 63;
+  float pv[kCache];
+#pragma unroll
+  for (int j = 0; j < kCache; ++j) {
+    const int c = 64 * j + lane;
+    pv[j] = c < nchunk ? pp[c] : 0.f;
+  }
+  auto part = [&](int j) {
+    const int c = 64 * j + lane;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < kCache; ++q)
+      if (q == j) v = pv[q];
+    return j < kCache ? v : (c < nchunk ? pp[c] : 0.f);
+  };
+  const int slabs = (nchunk + 63) / 64;
+  float total = 0.f;
+  for (int j = 0; j < slabs; ++j) total += __shfl(wave_scan(part(j)), 63);
+  if (!(total > 0.f)) return min((int)floor((double)u * (double)n), n - 1);
+  const float target = u * total;
+  int ch = -1;
+  float before = 0.f, carry = 0.f, last_before = 0.f;
+  for (int j = 0; j < slabs; ++j) {
+    const float v = part(j);
+    const float incl = wave_scan(v);
+    const int c = 64 * j + lane;
+    const unsigned long long hit = __ballot(c < nchunk && carry + incl > target);
+    if (c == nchunk - 1) last_before = carry + incl - v;
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      ch = 64 * j + f;
+      before = carry + __shfl(incl - v, f);
+      break;
+    }
+    carry += __shfl(incl, 63);
+  }
+  if (ch < 0) {
+    ch = nchunk - 1;
+    before = __shfl(last_before, (nchunk - 1) & 63);
+  }
+  // the token inside the chunk: four slabs of 64
+  float dv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = ch * kChunk + 64 * j + lane;
+    dv[j] = i < n ? d2p[i] : 0.f;
+  }
+  int last_pos = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = ch * kChunk + 64 * j + lane;
+    const float incl = wave_scan(dv[j]);
+    const unsigned long long hit = __ballot(i < n && before + incl > target);
+    if (hit) return ch * kChunk + 64 * j + __builtin_ctzll(hit);
+    const unsigned long long pos = __ballot(i < n && dv[j] > 0.f);
+    if (pos) last_pos = ch * kChunk + 64 * j + 63 - __builtin_clzll(pos);
+    before += __shfl(incl, 63);
+  }
+  return last_pos >= 0 ? last_pos : min(n, (ch + 1) * kChunk) - 1;
 }
 
 }  // namespace
 
-// D^2 of the tokens of this chunk to centre `cidx` (wave-uniform: read with
-// scalar loads); min with the previous D^2 unless first. Each thread reads its
-// token row in 16-byte pieces. Writes the chunk's partial sum.
+// One seeding round. Five waves per workgroup: waves 0-3 own the chunk's 256
+// tokens, wave 4 draws the round's centre from the previous round's D^2. The
+// token waves issue the first half of their rows' 16-byte pieces and their
+// previous D^2 before the draw is known, so those reads overlap it (each
+// wave waits only on its own loads); after the workgroup barrier they read
+// the rest of the row and the centre (wave-uniform: scalar loads), update
+// D^2 (min with the previous unless first) and sum it over the chunk in a
+// fixed order (a butterfly per wave, then the four wave totals). The first
+// workgroup records the centre.
 template <int D>
-__device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_prev,
-                           float* d2_next, float* part_next, bool first, float* red) {
-  const int i = blockIdx.x * kChunk + threadIdx.x;
+__global__ __launch_bounds__(320) void kpp_round_kernel(const uint16_t* __restrict__ x, int N,
+                                                        int n, int C, int r,
+                                                        const float* __restrict__ uni,
+                                                        float* __restrict__ cent, KmWs ws,
+                                                        int BH) {
+  constexpr int P = D / 8, PH = P / 2;             // 16-byte pieces per row, pieces read early
+  __shared__ int sidx;
+  __shared__ float wsum[4];
+  const int bh = blockIdx.y;
+  const int nchunk = gridDim.x;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const uint16_t* xh = x + (size_t)bh * N * D;
+  const int prev = (r + 1) & 1, next = r & 1;
+  const float* d2p = ws.d2 + ((size_t)prev * BH + bh) * N;
+  float* d2n = ws.d2 + ((size_t)next * BH + bh) * N;
+  const float* pp = ws.part + ((size_t)prev * BH + bh) * nchunk;
+  float* pn = ws.part + ((size_t)next * BH + bh) * nchunk;
+  const int i = blockIdx.x * kChunk + t;
+  const bool tok = wave < 4 && i < n;
+
+  uint4 xa[P];
+  float dprev = 0.f;
+  if (wave == 4) {
+    const float u = uni[(size_t)bh * C + r];
+    const int idx = r == 0 ? min((int)floor((double)u * (double)n), n - 1) : kpp_draw_wave(pp, d2p, nchunk, n, u);
+    if (lane == 0) sidx = idx;
+  } else if (tok) {
+    const uint4* xr = reinterpret_cast<const uint4*>(xh + (size_t)i * D);
+#pragma unroll
+    for (int k = 0; k < PH; ++k) xa[k] = xr[k];
+    if (r > 0) dprev = d2p[i];
+  }
+  __syncthreads();
+  const int cidx = __builtin_amdgcn_readfirstlane(min(max(sidx, 0), n - 1));
+  if (blockIdx.x == 0 && t < D)
+    cent[((size_t)bh * C + r) * D + t] = load_x(xh + (size_t)cidx * D, t);
   float v = 0.f;
-  if (i < n) {
+  if (tok) {
     const uint4* xr = reinterpret_cast<const uint4*>(xh + (size_t)i * D);
     const uint4* cr = reinterpret_cast<const uint4*>(xh + (size_t)cidx * D);
+#pragma unroll
+    for (int k = PH; k < P; ++k) xa[k] = xr[k];
     float acc = 0.f;
 #pragma unroll
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const uint4 w = xr[c8], c = cr[c8];
+    for (int k = 0; k < P; ++k) {
+      const uint4 w = xa[k], c = cr[k];
       const uint32_t xs[4] = {w.x, w.y, w.z, w.w}, cs[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -99,128 +208,14 @@ __device__ void kpp_update(const uint16_t* xh, int n, int cidx, const float* d2_
         acc = fmaf(t1, t1, acc);
       }
     }
-    v = first ? acc : fminf(acc, d2_prev[i]);
-    d2_next[i] = v;
+    v = r == 0 ? acc : fminf(acc, dprev);
+    d2n[i] = v;
   }
-  const float s = block_sum_256(v, red);
-  if (threadIdx.x == 0) part_next[blockIdx.x] = s;
-}
-
-namespace {
-
-// Inclusive scan of one value per thread over the 256 threads: a shuffle scan
-// inside each wave, then the wave totals added in wave order (fixed order:
-// every workgroup computes the same sums). Returns the thread's inclusive and
-// exclusive sums and the segment total.
-struct ScanOut {
-  float incl, excl, seg;
-};
-__device__ ScanOut block_scan_256(float v, float* buf) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  float incl = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float up = __shfl_up(incl, o);
-    if (lane >= o) incl += up;
-  }
-  const float prev = __shfl_up(incl, 1);
-  if (lane == 63) buf[w] = incl;
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  if (lane == 0 && wave < 4) wsum[wave] = v;
   __syncthreads();
-  float off = 0.f;
-  for (int j = 0; j < w; ++j) off += buf[j];
-  const float seg = ((buf[0] + buf[1]) + buf[2]) + buf[3];
-  __syncthreads();
-  return ScanOut{incl + off, lane ? prev + off : off, seg};
-}
-
-// Inverse-CDF draw of the next centre by the whole workgroup: the first token
-// whose running sum of D^2 (chunk partials in order, then the chunk's tokens)
-// exceeds u * total. Rounding can leave the target past the last sum: then the
-// last chunk is taken, and in the chunk the last token with positive D^2.
-// Every thread returns the same token.
-__device__ int kpp_draw(const float* pp, const float* d2p, int nchunk, int n, float u, float* buf, int* flag,
-                        float* fsh) {
-  const int t = threadIdx.x;
-  float total = 0.f;
-  ScanOut first{0.f, 0.f, 0.f};                    // the first 256 partials' scan, reused below
-  for (int c0 = 0; c0 < nchunk; c0 += 256) {
-    const int c = c0 + t;
-    const ScanOut sc = block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
-    if (c0 == 0) first = sc;
-    total += sc.seg;
-  }
-  if (!(total > 0.f)) return min((int)floor((double)u * (double)n), n - 1);
-  const float target = u * total;
-  // the chunk: first one whose running sum passes the target
-  int ch = -1;
-  float before = 0.f, carry = 0.f;
-  for (int c0 = 0; c0 < nchunk; c0 += 256) {
-    const int c = c0 + t;
-    const ScanOut sc = c0 == 0 ? first : block_scan_256(c < nchunk ? pp[c] : 0.f, buf);
-    if (t == 0) flag[0] = 256;
-    __syncthreads();
-    if (c < nchunk && carry + sc.incl > target) atomicMin(&flag[0], t);
-    if (c == nchunk - 1) fsh[0] = carry + sc.excl;            // the fallback's running sum
-    __syncthreads();
-    const int f = flag[0];
-    if (f == t) fsh[1] = carry + sc.excl;
-    __syncthreads();
-    if (f < 256) {
-      ch = c0 + f;
-      before = fsh[1];
-      break;
-    }
-    carry += sc.seg;
-  }
-  if (ch < 0) {
-    ch = nchunk - 1;
-    before = fsh[0];
-  }
-  // the token inside the chunk
-  const int i = ch * kChunk + t;
-  const float v = i < n ? d2p[i] : 0.f;
-  const ScanOut sc = block_scan_256(v, buf);
-  if (t == 0) {
-    flag[0] = 256;
-    flag[1] = -1;
-  }
-  __syncthreads();
-  if (i < n && before + sc.incl > target) atomicMin(&flag[0], t);
-  if (i < n && v > 0.f) atomicMax(&flag[1], t);
-  __syncthreads();
-  const int idx = flag[0] < 256 ? ch * kChunk + flag[0]
-                                : (flag[1] >= 0 ? ch * kChunk + flag[1] : min(n, (ch + 1) * kChunk) - 1);
-  __syncthreads();
-  return idx;
-}
-
-}  // namespace
-
-template <int D>
-__global__ __launch_bounds__(256) void kpp_round_kernel(const uint16_t* __restrict__ x, int N,
-                                                        int n, int C, int r,
-                                                        const float* __restrict__ uni,
-                                                        float* __restrict__ cent, KmWs ws,
-                                                        int BH) {
-  __shared__ float red[256];
-  __shared__ int flag[2];
-  __shared__ float fsh[2];
-  const int bh = blockIdx.y;
-  const int nchunk = gridDim.x;
-  const uint16_t* xh = x + (size_t)bh * N * D;
-  const float u = uni[(size_t)bh * C + r];
-  const int prev = (r + 1) & 1, next = r & 1;
-  const float* d2p = ws.d2 + ((size_t)prev * BH + bh) * N;
-  float* d2n = ws.d2 + ((size_t)next * BH + bh) * N;
-  const float* pp = ws.part + ((size_t)prev * BH + bh) * nchunk;
-  float* pn = ws.part + ((size_t)next * BH + bh) * nchunk;
-
-  const int idx = r == 0 ? min((int)floor((double)u * (double)n), n - 1)
-                         : kpp_draw(pp, d2p, nchunk, n, u, red, flag, fsh);
-  const int cidx = __builtin_amdgcn_readfirstlane(min(max(idx, 0), n - 1));
-  if (blockIdx.x == 0 && threadIdx.x < D)
-    cent[((size_t)bh * C + r) * D + threadIdx.x] = load_x(xh + (size_t)cidx * D, threadIdx.x);
-  kpp_update<D>(xh, n, cidx, d2p, d2n, pn, r == 0, red);
+  if (t == 0) pn[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
 // Assignment on the matrix cores. The nearest centroid minimises
@@ -556,7 +551,7 @@ static hipError_t kmeans_t(const uint16_t* x, int BH, int N, int n, int C, int i
   const int nchunk_n = (n + kChunk - 1) / kChunk;
   if (uni)
     for (int r = 0; r < C; ++r)
-      kpp_round_kernel<D><<<dim3(nchunk_n, BH), 256, 0, s>>>(x, N, n, C, r, uni, cent, ws, BH);
+      kpp_round_kernel<D><<<dim3(nchunk_n, BH), 320, 0, s>>>(x, N, n, C, r, uni, cent, ws, BH);
   if (changes && iters > 0) {
     const size_t total = (size_t)BH * iters;
     changes_init_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(changes, total, iters, n);
