@@ -64,6 +64,7 @@ _SIGS = {
     "bsa_kmeans": ([_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
     "bsa_attention_tile_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P], _I),
     "bsa_mask_recall": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "bsa_check_mask": ([_P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "bsa_kmeans_warm": ([_P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
     "bsa_cluster_order_workspace": ([_I, _I, _I, _I], _Z),
     "bsa_cluster_order": ([_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
@@ -396,6 +397,20 @@ def mask_recall(tile_max: torch.Tensor, tile_sum: torch.Tensor, kv_count: torch.
                                   kv_index.shape[-1], B, H, nqb, nkb, rec.data_ptr(), mass.data_ptr(),
                                   _stream(tile_max.device)), "mask_recall")
     return rec, mass
+
+
+def check_mask(kv_count: torch.Tensor, kv_index: torch.Tensor, nkb: int):
+    """Counts list defects: (rows with a count outside [0, kv_stride], ids
+    outside [0, nkb), entries not greater than their predecessor)."""
+    _dev_tensor(kv_count, torch.int32, "kv_count")
+    _dev_tensor(kv_index, torch.int32, "kv_index")
+    B, H, nqb, stride = kv_index.shape
+    if kv_count.numel() != B * H * nqb:
+        raise ValueError("kv_count must be [B, H, nqb]")
+    bad = torch.empty(3, dtype=torch.int32, device=kv_index.device)
+    _check(load().bsa_check_mask(kv_count.data_ptr(), kv_index.data_ptr(), B, H, nqb, nkb, stride, bad.data_ptr(),
+                                 _stream(kv_index.device)), "check_mask")
+    return tuple(int(v) for v in bad.cpu().tolist())
 
 
 # ------------------------------------------------------------------ reorder

@@ -376,6 +376,16 @@ int bsa_mask_recall(const float* tile_max, const float* tile_sum, const int32_t*
                     "mask_recall");
 }
 
+int bsa_check_mask(const int32_t* kv_count, const int32_t* kv_index, int B, int H, int nqb, int nkb, int kv_stride,
+                   int32_t* bad, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (B <= 0 || H <= 0 || nqb < 0 || nkb <= 0) return fail(BSA_EINVAL, "check_mask: bad sizes");
+  if (kv_stride < 1) return fail(BSA_EINVAL, "check_mask: kv_stride must be >= 1");
+  if (!kv_count || !kv_index || !bad) return fail(BSA_EINVAL, "check_mask: null pointer");
+  return hip_status(bsa::launch_check_mask(kv_count, kv_index, (size_t)B * H * nqb, nkb, kv_stride, bad, stream),
+                    "check_mask");
+}
+
 size_t bsa_kmeans_workspace(int B, int H, int N, int C, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || C <= 0) return 0;
   return bsa::kmeans_ws_bytes(B * H, N, C, d);

@@ -131,6 +131,8 @@ hipError_t launch_tile_stats(const uint16_t* q, const uint16_t* k, const float* 
 hipError_t launch_mask_recall(const float* tmax, const float* tsum, const int32_t* kv_count,
                               const int32_t* kv_index, int kv_stride, size_t rows, int nkb, float* oracle_recall,
                               float* mass_recall, hipStream_t s);
+hipError_t launch_check_mask(const int32_t* kv_count, const int32_t* kv_index, size_t rows, int nkb, int kv_stride,
+                             int32_t* bad, hipStream_t s);
 hipError_t launch_kmeans(const uint16_t* x, int BH, int N, int d, int n_valid, int C, int iters,
                          const float* uniforms, float* centroids, int32_t* assign,
                          int32_t* sizes, int32_t* changes, int tol, void* ws, hipStream_t s);

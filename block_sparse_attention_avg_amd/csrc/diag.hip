@@ -15,6 +15,9 @@
 // min: lane-local, then a fixed butterfly over the wave, then the two waves'
 // partials in LDS. Every order is fixed, so the map is bit-reproducible.
 //
+// check_mask_kernel: one wave per row of the lists; integer counts, so the
+// totals are exact in any order.
+//
 // recall_kernel: one wave per (head, query block) row of the mask. The row's
 // max-pooled values sit in LDS; a kept tile J is in the equal-budget oracle
 // mask when fewer than k tiles outrank it (larger value, or equal value and a
@@ -215,6 +218,47 @@ __global__ __launch_bounds__(256) void recall_kernel(RecallArgs a, size_t rows) 
     a.oracle_recall[row] = valid > 0 ? (float)hits / (float)valid : 0.f;
     a.mass_recall[row] = tot > 0.f ? kept / tot : 0.f;
   }
+}
+
+__global__ __launch_bounds__(64) void zero_counts_kernel(int32_t* __restrict__ bad) {
+  if (threadIdx.x < 3) bad[threadIdx.x] = 0;
+}
+
+// bad[0] += rows whose count lies outside [0, kv_stride]; for the other rows,
+// over their first kv_count entries, bad[1] += ids outside [0, nkb) and
+// bad[2] += ids not greater than the entry before them.
+__global__ __launch_bounds__(256) void check_mask_kernel(const int32_t* __restrict__ kv_count,
+                                                         const int32_t* __restrict__ kv_index, size_t rows, int nkb,
+                                                         int kv_stride, int32_t* __restrict__ bad) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int cnt = kv_count[row];
+  if (cnt < 0 || cnt > kv_stride) {
+    if (lane == 0) atomicAdd(&bad[0], 1);
+    return;
+  }
+  const int32_t* l = kv_index + row * kv_stride;
+  int oor = 0, uns = 0;
+  for (int e = lane; e < cnt; e += 64) {
+    const int v = l[e];
+    oor += (unsigned)v >= (unsigned)nkb;
+    uns += e > 0 && v <= l[e - 1];
+  }
+  oor = wave_sum_i(oor);
+  uns = wave_sum_i(uns);
+  if (lane == 0) {
+    if (oor) atomicAdd(&bad[1], oor);
+    if (uns) atomicAdd(&bad[2], uns);
+  }
+}
+
+hipError_t launch_check_mask(const int32_t* kv_count, const int32_t* kv_index, size_t rows, int nkb, int kv_stride,
+                             int32_t* bad, hipStream_t s) {
+  zero_counts_kernel<<<1, 64, 0, s>>>(bad);
+  if (rows > 0)
+    check_mask_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(kv_count, kv_index, rows, nkb, kv_stride, bad);
+  return hipGetLastError();
 }
 
 hipError_t launch_tile_stats(const uint16_t* q, const uint16_t* k, const float* lse, int BH, int N, int d,

@@ -345,6 +345,24 @@ int bsa_mask_recall(const float* tile_max, const float* tile_sum,
                     float* oracle_recall, float* mass_recall,
                     hipStream_t stream);
 
+/*
+ * Validator of block lists, for tests (the lists' contract: the NABLA
+ * summary's CDF thresholding keeps a set of key blocks per query block, which
+ * the mask stage writes as ascending ids). Over the B*H*nqb rows:
+ *   bad[0] = rows whose kv_count lies outside [0, kv_stride];
+ *   bad[1] = ids outside [0, nkb) among the first kv_count entries of the
+ *            other rows;
+ *   bad[2] = entries of those rows not greater than the entry before them
+ *            (the list is not strictly ascending there).
+ *   kv_count  int32 [B,H,nqb], kv_index int32 [B,H,nqb,kv_stride] (device)
+ *   bad       int32 [3] (device), overwritten
+ * Exact integer counts. The attention entry points do not check their lists;
+ * a caller that builds or edits them can run this first.
+ */
+int bsa_check_mask(const int32_t* kv_count, const int32_t* kv_index,
+                   int B, int H, int nqb, int nkb, int kv_stride,
+                   int32_t* bad, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Token reorder helpers
  * ------------------------------------------------------------------------ */

@@ -112,6 +112,11 @@ def test_argument_validation_newer_entry_points(lib):
     assert lib.bsa_mask_recall(P, P, P, P, 9000, 1, 1, 4, 9000, P, P, None) == 2
     assert lib.bsa_mask_recall(P, P, P, P, 0, 1, 1, 4, 4, P, P, None) == 1
     assert lib.bsa_mask_recall(P, None, P, P, 4, 1, 1, 4, 4, P, P, None) == 1
+    # list validator
+    assert lib.bsa_check_mask(P, P, 1, 1, 4, 0, 4, P, None) == 1
+    assert lib.bsa_check_mask(P, P, 1, 1, 4, 4, 0, P, None) == 1
+    assert lib.bsa_check_mask(P, None, 1, 1, 4, 4, 4, P, None) == 1
+    assert lib.bsa_check_mask(P, P, 1, 1, 4, 4, 4, None, None) == 1
 
 
 def test_workspace_queries(lib):

@@ -161,6 +161,52 @@ def test_mask_deterministic(gpu_lib):
         assert torch.equal(a[1].view(-1, a[1].shape[-1])[r, :c], b[1].view(-1, b[1].shape[-1])[r, :c])
 
 
+def _list_defects(cnt, idx, nkb):
+    """Host count of what bsa_check_mask reports, from its definition."""
+    cnt = cnt.reshape(-1)
+    idx = idx.reshape(len(cnt), -1)
+    stride = idx.shape[1]
+    bad_rows = oor = uns = 0
+    for r, c in enumerate(cnt):
+        if c < 0 or c > stride:
+            bad_rows += 1
+            continue
+        row = idx[r, :c]
+        oor += int(((row < 0) | (row >= nkb)).sum())
+        uns += int((row[1:] <= row[:-1]).sum())
+    return bad_rows, oor, uns
+
+
+def test_check_mask_counts_defects(gpu_lib):
+    """The list validator finds nothing in the mask stage's lists and counts
+    planted defects exactly: counts outside [0, stride], ids outside
+    [0, nkb), entries out of ascending order (a swap, a repeat)."""
+    bsa = gpu_lib
+    w, q, k, v = _inputs("wan480")
+    cnt, idx = bsa.build_block_mask(q.cuda(), k.cuda(), w.thr, n_valid=w.n_valid)
+    nkb = (w.n_valid + 63) // 64
+    say(f"check_mask on the 480p lists ({cnt.numel()} rows)")
+    assert bsa.check_mask(cnt, idx, nkb) == (0, 0, 0)
+    c, x = cnt.cpu().numpy().copy(), idx.cpu().numpy().copy()
+    flat_c, flat_x = c.reshape(-1), x.reshape(len(c.reshape(-1)), -1)
+    long_rows = np.nonzero(flat_c >= 4)[0]
+    flat_c[3] = -1
+    flat_c[5] = flat_x.shape[1] + 1
+    r = long_rows[10]
+    flat_x[r, 1] = nkb                                # out of range (and not ascending after it)
+    r = long_rows[20]
+    flat_x[r, [1, 2]] = flat_x[r, [2, 1]]             # swapped pair
+    r = long_rows[30]
+    flat_x[r, 2] = flat_x[r, 1]                       # repeated id
+    r = long_rows[40]
+    flat_x[r, 0] = -7
+    want = _list_defects(c, x, nkb)
+    got = bsa.check_mask(torch.from_numpy(c).cuda(), torch.from_numpy(x).cuda(), nkb)
+    say(f"  planted defects: expected {want}, counted {got}")
+    assert want[0] == 2 and want[1] == 2 and want[2] >= 3
+    assert got == want
+
+
 def test_mask_exact_ties(gpu_lib):
     """All scores equal: the cut falls inside one run of ties.
 
