@@ -1,8 +1,9 @@
-// MFMA tile helpers shared by the attention-gradient and tile-statistics
-// kernels: 64-row bf16 tiles staged in LDS by direct-to-LDS buffer loads with
-// XOR-swizzled 16-byte pieces, the row operand read, the transposed operand
-// read (LDS transpose read, rows in the order of the 32 x 32 accumulator
-// layout), and the accumulator-to-rows store.
+// MFMA tile helpers shared by the attention-gradient, tile-statistics and
+// k-means assignment kernels: 64-row bf16 tiles staged in LDS by
+// direct-to-LDS buffer loads with XOR-swizzled 16-byte pieces, the row
+// operand read, the transposed operand read (LDS transpose read, rows in the
+// order of the 32 x 32 accumulator layout), and the accumulator-to-rows
+// store.
 #pragma once
 
 #include "attn.h"
