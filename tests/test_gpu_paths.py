@@ -89,6 +89,7 @@ def test_fractal_sta_path(gpu_lib):
     o, cnt, idx = pl.fractal_sta_attention(q.cuda(), k.cuda(), v.cuda(), lay, w.thr,
                                            radius=w.window, n_valid=w.n_valid, return_mask=True)
     torch.cuda.synchronize()
+    assert gpu_lib.check_mask(cnt, idx, idx.shape[-1]) == (0, 0, 0)
     o, cnt, idx = _np(o), cnt.cpu().numpy(), idx.cpu().numpy()
     perm, st, ln, coords = ol.fractal_order(w.T, w.Hl, w.Wl, w.patch, w.N)
     derived = ol.block_coords_from_tokens(token_coords(w.T, w.Hl, w.Wl), perm, st, ln, w.patch)
@@ -164,6 +165,7 @@ def test_head_tiling_path(gpu_lib):
     o, cnt, idx = pl.head_tiled_attention(q.cuda(), k.cuda(), v.cuda(), lay, w.thr, n_valid=w.n_valid,
                                           return_mask=True)
     torch.cuda.synchronize()
+    assert gpu_lib.check_mask(cnt, idx, idx.shape[-1]) == (0, 0, 0)
     o, cnt, idx = _np(o), cnt.cpu().numpy(), idx.cpu().numpy()
     assert (o[:, :, w.n_valid:] == 0).all()
     nbp = lay.blocks.nblocks
@@ -391,6 +393,7 @@ def test_semantic_path(gpu_lib):
     torch.cuda.synchronize()
     o = _np(o)
     assert (o[:, :, w.n_valid:] == 0).all()
+    assert bsa.check_mask(st.kv_count, st.kv_index, w.Ck) == (0, 0, 0)
     cnt, idx = st.kv_count.cpu().numpy(), st.kv_index.cpu().numpy()
     cq, ck = st.cq.cpu().numpy(), st.ck.cpu().numpy()
     nq, nk = st.nq.cpu().numpy(), st.nk.cpu().numpy()
