@@ -232,9 +232,11 @@ __global__ __launch_bounds__(320) void kpp_round_kernel(const uint16_t* __restri
 // same in every workgroup); the parts are the A operand, shared by both
 // token groups. A lane holds 16 centroid scores of one token; it keeps the
 // first minimum in centroid order, and the two lane halves merge at the end
-// (equal scores go to the lower index).
+// (equal scores go to the lower index). Three waves per SIMD (at most 168
+// registers; left alone the compiler takes 154 + 32 accumulation registers
+// and fits two).
 template <int D>
-__global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict__ x, int N, int n,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void assign_kernel(const uint16_t* __restrict__ x, int N, int n,
                                                      int C, const float* __restrict__ cent,
                                                      int32_t* __restrict__ assign, Stop stop,
                                                      int32_t* __restrict__ changes) {
