@@ -17,7 +17,8 @@ nearest to its own centroid; seeding follows the D^2 inverse-CDF rule
 (checked against a brute-force loop); the cluster order is a stable sort;
 ``kmeans_warm`` -- a hand-worked 1-D case (tests/golden/kmeans_warm_cases.txt),
 a cold run equals a warm start from its seeds, converged centroids are a
-fixed point.
+fixed point; empty clusters -- hand-worked rounds in which a cluster gets no
+point and keeps its centroid (tests/golden/kmeans_empty_cases.txt).
 """
 
 from __future__ import annotations

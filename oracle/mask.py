@@ -25,7 +25,10 @@ hand-worked fixture; reduced map -- two-block logistic closed form, identical
 keys give a uniform row; selection -- brute force over every subset for small
 rows, hand-worked fixtures in tests/golden/cdf_select_cases.txt, thr = 0 and
 thr = 1 special cases; window union -- superset property and closed-form
-counts.
+counts; centroid top-p -- hand-worked size-weighted cases with unequal
+cluster sizes, empty clusters and p < 1 (tests/golden/centroid_mask_cases.txt),
+and a key cluster of n tokens weighing exactly what n one-token clusters at
+its centroid weigh together.
 """
 
 from __future__ import annotations

@@ -23,7 +23,7 @@ from gen import BY_INDEX, WORKLOADS, generate
 from oracle import attention as oa
 from oracle import layout as ol
 from oracle import mask as om
-from tests.band import keep_from_lists, mask_mismatches
+from tests.band import keep_from_lists, mask_mismatches, set_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -224,6 +224,8 @@ def test_mask_exact_ties(gpu_lib):
     assert ref.sum() == 300 and ref[:300].all()
     assert (cnt == 300).all()
     assert (idx[0, 0, :, :300] == np.arange(300)).all()
+    keep = keep_from_lists(cnt[0, 0], idx[0, 0], n)
+    assert all(set_violations(np.full(n, 1.0 / n), 0.5004, row) == 0 for row in keep)
 
 
 @pytest.mark.parametrize("nkb", [1000, 2112])

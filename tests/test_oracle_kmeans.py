@@ -129,3 +129,37 @@ def test_converged_centroids_are_a_fixed_point():
     assert ch2.tolist() == [300, 0, 0, 0, 0]
     np.testing.assert_array_equal(c2, c)
     assert np.array_equal(a2, a) and np.array_equal(s2, s)
+
+
+# ------------------------------------------------------- empty clusters
+
+def _empty_cases():
+    with open(os.path.join(GOLDEN, "kmeans_empty_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield [s.split() for s in line.split("|")]
+
+
+@pytest.mark.parametrize("case", list(_empty_cases()))
+def test_empty_cluster_keeps_its_centroid_golden(case):
+    kind = case[0][0]
+    x = np.array([float(v) for v in case[1]])[:, None]
+    if kind == "warm":
+        start, iters, tol, a, cent, sizes, changes = case[2:]
+        c, got_a, got_s, got_ch = ok.kmeans_warm(x, np.array([float(v) for v in start])[:, None],
+                                                 int(iters[0]), int(tol[0]))
+        assert got_ch.tolist() == [int(v) for v in changes]
+        # one round of the update from the start also leaves the empty centroids
+        a0 = ok.assign(x, np.array([float(v) for v in start])[:, None])
+        c1, s1 = ok.update(x, a0, np.array([float(v) for v in start])[:, None])
+        for j, n in enumerate(s1):
+            if n == 0:
+                assert c1[j, 0] == float(start[j])
+    else:
+        u, iters, a, cent, sizes, seeds = case[2:]
+        c, got_a, got_s, got_seeds, _ = ok.kmeans(x, len(u), int(iters[0]), np.array([float(v) for v in u]))
+        assert got_seeds.tolist() == [int(v) for v in seeds]
+    assert got_a.tolist() == [int(v) for v in a]
+    assert got_s.tolist() == [int(v) for v in sizes]
+    np.testing.assert_allclose(c[:, 0], [float(v) for v in cent], rtol=0, atol=1e-12)

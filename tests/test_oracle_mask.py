@@ -241,3 +241,60 @@ def test_block_mask_empty_blocks_take_no_part():
     win = np.ones((7, 7), dtype=bool)
     keep3, _ = om.block_mask(q, k, st2, ln2, st2, ln2, 0.9, window=win)
     assert not keep3[~real].any() and keep3[real].all()
+
+
+# ------------------------------------------------ centroid top-p (size-weighted)
+
+def _num(tok):
+    """A fixture number: a decimal, a fraction 'a/b', or 'lnX' / '-lnX'."""
+    from fractions import Fraction
+    neg = tok.startswith("-")
+    t = tok[1:] if neg else tok
+    v = float(np.log(float(t[2:]))) if t.startswith("ln") else float(Fraction(t))
+    return -v if neg else v
+
+
+def _rows(field):
+    return np.array([[_num(t) for t in r.split()] for r in field.split(";")])
+
+
+def _centroid_cases():
+    with open(os.path.join(GOLDEN, "centroid_mask_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield [s.strip() for s in line.split("|")]
+
+
+@pytest.mark.parametrize("case", list(_centroid_cases()))
+def test_centroid_mask_golden(case):
+    scale, cq, nq, ck, nk, p, w, kept = case
+    nq = np.array([int(v) for v in nq.split()])
+    nk = np.array([int(v) for v in nk.split()])
+    keep, got_w = om.centroid_mask(_rows(cq), nq, _rows(ck), nk, float(p), scale=float(scale))
+    np.testing.assert_allclose(got_w, _rows(w), rtol=1e-12, atol=1e-15)
+    want = np.zeros_like(keep)
+    for r, ids in enumerate(kept.split(";")):
+        if ids.strip() != "-":
+            want[r, [int(i) for i in ids.split()]] = True
+    assert np.array_equal(keep, want)
+
+
+def test_centroid_weight_equals_copies_of_the_centroid():
+    # A key cluster of n tokens weighs exactly what n clusters of one token at
+    # the same centroid weigh together: the size enters as a factor n_b on
+    # exp(s_ab). Checked through centroid_mask on unequal sizes.
+    rng = np.random.default_rng(31)
+    cq = rng.normal(size=(5, 8))
+    ck = rng.normal(size=(7, 8))
+    nq = np.array([2, 1, 4, 3, 1])
+    nk = np.array([1, 5, 2, 9, 3, 1, 6])
+    _, w = om.centroid_mask(cq, nq, ck, nk, 0.9, scale=0.7)
+    ck_copies = np.repeat(ck, nk, axis=0)
+    owner = np.repeat(np.arange(7), nk)
+    _, w1 = om.centroid_mask(cq, nq, ck_copies, np.ones(len(ck_copies), np.int64), 0.9, scale=0.7)
+    summed = np.stack([w1[:, owner == b].sum(1) for b in range(7)], axis=1)
+    np.testing.assert_allclose(w, summed, rtol=1e-13)
+    # and an unweighted softmax differs when sizes differ
+    plain = om.softmax_rows(om.reduced_scores(cq, ck, 0.7))
+    assert np.abs(plain - w).max() > 1e-2
