@@ -1,19 +1,25 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config wan480]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config hunyuan720]
 
 One step = the whole hot path on one batch of synthetic input already resident
 in HBM: block mean pooling of Q and K, reduced attention + CDF selection (the
 mask stage), then the block-sparse attention forward. Prints ONE JSON line.
+The headline workload is the 118,800-token 720p layer at ~90 % block sparsity
+(24 heads, d 128, thr 0.1); the 32,760-token 480p layer follows under "also"
+with the same step and warm-up counts and its own roofline.
 
   value      effective TFLOP/s of the whole step: F_eff / step time, where
              F_eff = 4 * d * sum over kept (query block I, key block J) of
              len_I * len_J (QK^T and PV of kept tiles only, padding excluded)
   roofline   the attention kernel (the dominant one) against the bf16 dense
              MFMA peak of MI355X (2516.6 TFLOP/s), timed with HIP events on
-             the stream the library launches on
+             the stream the library launches on; traffic = calibrated HBM
+             bytes per launch from the committed counter summary of that
+             kernel (null once its source changed)
   cpu_baseline  the float64 CPU reference timed on a bounded sample of the
-             same workload and extrapolated to one step
+             same workload and extrapolated to one step (the 480p layer under
+             "also": the whole step, not extrapolated)
 
 Beside the step, on the same inputs (each switchable off):
   backward   forward with row normalisers + dQ/dK/dV over the step's lists
@@ -24,9 +30,6 @@ Beside the step, on the same inputs (each switchable off):
   cold_cache the step with Q, K, V flushed from the caches
   mfma_probe / dense_gemm_ref  what the MFMA pipe and the vendor GEMM reach
              on the same box (context for the roofline fraction)
-
-A second workload (the 118,800-token 720p layer) is measured after the main
-one and reported under "also", with its mask-stage / attention time ratio.
 """
 
 from __future__ import annotations
@@ -465,8 +468,15 @@ def dense_gemm_ref(dev, n: int = 8192, reps: int = 20):
     return 2.0 * n ** 3 / t / 1e12
 
 
-def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
-    """Times the float64 CPU reference on a bounded sample, extrapolated to a step."""
+def cpu_baseline(r: Runner, flops_total: float, mask_heads=None, attn_blocks=None):
+    """Times the float64 CPU reference (untuned) on the host.
+
+    mask_heads / attn_blocks None: the whole step (every head's mask stage and
+    every query block's attention). Otherwise a bounded sample -- the mask
+    stage of ``mask_heads`` heads and the attention of ``attn_blocks`` seeded
+    query blocks of head 0 on head 0's own mask -- extrapolated to one step by
+    the share of heads and query blocks it covers.
+    """
     from oracle import attention as oa, layout as ol, mask as om  # CPU reference (baseline leg only)
     try:
         from threadpoolctl import threadpool_info
@@ -475,28 +485,46 @@ def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
         cores = os.cpu_count() or 1
     w = r.w
     st, ln = ol.raster_blocks(w.n_valid, w.block)
+    full = mask_heads is None
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    mheads = heads if full else heads[:mask_heads]
     t0 = time.perf_counter()
-    keeps = []
-    for h in range(mask_heads):
-        kp, _ = om.block_mask(r.q_cpu[0, h].double().numpy(), r.k_cpu[0, h].double().numpy(),
-                              st, ln, st, ln, w.thr)
-        keeps.append(kp)
-    t_mask = (time.perf_counter() - t0) / mask_heads * w.H * w.B
-    rng = np.random.default_rng(0)
-    blocks = sorted(rng.choice(len(st), size=min(attn_blocks, len(st)), replace=False).tolist())
-    qh, kh, vh = (t[0, 0].double().numpy() for t in (r.q_cpu, r.k_cpu, r.v_cpu))
+    keeps = {}
+    for b, h in mheads:
+        keeps[(b, h)], _ = om.block_mask(r.q_cpu[b, h].double().numpy(), r.k_cpu[b, h].double().numpy(),
+                                         st, ln, st, ln, w.thr)
+    t_mask = (time.perf_counter() - t0) * len(heads) / len(mheads)
+    if full:
+        blocks = None
+        aheads = heads
+    else:
+        rng = np.random.default_rng(0)
+        blocks = sorted(rng.choice(len(st), size=min(attn_blocks, len(st)), replace=False).tolist())
+        aheads = heads[:1]
     t0 = time.perf_counter()
-    oa.masked_attention(qh, kh, vh, st, ln, st, ln, keeps[0], blocks=blocks)
-    t_att = (time.perf_counter() - t0) / len(blocks) * len(st) * w.H * w.B
+    for b, h in aheads:
+        qh, kh, vh = (t[b, h].double().numpy() for t in (r.q_cpu, r.k_cpu, r.v_cpu))
+        oa.masked_attention(qh, kh, vh, st, ln, st, ln, keeps[(b, h)], blocks=blocks)
+    t_att = time.perf_counter() - t0
+    if not full:
+        t_att *= len(st) / len(blocks) * len(heads)
     t_step = t_mask + t_att
+    if full:
+        sample = (f"float64 numpy reference, the whole step: mask stage of all {len(heads)} heads and "
+                  f"attention of all {len(st)} query blocks of every head ({t_step:.1f} s/step, measured)")
+    else:
+        sample = (f"float64 numpy reference on a bounded sample, extrapolated: mask stage of {len(mheads)} of "
+                  f"{len(heads)} heads and attention of {len(blocks)} of {len(st)} query blocks of head 0 "
+                  f"(est. {t_step:.1f} s/step)")
     return {
         "value": flops_total / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"float64 numpy reference: mask stage of {mask_heads} of {w.H} heads and "
-                   f"attention of {len(blocks)} of {len(st)} query blocks of head 0, "
-                   f"extrapolated to one step (est. {t_step:.1f} s/step)"),
+        "sample": sample,
+        "extrapolated": not full,
+        "host_cpus": os.cpu_count(),
+        "blas_threads": int(cores),
     }
 
 
@@ -504,14 +532,28 @@ def cpu_baseline(r: Runner, flops_total: float, mask_heads=2, attn_blocks=48):
 # Summaries of rocprofv3 CSV output (kernel trace statistics, counter runs),
 # written as the text files kept under profiles/.
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan480_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_avg_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "block_sparse_attention_avg_amd", "csrc")
+# Sources of the attention forward kernels; the counter summary of a kernel
+# stays valid while their combined hash is unchanged.
+ATTN_SOURCES = ("attn.h", "attn_fwd.hip", "attn_fwd_1w.hip", "attn_tile.h", "common.h")
 
 
-def _sha256(path: str) -> str:
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.txt")
+
+
+def _sha256(paths) -> str:
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in paths:
+        if os.path.exists(p):
+            with open(p, "rb") as f:
+                h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def attn_sources_sha() -> str:
+    return _sha256([os.path.join(CSRC, n) for n in ATTN_SOURCES])
 
 
 def _csv_rows(path: str):
@@ -543,20 +585,21 @@ def rocprof_counter(run_dir: str, counter: str, kernel: str):
     return sum(vals) / len(vals), len(vals)
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when the kernel source changed after the counters were taken."""
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary of
+    that workload, or None when the attention sources changed after the
+    counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
-        if kv.get("source_sha256", "").strip() != _sha256(ATTN_SRC):
+        if kv.get("source_sha256", "").strip() != attn_sources_sha():
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
+def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", workload=""):
     lines = []
     if kind == "stats":
         lines.append(f"command: {command}")
@@ -595,7 +638,7 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
             lines.append(f"{k} (mean per dispatch): " + " ".join(vals))
     elif kind == "traffic":
         fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-        kern = "bsa::attn_fwd_kernel<128, false, 0>"
+        kern = kernel
         copy = "bsa::permute_kernel<16>"
         f_att, n1 = rocprof_counter(fetch_dir, "FETCH_SIZE", kern)
         w_att, n2 = rocprof_counter(write_dir, "WRITE_SIZE", kern)
@@ -608,7 +651,7 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
         write_b = w_att * 1024.0 * w_scale
         lines += [
             f"command: {command}",
-            f"kernel: {kern} (wan480 workload, bench.py --steps 5 --warmup 2 --no-cpu-baseline --also none)",
+            f"kernel: {kern} ({workload} workload)",
             f"FETCH_SIZE per dispatch: {f_att:.1f} KiB over {n1} dispatches",
             f"WRITE_SIZE per dispatch: {w_att:.1f} KiB over {n2} dispatches",
             f"copy calibration ({copy}, identity permutation reading and writing 1 GiB): "
@@ -616,7 +659,8 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command=""):
             f"fetch_bytes_per_launch: {fetch_b:.6g}",
             f"write_bytes_per_launch: {write_b:.6g}",
             f"traffic_bytes_per_launch: {fetch_b + write_b:.6g}",
-            f"source_sha256: {_sha256(ATTN_SRC)}",
+            f"sources: {' '.join(ATTN_SOURCES)}",
+            f"source_sha256: {attn_sources_sha()}",
         ]
     print("\n".join(lines))
 
@@ -635,13 +679,70 @@ def copy_calibration(dev, steps: int):
                                            "launches": steps}}), flush=True)
 
 
+def measure(w, a, dev):
+    """Times one raster workload: the step, its roofline, and (per flags) the
+    backward, the cold-cache step, the reorder-based paths (480p layer only)
+    and the CPU reference. Returns (entry dict, step summary)."""
+    r = Runner(w, dev)
+    ms_step, t_mask, t_attn = r.timed(a.steps, a.warmup)
+    s = r.summary(ms_step, t_mask, t_attn)
+    e = {
+        "workload": describe(w),
+        "ms_per_step": round(ms_step, 4),
+        "step_tflops": round(s["step_tflops"], 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": attn_kernel_name(w),
+            "achieved": round(s["attn_tflops"], 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(s["attn_frac_of_peak"], 4),
+            "traffic": measured_traffic(w.key),
+        },
+        "pct_bf16_peak_attn": round(100 * s["attn_frac_of_peak"], 2),
+        "sparsity": {"blocks": round(s["sparsity_blocks"], 4),
+                     "token_pairs": round(s["sparsity_token_pairs"], 4),
+                     "kept_per_row_mean": round(s["kept_per_row_mean"], 2),
+                     "kept_per_row_max": s["kept_per_row_max"]},
+        "stages_ms": {"mask": round(t_mask, 4), "attention": round(t_attn, 4),
+                      "attention_median": round(float(np.median(r.attn_each)), 4),
+                      "attention_min": round(float(np.min(r.attn_each)), 4),
+                      "mask_over_attention": round(s["mask_over_attn"], 4),
+                      "mask_gbs": round(s["mask_gbs"], 1),
+                      "mask_frac_of_hbm": round(s["mask_frac_of_hbm"], 4)},
+        "flops_eff_per_step": s["flops_eff"],
+    }
+    if a.bwd_steps > 0:
+        tf, tb = r.backward(a.bwd_steps)
+        fb = 2.5 * s["flops_eff"]                  # five products per kept tile
+        e["backward"] = {"ms": round(tb, 4), "tflops_eff": round(fb / (tb * 1e-3) / 1e12, 3),
+                         "frac_of_peak": round(fb / (tb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "fwd_with_lse_ms": round(tf, 4), "steps": a.bwd_steps,
+                         "flops": "2.5 x the forward's effective FLOP (S, dP, dV, dK, dQ products of "
+                                  "kept tiles; the dQ pass also recomputes S and dP, not counted)"}
+    if a.path_steps > 0 and w.key == "wan480":
+        e["paths"] = paths_bench(r, a.path_steps)
+    if a.cold_reps > 0:
+        cm, ca = r.cold(a.cold_reps)
+        e["cold_cache"] = {"mask_ms": round(cm, 4), "attention_ms": round(ca, 4),
+                           "attn_tflops": round(s["flops_eff"] / (ca * 1e-3) / 1e12, 3),
+                           "reps": a.cold_reps,
+                           "how": "median; 512 MiB written before each step (outside the events)"}
+    return r, e, s
+
+
+# Bounded CPU-reference samples per workload (mask heads, attention query
+# blocks), sized to about 10-30 s on 16 host cores; None = the whole step.
+CPU_SAMPLE = {"hunyuan720": (2, 128), "wan480": (None, None), "tiny": (None, None)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="wan480", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="hunyuan720", help="second workload to report, or 'none'")
+    ap.add_argument("--config", default="hunyuan720", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", default="wan480", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="extra steps timed with flushed caches (reported under cold_cache; 0 = skip)")
@@ -658,12 +759,16 @@ def main():
     ap.add_argument("--rocprof-summary", nargs="+", metavar=("KIND", "DIR"),
                     help="summarise rocprofv3 CSV output: 'stats DIR' (kernel trace), "
                          "'counters DIR' (counter means) or "
-                         "'traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR'")
+                         "'traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR' "
+                         "(with --kernel and --workload)")
+    ap.add_argument("--kernel", default="", help="kernel name of a traffic summary")
+    ap.add_argument("--workload", default="", help="workload of a traffic summary")
     ap.add_argument("--bench-log", help="bench output of the profiled run (stats summary)")
     ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     a = ap.parse_args()
     if a.rocprof_summary:
-        rocprof_summary(a.rocprof_summary[0], a.rocprof_summary[1:], a.bench_log, a.command)
+        rocprof_summary(a.rocprof_summary[0], a.rocprof_summary[1:], a.bench_log, a.command, a.kernel,
+                        a.workload)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -683,18 +788,15 @@ def main():
     if w.order != "raster":
         print("bench.py times the raster-order workloads (tiny, wan480, hunyuan720)", file=sys.stderr)
         sys.exit(1)
-    r = Runner(w, dev)
-    ms_step, t_mask, t_attn = r.timed(a.steps, a.warmup)
-    s = r.summary(ms_step, t_mask, t_attn)
-
+    r, e, s = measure(w, a, dev)
     line = {
         "metric": METRIC,
-        "value": round(s["step_tflops"], 3),
+        "value": e["step_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": e["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -703,43 +805,8 @@ def main():
         "config": {"workload": describe(w), "global_batch": w.B, "seq_len": w.N,
                    "heads": w.H, "head_dim": w.d, "block": w.block, "thr": w.thr,
                    "parallelism": "single GPU"},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": attn_kernel_name(w),
-            "achieved": round(s["attn_tflops"], 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(s["attn_frac_of_peak"], 4),
-            "traffic": measured_traffic() if a.config == "wan480" else None,
-        },
-        "pct_bf16_peak_attn": round(100 * s["attn_frac_of_peak"], 2),
-        "sparsity": {"blocks": round(s["sparsity_blocks"], 4),
-                     "token_pairs": round(s["sparsity_token_pairs"], 4),
-                     "kept_per_row_mean": round(s["kept_per_row_mean"], 2),
-                     "kept_per_row_max": s["kept_per_row_max"]},
-        "stages_ms": {"mask": round(t_mask, 4), "attention": round(t_attn, 4),
-                      "attention_median": round(float(np.median(r.attn_each)), 4),
-                      "attention_min": round(float(np.min(r.attn_each)), 4),
-                      "mask_over_attention": round(s["mask_over_attn"], 4),
-                      "mask_gbs": round(s["mask_gbs"], 1)},
-        "flops_eff_per_step": s["flops_eff"],
     }
-    if a.bwd_steps > 0:
-        tf, tb = r.backward(a.bwd_steps)
-        fb = 2.5 * s["flops_eff"]                  # five products per kept tile
-        line["backward"] = {"ms": round(tb, 4), "tflops_eff": round(fb / (tb * 1e-3) / 1e12, 3),
-                            "frac_of_peak": round(fb / (tb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                            "fwd_with_lse_ms": round(tf, 4), "steps": a.bwd_steps,
-                            "flops": "2.5 x the forward's effective FLOP (S, dP, dV, dK, dQ products of "
-                                     "kept tiles; the dQ pass also recomputes S and dP, not counted)"}
-    if a.path_steps > 0 and a.config == "wan480":
-        line["paths"] = paths_bench(r, a.path_steps)
-    if a.cold_reps > 0:
-        cm, ca = r.cold(a.cold_reps)
-        line["cold_cache"] = {"mask_ms": round(cm, 4), "attention_ms": round(ca, 4),
-                              "attn_tflops": round(s["flops_eff"] / (ca * 1e-3) / 1e12, 3),
-                              "reps": a.cold_reps,
-                              "how": "median; 512 MiB written before each step (outside the events)"}
+    line.update({k: v for k, v in e.items() if k not in ("workload", "ms_per_step", "step_tflops")})
     if not a.no_gemm_ref:
         mp = mfma_probe()
         if mp:
@@ -750,32 +817,15 @@ def main():
                                   "attn_over_gemm": round(s["attn_tflops"] / g, 4),
                                   "how": "torch.matmul bf16 8192x8192x8192 (vendor GEMM) on this box"}
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(r, s["flops_eff"])
+        line["cpu_baseline"] = cpu_baseline(r, s["flops_eff"], *CPU_SAMPLE.get(w.key, (1, 24)))
     if a.also and a.also != "none" and a.also != a.config:
         del r
         torch.cuda.empty_cache()
         w2 = WORKLOADS[a.also]
-        r2 = Runner(w2, dev)
-        m2, tm2, ta2 = r2.timed(max(3, a.steps // 10), max(1, a.warmup // 10))
-        s2 = r2.summary(m2, tm2, ta2)
-        line["also"] = {w2.key: {
-            "workload": describe(w2),
-            "ms_per_step": round(m2, 4),
-            "step_tflops": round(s2["step_tflops"], 3),
-            "attn_tflops": round(s2["attn_tflops"], 3),
-            "attn_kernel": attn_kernel_name(w2),
-            "pct_bf16_peak_attn": round(100 * s2["attn_frac_of_peak"], 2),
-            "mask_ms": round(tm2, 4),
-            "attention_ms": round(ta2, 4),
-            "mask_over_attention": round(s2["mask_over_attn"], 4),
-            "mask_gbs": round(s2["mask_gbs"], 1),
-            "sparsity_blocks": round(s2["sparsity_blocks"], 4),
-        }}
-        if a.bwd_steps > 0:
-            tf2, tb2 = r2.backward(max(2, a.bwd_steps // 10), warmup=1)
-            fb2 = 2.5 * s2["flops_eff"]
-            line["also"][w2.key]["backward"] = {"ms": round(tb2, 3), "tflops_eff": round(fb2 / (tb2 * 1e-3) / 1e12, 3),
-                                                "fwd_with_lse_ms": round(tf2, 3)}
+        r2, e2, s2 = measure(w2, a, dev)
+        if not a.no_cpu_baseline:
+            e2["cpu_baseline"] = cpu_baseline(r2, s2["flops_eff"], *CPU_SAMPLE.get(w2.key, (1, 24)))
+        line["also"] = {w2.key: e2}
     print(json.dumps(line), flush=True)
 
 

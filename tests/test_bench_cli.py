@@ -40,11 +40,23 @@ def test_stats_summary_from_kernel_trace(tmp_path):
 
 
 def test_traffic_figure_follows_the_source(tmp_path, monkeypatch):
-    # the committed counter summary counts only for the attention source it
+    # the committed counter summary counts only for the attention sources it
     # was taken from
-    t = tmp_path / "traffic.txt"
-    t.write_text("traffic_bytes_per_launch: 4.5e+09\nsource_sha256: " + bench._sha256(bench.ATTN_SRC) + "\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(t))
-    assert bench.measured_traffic() == 4.5e9
+    t = tmp_path / "attn_fwd_hunyuan720_traffic.txt"
+    t.write_text("traffic_bytes_per_launch: 4.5e+09\nsource_sha256: " + bench.attn_sources_sha() + "\n")
+    monkeypatch.setattr(bench, "traffic_file", lambda wl: str(tmp_path / f"attn_fwd_{wl}_traffic.txt"))
+    assert bench.measured_traffic("hunyuan720") == 4.5e9
+    assert bench.measured_traffic("wan480") is None
     t.write_text("traffic_bytes_per_launch: 4.5e+09\nsource_sha256: 0000\n")
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic("hunyuan720") is None
+
+
+def test_headline_is_the_720p_layer():
+    # the metric names ~90 % sparsity on the largest layer: the 118,800-token
+    # 720p one is the default workload, the 480p layer comes second
+    import argparse
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--config", default="hunyuan720"' in src
+    assert 'ap.add_argument("--also", default="wan480"' in src
+    from gen import WORKLOADS
+    assert WORKLOADS["hunyuan720"].n_valid == 118800
