@@ -50,6 +50,8 @@ _SIGS = {
     "bsa_build_centroid_mask": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P], _I),
     "bsa_block_sparse_attn_fwd_workspace": ([_I, _I, _I, _P], _Z),
     "bsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z, _P], _I),
+    "bsa_block_sparse_attn_fwd_noalloc_capacity": ([], _Z),
+    "bsa_block_sparse_attn_fwd_noalloc": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P], _I),
     "bsa_block_sparse_attn_fwd_lse": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _F, _P, _Z,
                                        _P], _I),
     "bsa_block_sparse_attn_bwd_workspace": ([_I, _I, _I, ctypes.POINTER(_Blocks), ctypes.POINTER(_Blocks)], _Z),

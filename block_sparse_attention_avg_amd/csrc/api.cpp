@@ -1,6 +1,7 @@
 // C ABI of libbsa: argument validation, workspace carving and kernel launch
 // (declarations and the contract of every entry point are in include/bsa.h).
 #include <algorithm>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -227,6 +228,66 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void*
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   return attn_fwd_impl(q, k, v, o, B, H, N, d, n_valid, block, qb, kb, kv_count, kv_index, kv_stride, scale,
                        nullptr, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward
+// The int32 table the forward needs (processing order of the query blocks,
+// or the tile table of variable blocks) lives in this file-scope device
+// array instead of a caller workspace. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): its
+// device address, one per GPU, comes from hipGetSymbolAddress and is kept
+// per device.
+namespace {
+constexpr size_t kScratchInts = (size_t)1 << 18;   // 1 MiB: B*H*(nqb+1) <= 262144
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_address(int32_t** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "attn_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(BSA_EUNSUPPORTED, "attn_fwd_noalloc: device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+      return hip_status(e, "attn_fwd_noalloc: hipGetSymbolAddress");
+    if (p == nullptr) return fail(BSA_EHIP, "attn_fwd_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(g_scratch_ptr[dev]);
+  return BSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t bsa_block_sparse_attn_fwd_noalloc_capacity(void) { return sizeof(int32_t) * kScratchInts; }
+
+int bsa_block_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                                      int d, int n_valid, int block, const bsa_blocks* qb, const bsa_blocks* kb,
+                                      const int32_t* kv_count, const int32_t* kv_index, int kv_stride, float scale,
+                                      hipStream_t stream) {
+  g_msg[0] = 0;
+  if (int e = check_shape(B, H, N, d, n_valid)) return e;
+  bsa::Blocks bq;
+  if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
+  const size_t need = bsa_block_sparse_attn_fwd_workspace(B, H, bq.nblocks, qb);
+  if (need > sizeof(int32_t) * kScratchInts)
+    return fail(BSA_ENOSPC,
+                "attn_fwd_noalloc: B*H*(nqb+1) = %zu int32 entries exceed the fixed scratch of %zu; "
+                "use bsa_block_sparse_attn_fwd with a workspace",
+                (size_t)B * H * ((size_t)bq.nblocks + 1), kScratchInts);
+  if (!q || !k || !v || !o || !kv_count || !kv_index) return fail(BSA_EINVAL, "attn_fwd_noalloc: null pointer");
+  int32_t* ws = nullptr;
+  if (int e = scratch_address(&ws)) return e;
+  return attn_fwd_impl(q, k, v, o, B, H, N, d, n_valid, block, qb, kb, kv_count, kv_index, kv_stride, scale,
+                       nullptr, ws, sizeof(int32_t) * kScratchInts, stream);
 }
 
 int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

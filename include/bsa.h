@@ -232,6 +232,32 @@ int bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                               hipStream_t stream);
 
 /*
+ * The forward above for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results as bsa_block_sparse_attn_fwd, with no workspace
+ * argument. The int32 table that the workspace would hold (B*H*(nqb+1)
+ * entries) lives in a fixed device array inside the library, one per GPU,
+ * held until the process ends; the call allocates nothing.
+ * Limit: B*H*(nqb+1) <= bsa_block_sparse_attn_fwd_noalloc_capacity() / 4
+ * (262144 entries, 1 MiB); larger problems get BSA_ENOSPC before anything is
+ * launched (use bsa_block_sparse_attn_fwd with a workspace).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams or threads) race and must be serialised by the
+ * caller. The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress). Every other argument, limit and error is that of
+ * bsa_block_sparse_attn_fwd.
+ */
+size_t bsa_block_sparse_attn_fwd_noalloc_capacity(void);
+int bsa_block_sparse_attn_fwd_noalloc(const void* q, const void* k,
+                                      const void* v, void* o, int B, int H,
+                                      int N, int d, int n_valid, int block,
+                                      const bsa_blocks* qb,
+                                      const bsa_blocks* kb,
+                                      const int32_t* kv_count,
+                                      const int32_t* kv_index, int kv_stride,
+                                      float scale, hipStream_t stream);
+
+/*
  * The forward above, also writing each row's softmax log-normaliser, which
  * the backward needs (NABLA summary, Contributi Chiave, "Accelerazione a Due
  * Fasi": the sparse attention runs in training as well):

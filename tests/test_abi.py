@@ -166,3 +166,20 @@ def test_fractal_order_capacity(lib):
     rc = lib.bsa_fractal_order(4, 8, 8, 4, 256, ctypes.cast(perm, ctypes.c_void_p), ctypes.cast(st, ctypes.c_void_p),
                                ctypes.cast(ln, ctypes.c_void_p), None, 4, ctypes.byref(nb))
     assert rc == 3 and nb.value == 16
+
+
+def test_noalloc_capacity_is_checked_before_any_launch(lib):
+    # past the fixed scratch the allocation-free forward refuses with
+    # BSA_ENOSPC before touching the GPU (dummy host pointers are never used)
+    cap = lib.bsa_block_sparse_attn_fwd_noalloc_capacity() // 4
+    assert cap == 1 << 18
+    buf = (ctypes.c_uint8 * 64)()
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+    H, nb = 64, cap // 64 + 1
+    st = lib.bsa_block_sparse_attn_fwd_noalloc(p, p, p, p, 1, H, nb * 64, 128, nb * 64, 64, None, None, p, p, nb,
+                                               ctypes.c_float(0.0), None)
+    assert st == 3
+    assert b"scratch" in lib.bsa_last_error_message()
+    # bad shapes are still refused first
+    assert lib.bsa_block_sparse_attn_fwd_noalloc(p, p, p, p, 0, H, 64, 128, 64, 64, None, None, p, p, 1,
+                                                 ctypes.c_float(0.0), None) == 1
