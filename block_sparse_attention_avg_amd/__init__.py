@@ -274,9 +274,9 @@ def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
         _qkv(o, "out")
     lib = load()
     qbc, kbc = (None if qb is None else qb._c()), (None if kb is None else kb._c())
-    ws_bytes = lib.bsa_block_sparse_attn_fwd_workspace(B, H, nqb, None if qbc is None else ctypes.byref(qbc))
-    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        ws_bytes = lib.bsa_block_sparse_attn_fwd_workspace(B, H, nqb, None if qbc is None else ctypes.byref(qbc))
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib.bsa_block_sparse_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d,
                                          n_valid, block, None if qbc is None else ctypes.byref(qbc),
                                          None if kbc is None else ctypes.byref(kbc), kv_count.data_ptr(),
@@ -313,9 +313,9 @@ def block_sparse_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("lse must have B*H*N entries")
     lib = load()
     qbc, kbc = (None if qb is None else qb._c()), (None if kb is None else kb._c())
-    ws_bytes = lib.bsa_block_sparse_attn_fwd_workspace(B, H, nqb, None if qbc is None else ctypes.byref(qbc))
-    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        ws_bytes = lib.bsa_block_sparse_attn_fwd_workspace(B, H, nqb, None if qbc is None else ctypes.byref(qbc))
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib.bsa_block_sparse_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                              lse.data_ptr(), B, H, N, d, n_valid, block,
                                              None if qbc is None else ctypes.byref(qbc),

@@ -190,10 +190,15 @@ int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes, const float
                            kv_index, kv_stride, stream);
 }
 
+// The order table alone (B*H*(nqb+1) int32): the least workspace the forward runs with.
+static size_t attn_fwd_min_ws(int B, int H, int nqb) { return round256(sizeof(int32_t) * (size_t)B * H * (nqb + 1)); }
+
 size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb, const bsa_blocks* qb) {
-  (void)qb;
   if (B <= 0 || H <= 0 || nqb < 0) return 0;
-  return round256(sizeof(int32_t) * (size_t)B * H * (nqb + 1));
+  // uniform blocks (self-attention: as many key as query blocks) over long
+  // rows also get room for the split over key segments (sized for d = 128)
+  if (qb == nullptr) return bsa::attn_fwd_ws_bytes(B * H, nqb, nqb, 128);
+  return attn_fwd_min_ws(B, H, nqb);
 }
 
 static int attn_fwd_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
@@ -211,14 +216,15 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* o, i
   if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
   if (int e = make_blocks(kb, block, n_valid, "key blocks", bk)) return e;
   if (kv_stride < 0 || (bk.nblocks > 0 && kv_stride < 1)) return fail(BSA_EINVAL, "attn_fwd: bad kv_stride");
-  const size_t need = bsa_block_sparse_attn_fwd_workspace(B, H, bq.nblocks, qb);
+  const size_t need = attn_fwd_min_ws(B, H, bq.nblocks);
   if (ws == nullptr || ws_bytes < need)
     return fail(BSA_ENOSPC, "attn_fwd: workspace %zu bytes < %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(BSA_EINVAL, "attn_fwd: workspace must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return hip_status(bsa::launch_attn_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), B * H, N, d,
                                          n_valid, bq, bk, kv_count, kv_index, kv_stride, sc,
-                                         static_cast<int32_t*>(ws), lse, stream),
+                                         static_cast<int32_t*>(ws), ws_bytes, lse, stream),
                     "attn_fwd");
 }
 
@@ -277,7 +283,7 @@ int bsa_block_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* 
   if (int e = check_shape(B, H, N, d, n_valid)) return e;
   bsa::Blocks bq;
   if (int e = make_blocks(qb, block, n_valid, "query blocks", bq)) return e;
-  const size_t need = bsa_block_sparse_attn_fwd_workspace(B, H, bq.nblocks, qb);
+  const size_t need = attn_fwd_min_ws(B, H, bq.nblocks);
   if (need > sizeof(int32_t) * kScratchInts)
     return fail(BSA_ENOSPC,
                 "attn_fwd_noalloc: B*H*(nqb+1) = %zu int32 entries exceed the fixed scratch of %zu; "

@@ -21,7 +21,20 @@ struct AttnArgs {
   int kv_stride;
   float sl2;                  // scale * log2(e)
   float* lse;                 // null, or [BH][N] natural-log row normaliser of the scaled scores
+  // Split over key segments (uniform blocks, long rows): every non-empty
+  // (query block I, key segment s) pair is an item; see split_plan_kernel.
+  const int32_t* items;       // [BH][max_items][4] {I, list offset, count, s}
+  const int32_t* item_base;   // [BH + 1] prefix of the per-head item counts
+  const int32_t* nseg;        // [BH][nqb] non-empty segments of each query block
+  const int32_t* slot_of;     // [BH][nqb][nsegs] item index of (I, s), or -1
+  float* part;                // [BH][max_items] partial results (kSplitSlotFloats each)
+  int max_items, nsegs;
 };
+
+// fp32 words of one partial result of a 64-row tile at d = 128: the O^T
+// accumulators of both waves as held in registers, then each lane's reference
+// row max (log2 units) and partial row sum.
+constexpr int kSplitSlotFloats = 2 * 4 * 16 * 64 + 2 * 2 * 64;
 
 // One-wave kernel (attn_fwd_1w.hip): uniform 64-token blocks, d = 128,
 // a.order set; `grid` workgroups of one wave.

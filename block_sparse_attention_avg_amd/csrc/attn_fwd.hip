@@ -49,10 +49,19 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // Read-only for the whole kernel: uniform loads through it become scalar loads.
 typedef __attribute__((address_space(4))) const int32_t cint;
 
-// Swizzle of the 16-byte piece index inside a K/V tile row.
+// Swizzle of the 16-byte piece index inside a K/V tile row (LDS position p of
+// row r holds data piece p ^ swz(r)). At d = 128 a row is 256 bytes, one full
+// sweep of the 64 four-byte LDS banks, so a piece index is a bank group. The
+// K operand reads (16 bytes per lane, 16 lanes per LDS cycle) cover 16
+// consecutive rows at one data piece: swz is a permutation of 0..15 over
+// any 16 aligned rows. The transposed V reads (8 bytes per lane, 32 lanes per
+// cycle) cover 4 consecutive rows x 4 consecutive data pieces: the rows'
+// swz values differ in bits 2-3, so the 16 (row, piece) pairs land in 16
+// distinct bank groups. (The former r0,r1,r2,r3 -> bits 1,2,0,3 layout left
+// those reads with 2-way conflicts.)
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (r >> 1) & 7;
 }
 
@@ -129,8 +138,16 @@ __device__ __forceinline__ float halves_sum(float x) {
 // most 64 tokens (each one chunk, loaded like a uniform block from its own
 // start), 2 = descriptor blocks of any length (keys gathered row by row into
 // 64-key chunks).
+template <int D>
+__device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, int ql, const f32x16* oacc,
+                                           float m_run, float l_run, lds_u8* Kp);
+
+// The tile walks the `cnt` list entries from `list` (a query block's whole
+// kept list, or one key segment of it). With `part` set it ends by storing
+// its unnormalised partial result there instead of output rows.
 template <int D, int KMODE>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
+                                          const int32_t* list, int cnt, float* part,
                                           lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
   constexpr int ROWB = D * 2;                  // bytes per K/V row
   constexpr int TILE = 64 * ROWB;              // bytes per K or V tile
@@ -178,9 +195,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   // exp2(-inf) = 0 rather than exp2(-inf + inf)
   float m_run = KMODE == 1 ? -1e30f : -INFINITY, l_run = 0.f;
 
-  const size_t qrow = (size_t)bh * a.nqb + I;
-  const int cnt = ((const cint*)a.kv_count)[qrow];
-  const int32_t* list = a.kv_index + qrow * a.kv_stride;
   const cint* slist = (const cint*)list;
 
   // ---- per-lane LDS offsets (loop invariant)
@@ -532,8 +546,41 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   }
   wait_vm<0>();                        // no load may still target LDS
 
-  // ---- epilogue: O = O^T / l, staged through the K tile (swizzled rows),
-  // stored as bf16 rows.
+  if (part) {
+    // partial result of one key segment: the registers as they are (rows of
+    // both waves, [wave][dg][r/4][lane][4]), then the reference max and row
+    // sum of each lane; combined by split_merge_kernel
+    if constexpr (D == 128) {
+      const int w64 = wave * 64 + lane;
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(part + (((wave * (D / 32) + dg) * 4 + r4) * 64 + lane) * 4) =
+              (f32x4){oacc[dg][4 * r4], oacc[dg][4 * r4 + 1], oacc[dg][4 * r4 + 2], oacc[dg][4 * r4 + 3]};
+      part[2 * (D / 32) * 16 * 64 + w64] = m_run;
+      part[2 * (D / 32) * 16 * 64 + 128 + w64] = l_run;
+    }
+    return;
+  }
+  store_rows<D>(a, bh, qs, ql, oacc, m_run, l_run, Kp);
+}
+
+// Epilogue of a 64-row tile (two waves, wave w owning rows 32w..32w+31):
+// O = O^T / l, staged through LDS (swizzled rows) and stored as bf16 rows,
+// plus the row log-normaliser when asked for. l_run is each lane's partial
+// row sum (the two wave halves hold the two halves of a row's keys).
+template <int D>
+__device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, int ql, const f32x16* oacc,
+                                           float m_run, float l_run, lds_u8* Kp) {
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = 64 * ROWB;
+  constexpr int PPR = ROWB / 16;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const size_t head_off = (size_t)bh * a.N * D;
   const float lt = halves_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int orow = 32 * wave + l32;
@@ -566,13 +613,44 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   }
 }
 
-template <int D, bool QVAR, int KMODE>
+template <int D, bool QVAR, int KMODE, bool SPLIT>
 __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = 64 * D * 2;
   __shared__ __align__(16) unsigned char Ks[TILE];
   __shared__ __align__(16) unsigned char Vs[TILE];
   __shared__ int tok[4 * 64];
   __shared__ int chunk_rows[4];
+
+  if constexpr (SPLIT) {
+    // One item (query block, key segment) per workgroup. The grid is an upper
+    // bound; the items of all heads are dealt to the XCDs as contiguous
+    // ranges of their order (head, then segment, then longest first), so the
+    // tiles running together on an XCD read the same key segment of a head.
+    const int total = ((const cint*)a.item_base)[a.bh];
+    const int L = blockIdx.x, x = L & 7, i = L >> 3;
+    const int per = total >> 3, rem = total & 7;
+    if (i >= per + (x < rem ? 1 : 0)) return;
+    const int flat = x * per + min(x, rem) + i;
+    int lo = 0, hi = a.bh - 1;                  // head: last bh with item_base[bh] <= flat
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (((const cint*)a.item_base)[mid] <= flat) lo = mid; else hi = mid - 1;
+    }
+    const int bh = lo;
+    const int k = flat - ((const cint*)a.item_base)[bh];
+    const cint* it = (const cint*)a.items + ((size_t)bh * a.max_items + k) * 4;
+    const int I = it[0], off = it[1], cnt = it[2];
+    int qs, ql;
+    a.qb.get(bh, I, qs, ql);
+    ql = min(ql, 64);
+    if (ql <= 0) return;
+    const size_t qrow = (size_t)bh * a.nqb + I;
+    float* part = ((const cint*)a.nseg)[qrow] > 1 ? a.part + ((size_t)bh * a.max_items + k) * kSplitSlotFloats
+                                                    : nullptr;
+    attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride + off, cnt, part, (lds_u8*)Ks,
+                        (lds_u8*)Vs, tok, chunk_rows);
+    return;
+  }
 
   // Flat id -> (head, tile). Consecutive workgroups are dealt round-robin to
   // the 8 XCDs, so workgroup 8i + x is the i-th one XCD x runs; XCD x takes a
@@ -611,7 +689,218 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
     ql = min(64, n0 - 64 * sub);
   }
   if (ql <= 0) return;
-  attn_tile<D, KMODE>(a, bh, I, qs, ql, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
+  const size_t qrow = (size_t)bh * a.nqb + I;
+  // counts outside [0, kv_stride] (a caller's contract) stay inside the row
+  const int cnt = min(max(((const cint*)a.kv_count)[qrow], 0), a.kv_stride);
+  attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride, cnt, nullptr, (lds_u8*)Ks, (lds_u8*)Vs,
+                      tok, chunk_rows);
+}
+
+// ---- split over key segments (uniform blocks, long rows)
+//
+// Per head, the kept list of every query block is cut where the key block id
+// crosses a multiple of `sg` into at most `nsegs` segments; every non-empty
+// (query block, segment) pair is an item, computed by one workgroup of the
+// forward above and, when its query block has more than one item, stored as
+// a partial result that split_merge_kernel combines. The items are ordered
+// segment-major (longest first inside a segment): tiles that run together on
+// an XCD then read the K/V blocks of one key segment, which its L2 holds
+// while they are reused. Scheduling only: every partial is the exact online
+// softmax of its segment's keys, merged in segment order.
+// Where each key segment starts in every query block's (ascending) list, one
+// wave per query block: segoff[row][s] = number of entries below s * sg;
+// nseg[row] = number of non-empty segments; slot_of[row][*] = -1.
+__global__ __launch_bounds__(1024) void split_rows_kernel(const int32_t* __restrict__ kv_count,
+                                                          const int32_t* __restrict__ kv_index, int kv_stride,
+                                                          int nqb, int nsegs, int sg, int32_t* __restrict__ segoff,
+                                                          int32_t* __restrict__ slot_of,
+                                                          int32_t* __restrict__ nseg) {
+  const int lane = threadIdx.x & 63;
+  const int I = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (I >= nqb) return;
+  const size_t row = (size_t)blockIdx.y * nqb + I;
+  const int cnt = min(max(kv_count[row], 0), kv_stride);
+  const int32_t* lst = kv_index + row * kv_stride;
+  int below = 0;                        // lane s: entries below s * sg
+  for (int c0 = 0; c0 < cnt; c0 += 64) {
+    const int J = c0 + lane < cnt ? lst[c0 + lane] : 0x7fffffff;
+    for (int s = 1; s < nsegs; ++s) {
+      const unsigned long long b = __ballot(J < s * sg);
+      if (lane == s) below += __popcll(b);
+    }
+  }
+  if (lane >= nsegs) below = cnt;      // lane nsegs: end of the list
+  const int nxt = __shfl_down(below, 1);
+  const int c_s = lane < nsegs ? nxt - below : 0;
+  if (lane < nsegs) {
+    segoff[row * nsegs + lane] = below;
+    slot_of[row * nsegs + lane] = -1;
+  }
+  const int ns = __popcll(__ballot(c_s > 0));
+  if (lane == 0) nseg[row] = ns;
+}
+
+// Item order of one head (one workgroup): a counting sort of the non-empty
+// (query block, segment) pairs by segment, then by descending count.
+__global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ kv_count, int kv_stride,
+                                                          int nqb, int nsegs, int sg, int max_items,
+                                                          const int32_t* __restrict__ segoff,
+                                                          int32_t* __restrict__ items, int32_t* __restrict__ slot_of,
+                                                          int32_t* __restrict__ n_items) {
+  extern __shared__ int hist[];          // [nsegs * (sg + 1)] bucket counts, then cursors
+  __shared__ int part[1025];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nbk = nsegs * (sg + 1);
+  const int npairs = nqb * nsegs;
+  for (int b = tid; b < nbk; b += 1024) hist[b] = 0;
+  __syncthreads();
+  // count of pair p = (I, s): the next segment's start (or the list end) minus its own
+  auto pair = [&](int p, int& I, int& s, int& off) -> int {
+    I = p / nsegs;
+    s = p - I * nsegs;
+    const size_t row = (size_t)bh * nqb + I;
+    off = segoff[row * nsegs + s];
+    const int end = s + 1 < nsegs ? segoff[row * nsegs + s + 1] : min(max(kv_count[row], 0), kv_stride);
+    return end - off;
+  };
+  for (int p = tid; p < npairs; p += 1024) {
+    int I, s, off;
+    const int c = pair(p, I, s, off);
+    if (c > 0) atomicAdd(&hist[s * (sg + 1) + (sg - min(c, sg))], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the buckets
+  const int per = (nbk + 1023) / 1024;
+  const int b0 = tid * per, b1 = min(nbk, b0 + per);
+  int loc = 0;
+  for (int b = b0; b < b1; ++b) loc += hist[b];
+  part[tid] = loc;
+  __syncthreads();
+  if (tid < 64) {                       // scan of the 1024 partial sums by one wave
+    int v[16], run = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      v[j] = part[tid * 16 + j];
+      run += v[j];
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (tid >= o) incl += t;
+    }
+    int ex = incl - run;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      part[tid * 16 + j] = ex;
+      ex += v[j];
+    }
+    if (tid == 63) part[1024] = incl;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int b = b0; b < b1; ++b) {
+    const int v = hist[b];
+    hist[b] = run;
+    run += v;
+  }
+  if (tid == 0) n_items[bh] = part[1024];
+  __syncthreads();
+  // scatter the items
+  for (int p = tid; p < npairs; p += 1024) {
+    int I, s, off;
+    const int c = pair(p, I, s, off);
+    if (c > 0) {
+      const int k = atomicAdd(&hist[s * (sg + 1) + (sg - min(c, sg))], 1);
+      int32_t* it = items + ((size_t)bh * max_items + k) * 4;
+      it[0] = I;
+      it[1] = off;
+      it[2] = c;
+      it[3] = s;
+      slot_of[((size_t)bh * nqb + I) * nsegs + s] = k;
+    }
+  }
+}
+
+// item_base[b] = sum of n_items over the heads before b; item_base[BH] = total.
+__global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __restrict__ n_items, int BH,
+                                                           int32_t* __restrict__ item_base) {
+  __shared__ int part[257];
+  const int per = (BH + 255) / 256;
+  const int b0 = threadIdx.x * per, b1 = min(BH, b0 + per);
+  int loc = 0;
+  for (int b = b0; b < b1; ++b) loc += n_items[b];
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    part[256] = run;
+  }
+  __syncthreads();
+  int run = part[threadIdx.x];
+  for (int b = b0; b < b1; ++b) {
+    item_base[b] = run;
+    run += n_items[b];
+  }
+  if (threadIdx.x == 0) item_base[BH] = part[256];
+}
+
+// Combines the partial results of query blocks with more than one item (in
+// segment order, online: each partial is rescaled to the running maximum of
+// the reference maxima) and writes their rows; query blocks with no kept key
+// block get zero rows (and lse -inf). Blocks with one item were written by
+// the forward itself.
+__global__ __launch_bounds__(128) void split_merge_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  __shared__ __align__(16) unsigned char stage[64 * D * 2];
+  const int bh = blockIdx.x / a.nqb, I = blockIdx.x - bh * a.nqb;
+  const size_t qrow = (size_t)bh * a.nqb + I;
+  const int ns = ((const cint*)a.nseg)[qrow];
+  if (ns == 1) return;
+  int qs, ql;
+  a.qb.get(bh, I, qs, ql);
+  ql = min(ql, 64);
+  if (ql <= 0) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
+  // the largest reference max over the partials, then their sum rescaled to it
+  constexpr int MOFF = 2 * (D / 32) * 16 * 64;
+  const float* base = a.part + (size_t)bh * a.max_items * kSplitSlotFloats;
+  const cint* slots = (const cint*)a.slot_of + qrow * a.nsegs;
+  float m = -1e30f;
+  for (int s = 0; s < a.nsegs; ++s) {
+    const int k = slots[s];
+    if (k >= 0) m = fmaxf(m, base[(size_t)k * kSplitSlotFloats + MOFF + wave * 64 + lane]);
+  }
+  float l = 0.f;
+  for (int s = 0; s < a.nsegs; ++s) {
+    const int k = slots[s];
+    if (k < 0) continue;
+    const float* p = base + (size_t)k * kSplitSlotFloats;
+    const float w = __builtin_amdgcn_exp2f(p[MOFF + wave * 64 + lane] - m);
+    l += p[MOFF + 128 + wave * 64 + lane] * w;
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p + (((wave * (D / 32) + dg) * 4 + r4) * 64 + lane) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oacc[dg][4 * r4 + j] += x[j] * w;
+      }
+  }
+  store_rows<D>(a, bh, qs, ql, oacc, m, l, (lds_u8*)stage);
 }
 
 // Processing order of uniform query blocks: longest first. The query blocks
@@ -725,13 +1014,56 @@ bool launch_qorder(const int32_t* counts, int BH, int n, int cap, int32_t* order
   return true;
 }
 
-// Key-block count from which uniform d = 128 attention runs one wave per tile.
+// Key-block count from which uniform d = 128 attention runs one wave per tile
+// (when the workspace is too small for the split path).
 constexpr int kOneWaveKeyBlocks = 1024;
+
+// Split over key segments: rows over at least kSplitMinKeyBlocks uniform key
+// blocks at d = 128, segments of kSplitSegBlocks key blocks (8 MiB of K and V,
+// twice an XCD's L2: at the 720p layer a concurrently running XCD still finds
+// most blocks in L2).
+constexpr int kSplitMinKeyBlocks = 1024;
+constexpr int kSplitSegBlocks = 384;
+
+namespace {
+struct SplitLayout {
+  int nsegs = 0, sg = 0, max_items = 0;
+  size_t segoff = 0, slot_of = 0, nseg = 0, n_items = 0, item_base = 0, items = 0, part = 0, end = 0;
+};
+size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
+// Workspace layout of the split path after the order table; nsegs = 0 when
+// the path does not apply.
+SplitLayout split_layout(int BH, int nqb, int nkb, int d) {
+  SplitLayout L;
+  L.end = r256(sizeof(int32_t) * (size_t)BH * (nqb + 1));
+  if (d != 128 || nkb < kSplitMinKeyBlocks || nqb <= 0) return L;
+  const int S = (nkb + kSplitSegBlocks - 1) / kSplitSegBlocks;
+  const int sg = (nkb + S - 1) / S;
+  if (S < 2 || S > 63 || sizeof(int) * (size_t)S * (sg + 1) > 64 * 1024) return L;
+  const size_t pairs = (size_t)BH * nqb * S;
+  if ((size_t)nqb * S > 0x7fffffff / 8) return L;
+  L.nsegs = S;
+  L.sg = sg;
+  L.max_items = nqb * S;
+  size_t o = L.end;
+  L.segoff = o; o += r256(4 * pairs);
+  L.slot_of = o; o += r256(4 * pairs);
+  L.nseg = o; o += r256(4 * (size_t)BH * nqb);
+  L.n_items = o; o += r256(4 * (size_t)BH);
+  L.item_base = o; o += r256(4 * ((size_t)BH + 1));
+  L.items = o; o += r256(16 * pairs);
+  L.part = o; o += r256(sizeof(float) * (size_t)kSplitSlotFloats * pairs);
+  L.end = o;
+  return L;
+}
+}  // namespace
+
+size_t attn_fwd_ws_bytes(int BH, int nqb, int nkb, int d) { return split_layout(BH, nqb, nkb, d).end; }
 
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int BH, int N, int d, int n_valid, const Blocks& qb, const Blocks& kb,
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
-                           float scale, int32_t* tile_ws, float* lse, hipStream_t s) {
+                           float scale, int32_t* tile_ws, size_t ws_bytes, float* lse, hipStream_t s) {
   if (BH == 0) return hipSuccess;
   // padding rows of O are zero (and their lse -inf): folded into the ordering
   // launch when there is one, else a launch of their own
@@ -765,6 +1097,41 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int kmode = kvar ? 2 : kshort ? 1 : 0;
   a.tile_base = tile_ws;
   a.order = nullptr;
+  a.items = nullptr; a.item_base = nullptr; a.nseg = nullptr; a.slot_of = nullptr; a.part = nullptr;
+  a.max_items = 0; a.nsegs = 0;
+  // Long uniform rows with a workspace of the full size: split over key
+  // segments (plan, items, merge).
+  if (!qvar && kmode == 0 && qb.start == nullptr && kb.start == nullptr && d == 128) {
+    const SplitLayout L = split_layout(BH, qb.nblocks, kb.nblocks, d);
+    if (L.nsegs >= 2 && ws_bytes >= L.end) {
+      char* w = reinterpret_cast<char*>(tile_ws);
+      int32_t* segoff = reinterpret_cast<int32_t*>(w + L.segoff);
+      a.slot_of = reinterpret_cast<int32_t*>(w + L.slot_of);
+      a.nseg = reinterpret_cast<int32_t*>(w + L.nseg);
+      int32_t* n_items = reinterpret_cast<int32_t*>(w + L.n_items);
+      a.item_base = reinterpret_cast<int32_t*>(w + L.item_base);
+      a.items = reinterpret_cast<int32_t*>(w + L.items);
+      a.part = reinterpret_cast<float*>(w + L.part);
+      a.max_items = L.max_items;
+      a.nsegs = L.nsegs;
+      a.tiles = 0;
+      a.bh = BH;
+      if (!pad_done) zero_pad();
+      const size_t lds = sizeof(int) * (size_t)L.nsegs * (L.sg + 1);
+      split_rows_kernel<<<dim3((qb.nblocks + 15) / 16, BH), 1024, 0, s>>>(
+          kv_count, kv_index, kv_stride, qb.nblocks, L.nsegs, L.sg, segoff, const_cast<int32_t*>(a.slot_of),
+          const_cast<int32_t*>(a.nseg));
+      split_plan_kernel<<<BH, 1024, lds, s>>>(kv_count, kv_stride, qb.nblocks, L.nsegs, L.sg, L.max_items, segoff,
+                                              const_cast<int32_t*>(a.items), const_cast<int32_t*>(a.slot_of),
+                                              n_items);
+      split_prefix_kernel<<<1, 256, 0, s>>>(n_items, BH, const_cast<int32_t*>(a.item_base));
+      const long long grid = 8LL * (((long long)BH * L.max_items + 7) / 8);
+      if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+      attn_fwd_kernel<128, false, 0, true><<<(int)grid, 128, 0, s>>>(a);
+      split_merge_kernel<<<BH * qb.nblocks, 128, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (qvar) {
     tile_base_kernel<<<BH, 256, 0, s>>>(qb, tile_ws);
     a.tiles = (N + 63) / 64 + qb.nblocks;
@@ -790,7 +1157,7 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   // (measured at 1857 key blocks: +8..11 %; at 512: -12 %).
   if (d == 128 && !qvar && qb.start == nullptr && kmode == 0 && a.order && kb.nblocks >= kOneWaveKeyBlocks)
     return launch_attn_fwd_1w(a, (int)grid, s);
-#define BSA_ATTN(DD, QV, KM) attn_fwd_kernel<DD, QV, KM><<<(int)grid, 128, 0, s>>>(a)
+#define BSA_ATTN(DD, QV, KM) attn_fwd_kernel<DD, QV, KM, false><<<(int)grid, 128, 0, s>>>(a)
 #define BSA_ATTN_K(DD, QV)               \
   do {                                   \
     if (kmode == 2) BSA_ATTN(DD, QV, 2); \

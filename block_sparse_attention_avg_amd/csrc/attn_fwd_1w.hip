@@ -50,10 +50,19 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // Read-only for the whole kernel: uniform loads through it become scalar loads.
 typedef __attribute__((address_space(4))) const int32_t cint;
 
-// Swizzle of the 16-byte piece index inside a K/V tile row.
+// Swizzle of the 16-byte piece index inside a K/V tile row (LDS position p of
+// row r holds data piece p ^ swz(r)). At d = 128 a row is 256 bytes, one full
+// sweep of the 64 four-byte LDS banks, so a piece index is a bank group. The
+// K operand reads (16 bytes per lane, 16 lanes per LDS cycle) cover 16
+// consecutive rows at one data piece: swz is a permutation of 0..15 over
+// any 16 aligned rows. The transposed V reads (8 bytes per lane, 32 lanes per
+// cycle) cover 4 consecutive rows x 4 consecutive data pieces: the rows'
+// swz values differ in bits 2-3, so the 16 (row, piece) pairs land in 16
+// distinct bank groups. (The former r0,r1,r2,r3 -> bits 1,2,0,3 layout left
+// those reads with 2-way conflicts.)
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (r >> 1) & 7;
 }
 

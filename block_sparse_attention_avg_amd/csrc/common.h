@@ -117,7 +117,10 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int BH, int N, int d, int n_valid, const Blocks& qb, const Blocks& kb,
                            const int32_t* kv_count, const int32_t* kv_index, int kv_stride,
-                           float scale, int32_t* tile_ws, float* lse, hipStream_t s);
+                           float scale, int32_t* tile_ws, size_t ws_bytes, float* lse, hipStream_t s);
+// Workspace bytes of the forward with every path available (the order table,
+// plus the split path's tables and partial results for long uniform rows).
+size_t attn_fwd_ws_bytes(int BH, int nqb, int nkb, int d);
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const uint16_t* dout, const float* lse, int BH, int N, int d, int n_valid,
                            const Blocks& qb, const Blocks& kb, const int32_t* kv_count, const int32_t* kv_index,

@@ -376,16 +376,20 @@ def test_hunyuan720_sampled(gpu_lib, part):
         _attn_case(gpu_lib, w, q, k, v, [4, 19], 5)
 
 
-def test_attn_long_rows_one_wave_path(gpu_lib):
-    # >= 1024 key blocks at d = 128 with uniform blocks selects the one-wave
-    # kernel: random kept lists (dense and single-block rows, the ragged last
-    # block) on a ragged length, sampled query blocks against the oracle, then
-    # repeat runs and poisoned padding must give the same bits
+@pytest.mark.parametrize("path", ["split", "one_wave"])
+def test_attn_long_rows(gpu_lib, path):
+    # >= 1024 uniform key blocks at d = 128: with the full workspace the rows
+    # run split over key segments (plan, items, partials, merge); with only
+    # the order table the one-wave kernel runs them whole. Random kept lists
+    # (a dense row, rows inside one segment, a row keeping nothing, the
+    # ragged last block) on a ragged length, sampled query blocks (and their
+    # log-normalisers) against the oracle, then repeat runs and poisoned
+    # padding must give the same bits
     bsa = gpu_lib
     H, d, nkb = 2, 128, 1025
     N = nkb * 64
     nv = N - 37
-    say(f"attention one-wave path H={H} N={N} n_valid={nv}")
+    say(f"attention long rows ({path}) H={H} N={N} n_valid={nv}")
     rng = np.random.default_rng(1025)
     x = rng.normal(size=(3, 1, H, N, d)).astype(np.float32)
     x[:, :, :, nv:] = 0
@@ -394,10 +398,15 @@ def test_attn_long_rows_one_wave_path(gpu_lib):
     assert len(st) == nkb
     keep = rng.random((H, nkb, nkb)) < 0.03
     keep[:, :, nkb - 1] |= rng.random((H, nkb)) < 0.3       # ragged last key block
+    keep[:, :, 0] |= ~keep.any(2)
     keep[:, 5, :] = True                                     # one dense row
     keep[:, 9, :] = False
     keep[:, 9, 700] = True                                   # one single-block row
-    keep[:, :, 0] |= ~keep.any(2)
+    keep[:, 10, :] = False
+    keep[:, 10, 260:300] = True                              # a row inside one key segment
+    keep[:, 11, :] = False                                   # a row keeping nothing
+    keep[:, nkb - 1, :] = False
+    keep[:, nkb - 1, [3, 255, 256, 511, 512, 1024]] = True   # segment edges, ragged last query block
     cnt = keep.sum(2).astype(np.int32)
     idx = np.full((H, nkb, nkb), -1, np.int32)
     for h in range(H):
@@ -406,19 +415,36 @@ def test_attn_long_rows_one_wave_path(gpu_lib):
             idx[h, i, :len(ids)] = ids
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     cd, id_ = torch.from_numpy(cnt[None]).cuda(), torch.from_numpy(idx[None]).cuda()
-    o1 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    lib = bsa.load()
+    full = lib.bsa_block_sparse_attn_fwd_workspace(1, H, nkb, None)
+    small = (4 * H * (nkb + 1) + 255) // 256 * 256
+    assert full > small
+    ws = torch.empty(full if path == "split" else small, dtype=torch.uint8, device="cuda")
+    o1, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cd, id_, n_valid=nv, workspace=ws)
     o = _np(o1)
-    blocks = sorted({0, 5, 9, nkb - 1} | set(rng.choice(nkb, 10, replace=False).tolist()))
+    lse = lse.cpu().numpy()
+    blocks = sorted({0, 5, 9, 10, 11, nkb - 1} | set(rng.choice(nkb, 10, replace=False).tolist()))
     for h in range(H):
-        ref = oa.masked_attention(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), st, ln, st, ln, keep[h],
-                                  blocks=blocks)
+        args = (_np(q[0, h]), _np(k[0, h]))
+        ref = oa.masked_attention(*args, _np(v[0, h]), st, ln, st, ln, keep[h], blocks=blocks)
         _check_out(o[0, h], ref, _rows_of(st, ln, blocks), f"head {h} ({len(blocks)} query blocks)")
+        ref_lse = oa.masked_attention_lse(*args, st, ln, st, ln, keep[h])
+        rows = _rows_of(st, ln, blocks)
+        fin = np.isfinite(ref_lse[rows])
+        assert np.array_equal(fin, np.isfinite(lse[0, h, rows]))
+        # the one-wave kernel sums the bf16-rounded P that PV multiplies (so O
+        # is a convex combination with exactly those weights): its row sum is
+        # within a relative 2^-8 of the exact one, its log within 4e-3
+        tol = 1e-3 if path == "split" else 4e-3
+        assert np.abs(lse[0, h, rows][fin] - ref_lse[rows][fin]).max() <= tol
     assert (o[:, :, nv:] == 0).all()
-    o2 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    assert (o[:, :, st[11]:st[11] + 64] == 0).all()          # no kept block: zero rows
+    assert np.isneginf(lse[:, :, nv:]).all()
+    o2 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv, workspace=ws)
     assert torch.equal(o1, o2)
     for t in (qd, kd, vd):
         t[:, :, nv:] = float("nan")
-    o3 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    o3 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv, workspace=ws)
     assert torch.equal(o1, o3)
 
 
