@@ -3,7 +3,8 @@
 // window union; Sparse VideoGen2 summary, Metodologia B for the
 // size-weighted centroid variant).
 //
-// One workgroup (4 waves) owns R consecutive rows of one head's reduced map.
+// One workgroup (4 waves, 8 for rows of 1025..2048 key blocks) owns R
+// consecutive rows of one head's reduced map.
 //
 // Phase 1 -- scores. s[r][J] = scale * qbar_r . kbar_J (+ log n_J) for all
 // key blocks, on fp32 MFMA 16x16x4 (A = 16 pooled query rows, B = 16 pooled
@@ -31,15 +32,29 @@
 
 namespace bsa {
 
+// Rows of 1025..2048 key blocks (the 118,800-token layer): 8 waves share
+// the 16 score rows, two per SIMD, so one wave's LDS atomics and scans wait
+// while the other issues (measured: mask stage 1.22 -> 0.99 ms at 1857 key
+// blocks; 16 waves, or the rows streamed from LDS instead of registers, were
+// slower).
+#ifndef BSA_SEL_W2048
+#define BSA_SEL_W2048 8
+#endif
+#ifndef BSA_SEL_E2048
+#define BSA_SEL_E2048 32
+#endif
+
 namespace {
 constexpr int kIdxBits = 13;          // supports nkb <= 8192
 constexpr int kKeyBits = 30 + kIdxBits;
 constexpr int kDigit = 8;
 constexpr int kPasses = (kKeyBits + kDigit - 1) / kDigit;   // 6
 constexpr int kBins = 1 << kDigit;
-constexpr int kSelWaves = 4;          // waves per workgroup
 constexpr float kMassScale = 0x1p31f; // block masses in 2^-31 fixed point
-constexpr int kHist = 512;           // histogram words per wave
+// histogram words per wave: 8 private copies of the first-digit histogram
+// (64 bins), or 4 with 16 waves sharing the LDS; later passes use 256
+template <int W>
+constexpr int hist_words() { return W >= 16 ? 256 : 512; }
 constexpr int kDigit0 = 192;          // first-digit value of p = 2^-31 (bits(p) >> 22)
 }  // namespace
 
@@ -48,13 +63,13 @@ constexpr int kDigit0 = 192;          // first-digit value of p = 2^-31 (bits(p)
 // below, but every pass streams registers instead of re-reading and
 // re-converting the scores. Writes the kept ids in ascending order and
 // returns their count (lane-uniform).
-template <int E>
+template <int E, int COPIES>
 __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float thr, int row,
                                                const int32_t* ksz, const Window& win,
                                                unsigned long long* h, int32_t* out, int lane) {
-  // per element: pb = bits of p (the key is pb << 13 | 8191 - j) and the
-  // fixed-point mass mm = floor(p * 2^31)
-  uint32_t pb[E], mm[E];
+  // per element: pb = bits of p (the key is pb << 13 | 8191 - j); its
+  // fixed-point mass floor(p * 2^31) is recomputed where needed (mass_of)
+  uint32_t pb[E];
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
@@ -71,9 +86,9 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
     // exp(s - max) as exp2 on the hardware unit: relative error ~1e-6
     const float pj = j < nkb ? __builtin_amdgcn_exp2f((__uint_as_float(pb[t]) - mx) * 1.4426950408889634f) : 0.f;
     pb[t] = __float_as_uint(pj);
-    mm[t] = (uint32_t)(pj * kMassScale);
-    z += mm[t];
+    z += (uint32_t)(pj * kMassScale);
   }
+  auto mass_of = [&](int t) -> uint32_t { return (uint32_t)(__uint_as_float(pb[t]) * kMassScale); };
   auto key_of = [&](int t) -> unsigned long long {
     return ((unsigned long long)pb[t] << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - (lane + kWave * t));
   };
@@ -113,7 +128,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
           if (c) {
             const int r = at + __popcll(bal & ((1ull << lane) - 1ull));
             slot[2 * r] = kt;
-            slot[2 * r + 1] = mm[t];
+            slot[2 * r + 1] = mass_of(t);
           }
           at += __popcll(bal);
         }
@@ -143,18 +158,20 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
     if (pass == 0) {
       // First digit (key bits 42..35 = bits 29..22 of p): a block with mass
       // has p >= 2^-31, so its digit is in [kDigit0, 255) -- 64 bins, one per
-      // lane, accumulated in 8 private copies (lanes l, l+8, ... share one).
-      unsigned long long* h0 = h;                  // [8][64]
+      // lane, accumulated in COPIES private copies (lanes l, l+COPIES, ...
+      // share one).
+      unsigned long long* h0 = h;                  // [COPIES][64]
 #pragma unroll
-      for (int q = 0; q < 8; ++q) h0[q * kWave + lane] = 0;
+      for (int q = 0; q < COPIES; ++q) h0[q * kWave + lane] = 0;
       wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < E; ++t)
-        if (mm[t]) atomicAdd(&h0[(lane & 7) * kWave + ((pb[t] >> 22) - kDigit0)], (unsigned long long)mm[t]);
+        if (const uint32_t mt = mass_of(t))
+          atomicAdd(&h0[(lane & (COPIES - 1)) * kWave + ((pb[t] >> 22) - kDigit0)], (unsigned long long)mt);
       wave_lds_sync();
       unsigned long long v = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v += h0[q * kWave + lane];
+      for (int q = 0; q < COPIES; ++q) v += h0[q * kWave + lane];
       const unsigned long long through = wave_incl_scan_u64(v, lane);
       const int b0 = wave_min_i32(through >= tint ? lane : 1 << 30);
       below = __shfl(through - v, b0);
@@ -168,8 +185,9 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
 #pragma unroll
     for (int t = 0; t < E; ++t) {
       const unsigned long long kt = key_of(t);
-      if ((kt >> (shift + width)) == prefix && mm[t])
-        atomicAdd(&h[(kt >> shift) & ((1 << width) - 1)], (unsigned long long)mm[t]);
+      const uint32_t mt = mass_of(t);
+      if ((kt >> (shift + width)) == prefix && mt)
+        atomicAdd(&h[(kt >> shift) & ((1 << width) - 1)], (unsigned long long)mt);
     }
     wave_lds_sync();
     // lane owns bins [4*lane, 4*lane+4)
@@ -218,15 +236,15 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   return base;
 }
 
-template <int D, int R, int E>
-__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
+template <int D, int R, int E, int W>
+__global__ __launch_bounds__(64 * W) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
     Sizes sz, float thr, float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
     int kv_stride) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
   unsigned long long* hist =
-      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [4][kBins]
+      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [W][kHist]
 
   constexpr int KQ = D / 4;
   const int bh = blockIdx.y;
@@ -260,12 +278,19 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
       b[4 * s4 + 0] = v.x; b[4 * s4 + 1] = v.y; b[4 * s4 + 2] = v.z; b[4 * s4 + 3] = v.w;
     }
   };
-  float b[KQ], bn[KQ] = {};
-  if (wave < ntiles) load_b(wave, b);
-  for (int t = wave; t < ntiles; t += kSelWaves) {
+  // the next tile's key rows are prefetched into registers when few waves
+  // share the CU; with more waves the others hide the load latency
+  constexpr bool PF = W <= 4;
+  float b[KQ], bn[PF ? KQ : 1] = {};
+  if (PF && wave < ntiles) load_b(wave, b);
+  for (int t = wave; t < ntiles; t += W) {
     const int key = t * 16 + i16;
     const bool kok = key < nkb;
-    if (t + kSelWaves < ntiles) load_b(t + kSelWaves, bn);
+    if constexpr (PF) {
+      if (t + W < ntiles) load_b(t + W, bn);
+    } else {
+      load_b(t, b);
+    }
     // four independent accumulation chains, summed at the end
     f32x4 acc4[4];
 #pragma unroll
@@ -287,14 +312,16 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
         if (rr < R) sc[rr * nkb_pad + key] = excluded ? -INFINITY : acc[v] * scale + bias;
       }
     }
+    if constexpr (PF) {
 #pragma unroll
-    for (int s4 = 0; s4 < KQ; ++s4) b[s4] = bn[s4];
+      for (int s4 = 0; s4 < KQ; ++s4) b[s4] = bn[s4];
+    }
   }
   __syncthreads();
 
   // ---------------- phase 2: per-row CDF selection
-  unsigned long long* h = hist + wave * kHist;
-  for (int rr = wave; rr < R; rr += kSelWaves) {
+  unsigned long long* h = hist + wave * hist_words<W>();
+  for (int rr = wave; rr < R; rr += W) {
     const int row = row0 + rr;
     if (row >= nqb) break;
     const size_t orow = (size_t)bh * nqb + row;
@@ -305,7 +332,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
     }
     float* sr = sc + rr * nkb_pad;
     if constexpr (E > 0) {
-      const int n = select_row_regs<E>(sr, nkb, thr, row, sz.krow(bh, nkb),
+      const int n = select_row_regs<E, W >= 16 ? 4 : 8>(sr, nkb, thr, row, sz.krow(bh, nkb),
                                        win, h, out, lane);
       if (lane == 0) kv_count[orow] = n;
       continue;
@@ -393,18 +420,18 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
   }
 }
 
-template <int D, int R, int E>
+template <int D, int R, int E, int W = 4>
 static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
                                   const Sizes& sz, float thr, float scale, const Window& win, int32_t* kv_count,
                                   int32_t* kv_index, int kv_stride, hipStream_t s) {
   const int nkb_pad = (nkb + 3) & ~3;
-  const size_t lds = (size_t)R * nkb_pad * sizeof(float) + kSelWaves * kHist * sizeof(unsigned long long);
-  auto kern = select_kernel<D, R, E>;
+  const size_t lds = (size_t)R * nkb_pad * sizeof(float) + W * hist_words<W>() * sizeof(unsigned long long);
+  auto kern = select_kernel<D, R, E, W>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((nqb + R - 1) / R, BH);
-  kern<<<grid, 64 * kSelWaves, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, sz, thr, scale, win,
+  kern<<<grid, 64 * W, lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, sz, thr, scale, win,
                               kv_count, kv_index, kv_stride);
   return hipGetLastError();
 }
@@ -416,11 +443,13 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
   if (BH == 0 || nqb == 0) return hipSuccess;
 #define BSA_SEL(DD, RR, EE) \
   launch_select_t<DD, RR, EE>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win, kv_count, kv_index, kv_stride, s)
+#define BSA_SELW(DD, RR, EE, WW) \
+  launch_select_t<DD, RR, EE, WW>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win, kv_count, kv_index, kv_stride, s)
   // rows of up to 2048 key blocks are selected from registers (E per lane)
   if (d == 128) {
     if (nkb <= 512) return BSA_SEL(128, 16, 8);
     if (nkb <= 1024) return BSA_SEL(128, 16, 16);
-    if (nkb <= 2048) return BSA_SEL(128, 16, 32);
+    if (nkb <= 2048) return BSA_SELW(128, 16, BSA_SEL_E2048, BSA_SEL_W2048);
     if (nkb <= 4096) return BSA_SEL(128, 8, 0);
     return BSA_SEL(128, 4, 0);
   }
@@ -429,6 +458,7 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
   if (nkb <= 2048) return BSA_SEL(64, 16, 32);
   if (nkb <= 4096) return BSA_SEL(64, 8, 0);
   return BSA_SEL(64, 4, 0);
+#undef BSA_SELW
 #undef BSA_SEL
 }
 
