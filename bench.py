@@ -445,10 +445,18 @@ def mfma_probe():
 
 
 def attn_kernel_name(w) -> str:
-    # the library runs one wave per tile for uniform d = 128 rows over at
-    # least 1024 key blocks, two waves per tile otherwise
+    # with the full workspace the library splits uniform d = 128 rows over at
+    # least 1024 key blocks into key segments (plan, items, merge); two waves
+    # per 64-row tile otherwise
     nb = -(-w.n_valid // w.block)
-    return "attn_fwd_1w_kernel" if (w.d == 128 and nb >= 1024) else "attn_fwd_kernel"
+    if w.d == 128 and nb >= 1024:
+        return "attn_fwd_kernel (items over key segments) + split_rows/plan/prefix/merge kernels"
+    return "attn_fwd_kernel"
+
+
+# Kernels launched by one attention-forward call (summed against its events).
+ATTN_CALL_KERNELS = ("bsa::attn_fwd", "bsa::split_", "bsa::qorder_kernel", "bsa::zero_rows_kernel",
+                     "bsa::tile_base_kernel")
 
 
 def dense_gemm_ref(dev, n: int = 8192, reps: int = 20):
@@ -611,13 +619,19 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
                 js = [json.loads(l) for l in f if l.startswith("{")]
             if js:
                 b = js[-1]
-                att = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::attn_fwd")]
+                st = rocprof_stats(dirs[0])
+                att = [x for x in st if x[0].startswith("bsa::attn_fwd")]
+                call = [x for x in st if x[0].startswith(ATTN_CALL_KERNELS)]
                 lines.append(f"bench (same run): attention stage {b['stages_ms']['attention'] * 1e3:.1f} us per "
                              f"call (HIP events around the C-ABI call), roofline.achieved "
                              f"{b['roofline']['achieved']} TFLOP/s")
                 if att:
                     lines.append(f"rocprof {att[0][0]} average {att[0][2]:.1f} us "
                                  f"(ratio events / kernel {b['stages_ms']['attention'] * 1e3 / att[0][2]:.3f})")
+                if len(call) > 1:
+                    tot = sum(x[2] for x in call)
+                    lines.append(f"rocprof kernels of one attention call ({', '.join(x[0] for x in call)}): "
+                                 f"{tot:.1f} us (ratio events / kernels {b['stages_ms']['attention'] * 1e3 / tot:.3f})")
                 if "backward" in b:
                     bw = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::bwd_") or
                           x[0].startswith("bsa::csc_")]
@@ -638,10 +652,20 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
             lines.append(f"{k} (mean per dispatch): " + " ".join(vals))
     elif kind == "traffic":
         fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+        # `kernel`: comma-separated name prefixes; the per-dispatch means of
+        # every matching kernel are summed (the kernels of one attention call)
+        prefixes = tuple(p for p in kernel.split(",") if p)
+
+        def summed(d, counter):
+            names = sorted({_short(r["Kernel_Name"]) for r in _csv_rows(os.path.join(d, "run_counter_collection.csv"))
+                            if _short(r["Kernel_Name"]).startswith(prefixes)})
+            vals = [rocprof_counter(d, counter, nm) for nm in names]
+            return sum(v for v, _ in vals), min((n for _, n in vals), default=0), names
         kern = kernel
         copy = "bsa::permute_kernel<16>"
-        f_att, n1 = rocprof_counter(fetch_dir, "FETCH_SIZE", kern)
-        w_att, n2 = rocprof_counter(write_dir, "WRITE_SIZE", kern)
+        f_att, n1, names = summed(fetch_dir, "FETCH_SIZE")
+        w_att, n2, _ = summed(write_dir, "WRITE_SIZE")
+        kern = " + ".join(names)
         f_cp, n3 = rocprof_counter(cfetch_dir, "FETCH_SIZE", copy)
         w_cp, n4 = rocprof_counter(cwrite_dir, "WRITE_SIZE", copy)
         gib = 1024.0 ** 3
