@@ -850,7 +850,12 @@ def main():
         if not a.no_cpu_baseline:
             e2["cpu_baseline"] = cpu_baseline(r2, s2["flops_eff"], *CPU_SAMPLE.get(w2.key, (1, 24)))
         line["also"] = {w2.key: e2}
+        del r2
     print(json.dumps(line), flush=True)
+    # leave no device work or allocation to interpreter teardown (where a
+    # profiler's own finaliser may already have run)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

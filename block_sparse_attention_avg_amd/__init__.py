@@ -75,11 +75,16 @@ _SIGS = {
 EXPORTS = tuple(_SIGS)
 
 
-def load(path: str = LIB_PATH):
-    """Loads libbsa.so (once). Raises if it is missing: there is no fallback."""
+def load(path: Optional[str] = None):
+    """Loads libbsa.so (once). Raises if it is missing: there is no fallback.
+
+    The path defaults to the in-tree build; BSA_LIBRARY names another build of
+    the same library (the host-sanitized one that the CPU tests run under).
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("BSA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise BsaError(f"{path} not found; build it with `python -m block_sparse_attention_avg_amd._build`")
     lib = ctypes.CDLL(path)

@@ -45,13 +45,52 @@ def _hipcc() -> str:
 EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_fwd_1w.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the whole
+# library (device code is built as usual): the argument checks, descriptor
+# conversions and host functions of the C ABI run instrumented on the CPU.
+SAN_OUT = os.path.join(OUT, "san")
+SAN_LIB = os.path.join(OUT, "libbsa_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out = SAN_OUT if sanitize else OUT
+    obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), *(SAN_FLAGS if sanitize else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Builds _build/libbsa_san.so (host code under ASan + UBSan). It needs the
+    sanitizer runtime preloaded (asan_runtime()) in the process that loads it."""
+    os.makedirs(SAN_OUT, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, True), SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    r = subprocess.run([os.path.join(os.path.dirname(_hipcc()), "..", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("shared AddressSanitizer runtime not found")
+    return path
 
 
 def build(verbose: bool = False) -> str:
@@ -76,5 +115,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)
