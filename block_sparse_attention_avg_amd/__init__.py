@@ -41,6 +41,7 @@ _I, _F, _P, _Z = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
 _SIGS = {
     "bsa_abi_version": ([], _I),
+    "bsa_lds_swizzle": ([_I, _I], _I),
     "bsa_strerror": ([_I], ctypes.c_char_p),
     "bsa_last_error_message": ([], ctypes.c_char_p),
     "bsa_pool_blocks": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "lds_tile.h"
 
 namespace {
 
@@ -90,6 +91,11 @@ int make_window(const bsa_window* w, int nqb, int nkb, bsa::Window& out) {
 extern "C" {
 
 int bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+int bsa_lds_swizzle(int d, int row) {
+  if (d != 64 && d != 128) return -1;
+  return d == 128 ? bsa::swz<128>(row & 15) : bsa::swz<64>(row & 15);
+}
 
 const char* bsa_strerror(int status) {
   switch (status) {

@@ -31,88 +31,11 @@
 //                      its key order matches the accumulator layout of S^T.
 // O is divided by the row sum once at the end, staged through LDS and
 // written as bf16 rows.
-#include "attn.h"
+#include "lds_tile.h"
 
 #include <math.h>
 
 namespace bsa {
-
-namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-// Read-only for the whole kernel: uniform loads through it become scalar loads.
-typedef __attribute__((address_space(4))) const int32_t cint;
-
-// Swizzle of the 16-byte piece index inside a K/V tile row (LDS position p of
-// row r holds data piece p ^ swz(r)). At d = 128 a row is 256 bytes, one full
-// sweep of the 64 four-byte LDS banks, so a piece index is a bank group. The
-// K operand reads (16 bytes per lane, 16 lanes per LDS cycle) cover 16
-// consecutive rows at one data piece: swz is a permutation of 0..15 over
-// any 16 aligned rows. The transposed V reads (8 bytes per lane, 32 lanes per
-// cycle) cover 4 consecutive rows x 4 consecutive data pieces: the rows'
-// swz values differ in bits 2-3, so the 16 (row, piece) pairs land in 16
-// distinct bank groups. (The former r0,r1,r2,r3 -> bits 1,2,0,3 layout left
-// those reads with 2-way conflicts.)
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (r >> 1) & 7;
-}
-
-// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 word 3: 32-bit
-// data format); loads at lane offsets >= bytes return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// 16 bytes per lane from a buffer straight into LDS (dst is the wave's
-// 1 KiB destination; lane l lands at dst + 16 l).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-
-// s_waitcnt lgkmcnt(0) (vmcnt, expcnt unconstrained).
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
-}
-
-// Workgroup barrier for the LDS pipeline: this wave's LDS accesses complete
-// before it arrives (so no other wave can refill a tile under a read still in
-// the LDS queue), compiler-level ordering of memory accesses on both sides,
-// but no wait on in-flight direct-to-LDS loads (those are waited explicitly).
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
-
-// max over lanes l and l^32 (the two wave halves hold the same query)
-__device__ __forceinline__ float halves_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-}  // namespace
 
 // One query tile. K and V tiles are separate LDS arrays so the compiler can
 // tell the two direct-to-LDS load streams apart; all waits on those loads are
@@ -631,13 +554,13 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
     const int per = total >> 3, rem = total & 7;
     if (i >= per + (x < rem ? 1 : 0)) return;
     const int flat = x * per + min(x, rem) + i;
-    int lo = 0, hi = a.bh - 1;                  // head: last bh with item_base[bh] <= flat
+    int lo = 0, hi = a.bh - 1;                  // position: last p with item_base[p] <= flat
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (((const cint*)a.item_base)[mid] <= flat) lo = mid; else hi = mid - 1;
     }
-    const int bh = lo;
-    const int k = flat - ((const cint*)a.item_base)[bh];
+    const int bh = ((const cint*)a.head_order)[lo];
+    const int k = flat - ((const cint*)a.item_base)[lo];
     const cint* it = (const cint*)a.items + ((size_t)bh * a.max_items + k) * 4;
     const int I = it[0], off = it[1], cnt = it[2];
     int qs, ql;
@@ -746,15 +669,24 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
                                                           int nqb, int nsegs, int sg, int max_items,
                                                           const int32_t* __restrict__ segoff,
                                                           int32_t* __restrict__ items, int32_t* __restrict__ slot_of,
-                                                          int32_t* __restrict__ n_items) {
+                                                          int32_t* __restrict__ n_items, int32_t* __restrict__ head_work) {
   extern __shared__ int hist[];          // [nsegs * (sg + 1)] bucket counts, then cursors
   __shared__ int part[1025];
+  __shared__ int work;
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int nbk = nsegs * (sg + 1);
   const int npairs = nqb * nsegs;
   for (int b = tid; b < nbk; b += 1024) hist[b] = 0;
+  if (tid == 0) work = 0;
   __syncthreads();
+  {
+    // kept tiles of the head: the XCD balance of the item order
+    int w = 0;
+    for (int I = tid; I < nqb; I += 1024) w += min(max(kv_count[(size_t)bh * nqb + I], 0), kv_stride);
+    for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
+    if ((tid & 63) == 0) atomicAdd(&work, w);
+  }
   // count of pair p = (I, s): the next segment's start (or the list end) minus its own
   auto pair = [&](int p, int& I, int& s, int& off) -> int {
     I = p / nsegs;
@@ -805,7 +737,10 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
     hist[b] = run;
     run += v;
   }
-  if (tid == 0) n_items[bh] = part[1024];
+  if (tid == 0) {
+    n_items[bh] = part[1024];
+    head_work[bh] = work;
+  }
   __syncthreads();
   // scatter the items
   for (int p = tid; p < npairs; p += 1024) {
@@ -823,17 +758,67 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
   }
 }
 
-// item_base[b] = sum of n_items over the heads before b; item_base[BH] = total.
-__global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __restrict__ n_items, int BH,
+// Order of the heads in the item sequence, and its prefix: the sequence is
+// dealt to the 8 XCDs as contiguous ranges of equal item counts, so each XCD
+// runs about BH / 8 consecutive heads. Heads differ in kept tiles (up to 2.3x
+// at the 720p layer), so the heads are first grouped by XCD greedily --
+// heaviest first, each to the least-loaded XCD that has fewer than
+// ceil(BH / 8) -- and the groups laid out one after the other.
+// head_order[p] = head at position p (identity for BH > kBalanceHeads);
+// item_base[p] = items of the heads at positions before p; item_base[BH] =
+// total.
+constexpr int kBalanceHeads = 2048;
+__global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __restrict__ n_items,
+                                                           const int32_t* __restrict__ head_work, int BH,
+                                                           int32_t* __restrict__ head_order,
                                                            int32_t* __restrict__ item_base) {
   __shared__ int part[257];
-  const int per = (BH + 255) / 256;
-  const int b0 = threadIdx.x * per, b1 = min(BH, b0 + per);
-  int loc = 0;
-  for (int b = b0; b < b1; ++b) loc += n_items[b];
-  part[threadIdx.x] = loc;
+  __shared__ int sorted[kBalanceHeads];
+  __shared__ int order[kBalanceHeads];
+  const int tid = threadIdx.x;
+  if (BH <= kBalanceHeads) {
+    for (int h = tid; h < BH; h += 256) {            // rank by work, descending (ties: lower head)
+      const int wh = head_work[h];
+      int r = 0;
+      for (int j = 0; j < BH; ++j) {
+        const int wj = head_work[j];
+        r += (wj > wh || (wj == wh && j < h)) ? 1 : 0;
+      }
+      sorted[r] = h;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const int cap = (BH + 7) / 8;
+      long long load[8];
+      int cnt[8];
+      for (int x = 0; x < 8; ++x) { load[x] = 0; cnt[x] = 0; }
+      for (int r = 0; r < BH; ++r) {                 // order[] doubles as the per-XCD slots
+        const int h = sorted[r];
+        int best = -1;
+        for (int x = 0; x < 8; ++x)
+          if (cnt[x] < cap && (best < 0 || load[x] < load[best])) best = x;
+        order[best * cap + cnt[best]] = h;
+        ++cnt[best];
+        load[best] += head_work[h];
+      }
+      int p = 0;                                     // compact the groups in XCD order
+      for (int x = 0; x < 8; ++x)
+        for (int i = 0; i < cnt[x]; ++i) sorted[p++] = order[x * cap + i];
+    }
+    __syncthreads();
+    for (int p = tid; p < BH; p += 256) head_order[p] = sorted[p];
+  } else {
+    for (int p = tid; p < BH; p += 256) head_order[p] = p;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  const int per = (BH + 255) / 256;
+  const int b0 = tid * per, b1 = min(BH, b0 + per);
+  auto items_at = [&](int p) { return n_items[BH <= kBalanceHeads ? sorted[p] : p]; };
+  int loc = 0;
+  for (int p = b0; p < b1; ++p) loc += items_at(p);
+  part[tid] = loc;
+  __syncthreads();
+  if (tid == 0) {
     int run = 0;
     for (int t = 0; t < 256; ++t) {
       const int v = part[t];
@@ -843,12 +828,12 @@ __global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __rest
     part[256] = run;
   }
   __syncthreads();
-  int run = part[threadIdx.x];
-  for (int b = b0; b < b1; ++b) {
-    item_base[b] = run;
-    run += n_items[b];
+  int run = part[tid];
+  for (int p = b0; p < b1; ++p) {
+    item_base[p] = run;
+    run += items_at(p);
   }
-  if (threadIdx.x == 0) item_base[BH] = part[256];
+  if (tid == 0) item_base[BH] = part[256];
 }
 
 // Combines the partial results of query blocks with more than one item (in
@@ -1028,7 +1013,8 @@ constexpr int kSplitSegBlocks = 384;
 namespace {
 struct SplitLayout {
   int nsegs = 0, sg = 0, max_items = 0;
-  size_t segoff = 0, slot_of = 0, nseg = 0, n_items = 0, item_base = 0, items = 0, part = 0, end = 0;
+  size_t segoff = 0, slot_of = 0, nseg = 0, n_items = 0, head_work = 0, head_order = 0, item_base = 0, items = 0,
+         part = 0, end = 0;
 };
 size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace layout of the split path after the order table; nsegs = 0 when
@@ -1050,6 +1036,8 @@ SplitLayout split_layout(int BH, int nqb, int nkb, int d) {
   L.slot_of = o; o += r256(4 * pairs);
   L.nseg = o; o += r256(4 * (size_t)BH * nqb);
   L.n_items = o; o += r256(4 * (size_t)BH);
+  L.head_work = o; o += r256(4 * (size_t)BH);
+  L.head_order = o; o += r256(4 * (size_t)BH);
   L.item_base = o; o += r256(4 * ((size_t)BH + 1));
   L.items = o; o += r256(16 * pairs);
   L.part = o; o += r256(sizeof(float) * (size_t)kSplitSlotFloats * pairs);
@@ -1097,7 +1085,8 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int kmode = kvar ? 2 : kshort ? 1 : 0;
   a.tile_base = tile_ws;
   a.order = nullptr;
-  a.items = nullptr; a.item_base = nullptr; a.nseg = nullptr; a.slot_of = nullptr; a.part = nullptr;
+  a.items = nullptr; a.item_base = nullptr; a.head_order = nullptr; a.nseg = nullptr; a.slot_of = nullptr;
+  a.part = nullptr;
   a.max_items = 0; a.nsegs = 0;
   // Long uniform rows with a workspace of the full size: split over key
   // segments (plan, items, merge).
@@ -1109,6 +1098,8 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
       a.slot_of = reinterpret_cast<int32_t*>(w + L.slot_of);
       a.nseg = reinterpret_cast<int32_t*>(w + L.nseg);
       int32_t* n_items = reinterpret_cast<int32_t*>(w + L.n_items);
+      int32_t* head_work = reinterpret_cast<int32_t*>(w + L.head_work);
+      a.head_order = reinterpret_cast<int32_t*>(w + L.head_order);
       a.item_base = reinterpret_cast<int32_t*>(w + L.item_base);
       a.items = reinterpret_cast<int32_t*>(w + L.items);
       a.part = reinterpret_cast<float*>(w + L.part);
@@ -1123,8 +1114,9 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
           const_cast<int32_t*>(a.nseg));
       split_plan_kernel<<<BH, 1024, lds, s>>>(kv_count, kv_stride, qb.nblocks, L.nsegs, L.sg, L.max_items, segoff,
                                               const_cast<int32_t*>(a.items), const_cast<int32_t*>(a.slot_of),
-                                              n_items);
-      split_prefix_kernel<<<1, 256, 0, s>>>(n_items, BH, const_cast<int32_t*>(a.item_base));
+                                              n_items, head_work);
+      split_prefix_kernel<<<1, 256, 0, s>>>(n_items, head_work, BH, const_cast<int32_t*>(a.head_order),
+                                            const_cast<int32_t*>(a.item_base));
       const long long grid = 8LL * (((long long)BH * L.max_items + 7) / 8);
       if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
       attn_fwd_kernel<128, false, 0, true><<<(int)grid, 128, 0, s>>>(a);

@@ -32,77 +32,11 @@
 //                      its key order matches the accumulator layout of S^T.
 // O is divided by the row sum once at the end, staged through LDS and
 // written as bf16 rows.
-#include "attn.h"
+#include "lds_tile.h"
 
 #include <math.h>
 
 namespace bsa {
-
-namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-// Read-only for the whole kernel: uniform loads through it become scalar loads.
-typedef __attribute__((address_space(4))) const int32_t cint;
-
-// Swizzle of the 16-byte piece index inside a K/V tile row (LDS position p of
-// row r holds data piece p ^ swz(r)). At d = 128 a row is 256 bytes, one full
-// sweep of the 64 four-byte LDS banks, so a piece index is a bank group. The
-// K operand reads (16 bytes per lane, 16 lanes per LDS cycle) cover 16
-// consecutive rows at one data piece: swz is a permutation of 0..15 over
-// any 16 aligned rows. The transposed V reads (8 bytes per lane, 32 lanes per
-// cycle) cover 4 consecutive rows x 4 consecutive data pieces: the rows'
-// swz values differ in bits 2-3, so the 16 (row, piece) pairs land in 16
-// distinct bank groups. (The former r0,r1,r2,r3 -> bits 1,2,0,3 layout left
-// those reads with 2-way conflicts.)
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (r >> 1) & 7;
-}
-
-// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 word 3: 32-bit
-// data format); loads at lane offsets >= bytes return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// 16 bytes per lane from a buffer straight into LDS (dst is the wave's
-// 1 KiB destination; lane l lands at dst + 16 l).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-
-// s_waitcnt lgkmcnt(0) (vmcnt, expcnt unconstrained).
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
-
-// max over lanes l and l^32 (the two wave halves hold the same query)
-__device__ __forceinline__ float halves_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-}  // namespace
 
 // One query tile of 64 rows on ONE wave. The two 32-row halves qh = 0, 1 of
 // the MFMA output share every K and V operand read from LDS (half the LDS

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         }
       }
       const int piece = (CPT / 8) * ls + pc;
-      const int off = lr * ROWB + ((piece ^ swz<D>(lr & 15)) << 4);
+      const int off = lr * ROWB + ((piece ^ swz_compact<D>(lr & 15)) << 4);
 #pragma unroll
       for (int p = 0; p < 3; ++p)
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((lds_u8*)parts + p * PART + off) = w[p];

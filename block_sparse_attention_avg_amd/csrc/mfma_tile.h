@@ -6,52 +6,10 @@
 // store.
 #pragma once
 
-#include "attn.h"
+#include "lds_tile.h"
 
 namespace bsa {
 namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef __attribute__((address_space(3))) float lds_f32;
-typedef __attribute__((address_space(4))) const int32_t cint;
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Swizzle of the 16-byte piece index inside a tile row (as in the forward).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
-  else return (r >> 1) & 7;
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
-}
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
 
 // Tile geometry: 64 rows of D bf16, row-major in LDS with swizzled 16-byte
 // pieces; the NW waves of a workgroup share its loads (wave w loads rows
@@ -72,7 +30,7 @@ __device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) 
 #pragma unroll
   for (int i = 0; i < T::NI; ++i) {
     const int r = (wave * T::NI + i) * T::RPI + lane / T::PPR;
-    off[i] = r * T::ROWB + (((lane % T::PPR) ^ swz<D>(r & 15)) << 4);
+    off[i] = r * T::ROWB + (((lane % T::PPR) ^ swz_compact<D>(r & 15)) << 4);
   }
 }
 // Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros.
@@ -87,7 +45,7 @@ __device__ __forceinline__ void tile_load(const uint16_t* head, int r0, int n, l
 // Row operand: lane supplies row (32 g + l32), channels 16 c + 8 half .. +7.
 template <int D>
 __device__ __forceinline__ bf16x8 row_read(const lds_u8* t, int g, int c, int l32, int half) {
-  const int off = (32 * g + l32) * Tile<D>::ROWB + (((2 * c + half) ^ swz<D>(l32 & 15)) << 4);
+  const int off = (32 * g + l32) * Tile<D>::ROWB + (((2 * c + half) ^ swz_compact<D>(l32 & 15)) << 4);
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off);
 }
 // Transposed operand through the LDS transpose read: lane receives channel
@@ -97,17 +55,17 @@ template <int D>
 struct TrOffsets {
   // offset of channel group dg = 0, row half t = 0; the others follow from
   // it: channel group dg flips the piece bits 4 dg (byte bits dg << 6), and
-  // the row half t = 1 lies 8 rows further with swizzle bit 8 (D = 128) or
-  // 4 (D = 64) flipped
+  // the row half t = 1 lies 8 rows further, its swizzle differing by the
+  // constant swz(8) ^ swz(0)
   int base;
   __device__ __forceinline__ TrOffsets(int lane) {
     const int half = lane >> 5, g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
     const int row = 4 * half + sj;
     const int piece = 2 * g16 + (sq >> 1);
-    base = row * Tile<D>::ROWB + ((piece ^ swz<D>(row)) << 4) + ((sq & 1) << 3);
+    base = row * Tile<D>::ROWB + ((piece ^ swz_compact<D>(row)) << 4) + ((sq & 1) << 3);
   }
   __device__ __forceinline__ int at(int dg, int t) const {
-    constexpr int kFlip = D == 128 ? 128 : 64;
+    const int kFlip = (swz_compact<D>(8) ^ swz_compact<D>(0)) << 4;   // rows r and r + 8 (r < 8)
     const int o = base ^ (dg << 6);
     return t ? (o ^ kFlip) + 8 * Tile<D>::ROWB : o;
   }
@@ -133,7 +91,7 @@ __device__ __forceinline__ void store_rows(const f32x16* acc, float mul, lds_u8*
   using T = Tile<D>;
   const int half = lane >> 5, l32 = lane & 31;
   const int orow = 32 * wave + l32;
-  const int fo = swz<D>(orow & 15);
+  const int fo = swz_compact<D>(orow & 15);
   if (active) {
 #pragma unroll
     for (int dg = 0; dg < D / 32; ++dg)
@@ -153,7 +111,7 @@ __device__ __forceinline__ void store_rows(const f32x16* acc, float mul, lds_u8*
     if (row < n)
       *reinterpret_cast<u32x4*>(out + (size_t)(r0 + row) * D + p * 8) =
           *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-              stage + row * T::ROWB + ((p ^ swz<D>(row & 15)) << 4));
+              stage + row * T::ROWB + ((p ^ swz_compact<D>(row & 15)) << 4));
   }
 }
 

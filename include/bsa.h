@@ -99,6 +99,12 @@ typedef struct bsa_window {
 } bsa_window;
 
 int bsa_abi_version(void);
+
+/* Test-only: the swizzle of the attention kernels' LDS tiles. A 64-row tile
+ * of d bf16 channels keeps row r's 16-byte data piece p at piece position
+ * p ^ bsa_lds_swizzle(d, r) (d in {64, 128}; -1 otherwise). Exposed so that
+ * host tests can map each LDS access pattern of the kernels to banks. */
+int bsa_lds_swizzle(int d, int row);
 const char* bsa_strerror(int status);
 /* Detail of the last error raised on the calling thread ("" if none). */
 const char* bsa_last_error_message(void);
