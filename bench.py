@@ -543,7 +543,7 @@ def cpu_baseline(r: Runner, flops_total: float, mask_heads=None, attn_blocks=Non
 CSRC = os.path.join(ROOT, "block_sparse_attention_avg_amd", "csrc")
 # Sources of the attention forward kernels; the counter summary of a kernel
 # stays valid while their combined hash is unchanged.
-ATTN_SOURCES = ("attn.h", "attn_fwd.hip", "attn_fwd_1w.hip", "attn_tile.h", "common.h")
+ATTN_SOURCES = ("attn.h", "attn_fwd.hip", "attn_fwd_1w.hip", "lds_tile.h", "common.h")
 
 
 def traffic_file(workload: str) -> str:

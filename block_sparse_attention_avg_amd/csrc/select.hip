@@ -114,20 +114,22 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
       // are at most 64 of them, finish exactly with one candidate per lane:
       // k* is the smallest candidate key whose inclusive cumulative mass
       // (below + candidates with keys <= it) reaches the threshold.
+      // (key >> 27 == pb >> 14: the prefix lies in the probability bits, so
+      // the test is one 32-bit shift and compare per element)
+      const uint32_t pfx = (uint32_t)prefix;
       int ncand = 0;
 #pragma unroll
-      for (int t = 0; t < E; ++t) ncand += __popcll(__ballot((key_of(t) >> (shift + width)) == prefix));
+      for (int t = 0; t < E; ++t) ncand += __popcll(__ballot((pb[t] >> 14) == pfx));
       if (ncand <= kWave) {
         unsigned long long* slot = h;          // 64 x (key, mass) = 1 KiB of this wave's histogram
         int at = 0;
 #pragma unroll
         for (int t = 0; t < E; ++t) {
-          const unsigned long long kt = key_of(t);
-          const bool c = (kt >> (shift + width)) == prefix;
+          const bool c = (pb[t] >> 14) == pfx;
           const unsigned long long bal = __ballot(c);
           if (c) {
             const int r = at + __popcll(bal & ((1ull << lane) - 1ull));
-            slot[2 * r] = kt;
+            slot[2 * r] = key_of(t);
             slot[2 * r + 1] = mass_of(t);
           }
           at += __popcll(bal);
@@ -182,12 +184,25 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
 #pragma unroll
     for (int q = 0; q < kBins / kWave; ++q) h[lane * (kBins / kWave) + q] = 0;
     wave_lds_sync();
+    if (shift >= kIdxBits) {
+      // the digit and the prefix lie in the probability bits (passes 1, 2):
+      // key >> n == pb >> (n - 13) for n >= 13, in 32-bit arithmetic
+      const int ps = shift - kIdxBits;
+      const uint32_t pfx = (uint32_t)prefix;
 #pragma unroll
-    for (int t = 0; t < E; ++t) {
-      const unsigned long long kt = key_of(t);
-      const uint32_t mt = mass_of(t);
-      if ((kt >> (shift + width)) == prefix && mt)
-        atomicAdd(&h[(kt >> shift) & ((1 << width) - 1)], (unsigned long long)mt);
+      for (int t = 0; t < E; ++t) {
+        const uint32_t mt = mass_of(t);
+        if ((pb[t] >> (ps + width)) == pfx && mt)
+          atomicAdd(&h[(pb[t] >> ps) & ((1 << width) - 1)], (unsigned long long)mt);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        const unsigned long long kt = key_of(t);
+        const uint32_t mt = mass_of(t);
+        if ((kt >> (shift + width)) == prefix && mt)
+          atomicAdd(&h[(kt >> shift) & ((1 << width) - 1)], (unsigned long long)mt);
+      }
     }
     wave_lds_sync();
     // lane owns bins [4*lane, 4*lane+4)
@@ -223,10 +238,14 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   if (!done) kstar = prefix;
 
   int base = 0;
+  // key >= k*  <=>  pb > k*_hi, or pb == k*_hi and 8191 - j >= k*_lo
+  const uint32_t ks_hi = (uint32_t)(kstar >> kIdxBits), ks_lo = (uint32_t)(kstar & ((1u << kIdxBits) - 1));
+  const bool none = (kstar >> kIdxBits) > 0xffffffffull;   // k* past every key: keep nothing by the CDF
 #pragma unroll
   for (int t = 0; t < E; ++t) {
     const int j = lane + kWave * t;
-    bool keep = j < nkb && key_of(t) >= kstar;
+    const uint32_t lo = (uint32_t)((1 << kIdxBits) - 1 - j);
+    bool keep = j < nkb && !none && (pb[t] > ks_hi || (pb[t] == ks_hi && lo >= ks_lo));
     if (keep && ksz && ksz[j] <= 0) keep = false;
     if (j < nkb && win.enabled && win.inside(row, j)) keep = true;
     const unsigned long long bal = __ballot(keep);
