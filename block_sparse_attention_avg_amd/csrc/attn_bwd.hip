@@ -9,15 +9,18 @@
 //   dP = dO_I V_J^T,        dS = P * (dP - Dr_I)   (Dr_i = dO_i . O_i)
 //   dQ_I += scale dS K_J,   dK_J += scale dS^T Q_I,   dV_J += P^T dO_I
 // Every kernel is deterministic (no atomics on the gradients):
-//   bwd_dot_kernel   Dr = rowsum(dO * O), fp32;
+//   bwd_dot_kernel   Dr = rowsum(dO * O), fp32, stored beside lse * log2e;
 //   csc_*_kernel     the lists transposed (key block -> query blocks that
 //                    kept it): a bit matrix, then ascending lists;
 //   bwd_grad_kernel  one launch with two roles, 4 waves per workgroup:
 //                    key tiles (dK, dV) walk the query blocks that kept them,
 //                    query tiles (dQ) walk their kept key blocks (the
-//                    forward's lists); each wave takes a 32 x 32 quarter of
-//                    every 64 x 64 chunk and the two partial sums of a tile
-//                    meet in LDS at the end.
+//                    forward's lists). Each wave computes S and dP of a
+//                    32 x 32 quarter of every 64 x 64 chunk. In a query tile
+//                    the two key halves' partial dQ meet in LDS at the end;
+//                    in a key tile the two waves of a key half trade P and dS
+//                    through LDS every chunk, so one accumulates dV and the
+//                    other dK over all 64 query rows.
 // The MFMA layouts are those of the forward: a 32 x 32 accumulator whose
 // lane holds one column (query, resp. key) and 16 rows; the second product of
 // each pair takes its bf16 B operand straight from that accumulator, and the
@@ -35,7 +38,7 @@ struct BwdArgs {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;           // [BH][N] natural-log row normaliser from the forward
-  float* dr;                  // [BH][N] rowsum(dO * O), written by bwd_dot_kernel
+  float* lsd;                 // [BH][N][2] (lse * log2e, rowsum(dO * O)), written by bwd_dot_kernel
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -78,7 +81,9 @@ __device__ __forceinline__ void block_at(const Blocks& b, int bh, int i, int n_v
   }
 }
 
-// Dr[row] = sum_c dO[row, c] O[row, c] (fp32), 0 on pad rows.
+// Per row: (lse * log2e, Dr = sum_c dO[row, c] O[row, c]) in fp32, one
+// 8-byte pair, so that a chunk's pairs are one contiguous run; (+inf, 0) on
+// pad rows.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a, size_t rows) {
   constexpr int LPR = D / 8;                       // lanes per row, 8 channels each
@@ -95,7 +100,10 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a, size_t rows) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) a.dr[row] = acc;
+  if (row < rows && part == 0) {
+    const bool valid = (int)(row % a.N) < a.n_valid;
+    *reinterpret_cast<f32x2*>(a.lsd + 2 * row) = (f32x2){valid ? a.lse[row] * kLog2e : INFINITY, acc};
+  }
 }
 
 // Transposed lists, step 1: clear the bit matrix.
@@ -183,8 +191,8 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
     qf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.q + off) : bf16x8{};
     gf[c] = qok ? *reinterpret_cast<const bf16x8*>(a.dout + off) : bf16x8{};
   }
-  const float lse2 = qok ? a.lse[head + qs + qr] * kLog2e : INFINITY;   // pad rows: P = 0
-  const float drow = qok ? a.dr[head + qs + qr] : 0.f;
+  const float lse2 = qok ? a.lsd[2 * (head + qs + qr)] : INFINITY;   // pad rows: P = 0
+  const float drow = qok ? a.lsd[2 * (head + qs + qr) + 1] : 0.f;
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -274,17 +282,20 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
   store_rows<D, 256>(dq, a.scale, (lds_u8*)K1, a.dq + head * D, qs, ql, qw, lane, kw == 0);
 }
 
-// dK, dV of one 64-key tile. Four waves: wave w owns keys 32 (w & 1) .. +31
+// dK, dV of one 64-key tile. Four waves: wave w takes keys 32 (w & 1) .. +31
 // and query rows 32 (w >> 1) .. +31 of every chunk. Per query block that kept
 // the tile, on double-buffered Q / dO tiles:
 //   S = Q K^T, dP = dO V^T          (32 queries x 32 keys; K^T, V^T in registers)
 //   P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - Dr)
-//   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through the transpose read)
-// The two query halves' partial dK^T, dV^T meet in LDS at the end (fixed order).
+// The two waves of a key half then trade their quarter of P or dS through
+// LDS (2 KiB each, lane-aligned: lane = key), and over the chunk's 64 query
+// rows the first accumulates dV^T += dO^T P, the second dK^T += Q^T dS (dO^T,
+// Q^T through the transpose read). One 32-key x D accumulator per wave, in
+// place of a partial dK^T and dV^T each, keeps a wave within the 256
+// registers of two waves per SIMD.
 template <int D, bool DESC>
 __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, unsigned char* Q0, unsigned char* G0,
-                                              unsigned char* Q1, unsigned char* G1, float* L0, float* R0, float* L1,
-                                              float* R1) {
+                                              unsigned char* Q1, unsigned char* G1, unsigned char* X) {
   using T = Tile<D, 4>;
   constexpr int NC = D / 16;                       // MFMA k-steps over the channels
 
@@ -295,7 +306,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
   if (kl <= 0) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = wave & 1, g = wave >> 1;
+  const int kw = wave & 1, g = wave >> 1;          // g = 0: dV, g = 1: dK
   const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * a.N;
   const uint16_t* qh = a.q + head * D;
@@ -313,11 +324,11 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
     kf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.k + o) : bf16x8{};
     vf[c] = kok ? *reinterpret_cast<const bf16x8*>(a.v + o) : bf16x8{};
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];                              // dV^T (g = 0) or dK^T (g = 1) of keys 32kw ..
 #pragma unroll
   for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[dg][r] = dv[dg][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[dg][r] = 0.f;
 
   const size_t lcol = (size_t)bh * a.nkb + J;
   const int cnt = ((const cint*)a.q_count)[lcol];
@@ -325,34 +336,37 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
   uint32_t off[T::NI];
   tile_offsets<D, 4>(wave, lane, off);
   const TrOffsets<D> tro(lane);
+  // hand-over slots, [key half][writer's g][hh][lane][4 words]: this wave
+  // writes its own, reads the other wave's of its key half
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_u32x4* mine = (lds_u32x4*)((lds_u8*)X + (2 * kw + g) * 2048);
+  const lds_u32x4* theirs = (const lds_u32x4*)((lds_u8*)X + (2 * kw + (g ^ 1)) * 2048);
 
-  // rows, lse and Dr of chunk c (clamped into range); lane l of each wave
-  // fetches row l's lse and Dr into registers (wave 0 stores them to LDS)
-  auto issue = [&](int c, lds_u8* Qn, lds_u8* Gn, float& lv, float& rv) {
+  // chunk c (clamped into range): its Q and dO rows, and its rows'
+  // (lse log2e, Dr) pairs straight into LDS after the Q tile (Qn + BYTES).
+  // Every wave loads all 64 pairs (lanes 0..31, 16 bytes each; lanes 32..63
+  // read past the descriptor and write zeros to the next 512 bytes): the
+  // waves write the same bytes, every wave issues the same loads, and no
+  // load sits under a branch (the compiler would then wait for it before
+  // any LDS read). Rows past the block read as zeros: their Q and dO rows
+  // are zero too, so they add nothing to dK or dV.
+  auto issue = [&](int c, lds_u8* Qn, lds_u8* Gn) {
     const int I = list[c < cnt ? c : cnt - 1];
     int qs, ql;
     block_at<DESC>(a.qb, bh, I, a.n_valid, qs, ql);
-    const bool ok = lane < ql;
-    lv = INFINITY;
-    rv = 0.f;
-    if (ok) {                                      // every wave: equal load counts
-      lv = a.lse[head + qs + lane];
-      rv = a.dr[head + qs + lane];
-    }
+    const int q0 = __builtin_amdgcn_readfirstlane(qs), n0 = __builtin_amdgcn_readfirstlane(max(ql, 0));
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lsd + 2 * (head + q0), (uint32_t)n0 * 8);
+    dma16(rl, Qn + T::BYTES, lane < 32 ? 16 * lane : 0xFFFFFFF0u);
     tile_load<D, 4>(qh, qs, ql, Qn, wave, off);
     tile_load<D, 4>(gh, qs, ql, Gn, wave, off);
   };
-  // one chunk: chunk c+1 (or a reload of c) goes out first; chunk c's tiles
-  // must have landed and its lse / Dr are in registers lv, rv (wave 0)
-  auto step = [&](int c, const lds_u8* Qc, const lds_u8* Gc, lds_f32* Lc, lds_f32* Rc, lds_u8* Qn, lds_u8* Gn,
-                  float& lv, float& rv, float& lv_n, float& rv_n) {
-    if (wave == 0) {
-      Lc[lane] = lv == INFINITY ? INFINITY : lv * kLog2e;
-      Rc[lane] = rv;
-    }
-    issue(c + 1, Qn, Gn, lv_n, rv_n);
-    wait_vm<2 * T::NI + 2>();                      // chunk c landed (and its lse / Dr before it)
-    wg_barrier();
+  // one chunk: chunk c+1 (or a reload of c) goes out first; chunk c must
+  // have landed in (Qc, Gc)
+  auto step = [&](int c, const lds_u8* Qc, const lds_u8* Gc, lds_u8* Qn, lds_u8* Gn) {
+    const lds_u8* LRc = Qc + T::BYTES;
+    issue(c + 1, Qn, Gn);
+    wait_vm<2 * T::NI + 1>();                      // this wave's share of chunk c landed
+    wg_barrier();                                  // and the other waves'
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -364,8 +378,11 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
     for (int r4 = 0; r4 < 4; ++r4) {
       // rows 32g + 8 r4 + 4 half + 0..3 of the chunk
       const int row0 = 32 * g + 8 * r4 + 4 * half;
-      const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Lc + row0);
-      const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(Rc + row0);
+      typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
+      const f32x4 a01 = *reinterpret_cast<lds_f32x4*>(LRc + 8 * row0);        // rows row0, row0 + 1
+      const f32x4 a23 = *reinterpret_cast<lds_f32x4*>(LRc + 8 * row0 + 16);   // rows row0 + 2, row0 + 3
+      const f32x4 l4 = {a01[0], a01[2], a23[0], a23[2]};
+      const f32x4 d4 = {a01[1], a01[3], a23[1], a23[3]};
       float p[4], d[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -378,59 +395,53 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
       pd[r4 >> 1][2 * (r4 & 1) + 0] = pack2(d[0], d[1]);
       pd[r4 >> 1][2 * (r4 & 1) + 1] = pack2(d[2], d[3]);
     }
+    // the dV wave keeps its P and hands over its dS, the dK wave the reverse
+    u32x4 own[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]});
-      const bf16x8 db = __builtin_bit_cast(bf16x8, (u32x4){pd[hh][0], pd[hh][1], pd[hh][2], pd[hh][3]});
-#pragma unroll
-      for (int dg = 0; dg < D / 32; ++dg) {
-        dv[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Gc, tro, g, hh, dg), pb, dv[dg], 0, 0, 0);
-        dk[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(Qc, tro, g, hh, dg), db, dk[dg], 0, 0, 0);
-      }
+      const u32x4 P4 = {pp[hh][0], pp[hh][1], pp[hh][2], pp[hh][3]};
+      const u32x4 D4 = {pd[hh][0], pd[hh][1], pd[hh][2], pd[hh][3]};
+      own[hh] = g ? D4 : P4;
+      mine[hh * 64 + lane] = g ? P4 : D4;
     }
-    wg_barrier();                                  // chunk c's buffers free for chunk c+2
+    wg_barrier();
+    // over the chunk's 64 query rows (half gq, 16-row group hh):
+    //   g = 0: dV^T += dO^T P,  g = 1: dK^T += Q^T dS
+    // (a branch per role rather than a selected pointer: the compiler then
+    // knows which tile each LDS read touches and does not wait for the loads
+    // in flight into the other buffers)
+    auto accumulate = [&](const lds_u8* src) {
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, gq == g ? own[hh] : theirs[hh * 64 + lane]);
+#pragma unroll
+          for (int dg = 0; dg < D / 32; ++dg)
+            acc[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(src, tro, gq, hh, dg), b, acc[dg], 0, 0, 0);
+        }
+    };
+    if (g)
+      accumulate(Qc);
+    else
+      accumulate(Gc);
+    wg_barrier();                                  // chunk c's buffers and the slots free again
   };
 
   if (cnt > 0) {
-    float lA = INFINITY, rA = 0.f, lB = INFINITY, rB = 0.f;
-    issue(0, (lds_u8*)Q0, (lds_u8*)G0, lA, rA);
+    issue(0, (lds_u8*)Q0, (lds_u8*)G0);
     for (int c = 0;;) {
-      step(c, (const lds_u8*)Q0, (const lds_u8*)G0, (lds_f32*)L0, (lds_f32*)R0, (lds_u8*)Q1, (lds_u8*)G1, lA, rA,
-           lB, rB);
+      step(c, (const lds_u8*)Q0, (const lds_u8*)G0, (lds_u8*)Q1, (lds_u8*)G1);
       if (++c >= cnt) break;
-      step(c, (const lds_u8*)Q1, (const lds_u8*)G1, (lds_f32*)L1, (lds_f32*)R1, (lds_u8*)Q0, (lds_u8*)G0, lB, rB,
-           lA, rA);
+      step(c, (const lds_u8*)Q1, (const lds_u8*)G1, (lds_u8*)Q0, (lds_u8*)G0);
       if (++c >= cnt) break;
     }
   }
   wait_vm<0>();
   wg_barrier();
-  // the second query half's partial dK^T, dV^T join the first's (16 KiB each)
-  lds_f32* park_k = (lds_f32*)(kw ? G0 : Q0);
-  lds_f32* park_v = (lds_f32*)(kw ? G1 : Q1);
-  if (g == 1) {
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        park_k[(dg * 16 + r) * 64 + lane] = dk[dg][r];
-        park_v[(dg * 16 + r) * 64 + lane] = dv[dg][r];
-      }
-  }
+  store_rows<D, 256>(acc, a.scale, (lds_u8*)Q0, a.dk + head * D, ks, kl, kw, lane, g == 1);
   wg_barrier();
-  if (g == 0) {
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk[dg][r] += park_k[(dg * 16 + r) * 64 + lane];
-        dv[dg][r] += park_v[(dg * 16 + r) * 64 + lane];
-      }
-  }
-  wg_barrier();                                    // the parks are read before staging reuses them
-  store_rows<D, 256>(dk, a.scale, (lds_u8*)Q0, a.dk + head * D, ks, kl, kw, lane, g == 0);
-  wg_barrier();
-  store_rows<D, 256>(dv, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, kw, lane, g == 0);
+  store_rows<D, 256>(acc, 1.f, (lds_u8*)G0, a.dv + head * D, ks, kl, kw, lane, g == 0);
 }
 
 // One launch for both gradients: workgroups [0, nkv) take key tiles (dK, dV;
@@ -440,18 +451,18 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
 // are shared by the two roles.
 template <int D, bool DESC>
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdArgs a, int BH, int nkv) {
-  __shared__ __align__(16) unsigned char B0[Tile<D>::BYTES];
+  // B0 and B2 hold a key tile's Q tiles, each followed by the chunk rows'
+  // (lse log2e, Dr) pairs (512 bytes, then the 512 zero bytes of the load's
+  // upper lanes)
+  __shared__ __align__(16) unsigned char B0[Tile<D>::BYTES + 1024];
   __shared__ __align__(16) unsigned char B1[Tile<D>::BYTES];
-  __shared__ __align__(16) unsigned char B2[Tile<D>::BYTES];
+  __shared__ __align__(16) unsigned char B2[Tile<D>::BYTES + 1024];
   __shared__ __align__(16) unsigned char B3[Tile<D>::BYTES];
-  __shared__ __align__(16) float L0[64];           // lse * log2e of the chunk's rows (+inf on pads)
-  __shared__ __align__(16) float R0[64];           // Dr of the chunk's rows (0 on pads)
-  __shared__ __align__(16) float L1[64];
-  __shared__ __align__(16) float R1[64];
+  __shared__ __align__(16) unsigned char X[8192];  // P / dS hand-over of the key tiles
   const int G = blockIdx.x;
   if (G < nkv) {
     if (G >= BH * a.nkb) return;                  // padding of the key-tile range
-    bwd_dkdv_tile<D, DESC>(a, G, BH, B0, B1, B2, B3, L0, R0, L1, R1);
+    bwd_dkdv_tile<D, DESC>(a, G, BH, B0, B1, B2, B3, X);
   } else {
     bwd_dq_tile<D, DESC>(a, G - nkv, BH, B0, B1, B2, B3);
   }
@@ -483,14 +494,14 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.kv_count = kv_count; a.kv_index = kv_index; a.kv_stride = kv_stride;
   a.W = (nqb + 31) / 32;
   a.scale = scale;
-  // workspace: Dr [BH][N] fp32 | q_count [BH][nkb] | q_index [BH][nkb][nqb] | bits [BH][nkb][W]
+  // workspace: (lse log2e, Dr) [BH][N][2] fp32 | q_count [BH][nkb] | q_index [BH][nkb][nqb] | bits [BH][nkb][W]
   char* p = static_cast<char*>(ws);
   auto take = [&](size_t bytes) {
     char* r = p;
     p += (bytes + 255) & ~(size_t)255;
     return r;
   };
-  a.dr = reinterpret_cast<float*>(take(sizeof(float) * (size_t)BH * N));
+  a.lsd = reinterpret_cast<float*>(take(2 * sizeof(float) * (size_t)BH * N));
   a.q_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nkb));
   a.q_index = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)BH * nkb * nqb));
   a.bits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)BH * nkb * a.W));
@@ -535,7 +546,7 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
 size_t attn_bwd_workspace(int BH, int N, int nqb, int nkb) {
   auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t W = ((size_t)nqb + 31) / 32;
-  return r(sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nkb) +
+  return r(2 * sizeof(float) * (size_t)BH * N) + r(sizeof(int32_t) * (size_t)BH * nkb) +
          r(sizeof(int32_t) * (size_t)BH * nkb * nqb) + r(sizeof(uint32_t) * (size_t)BH * nkb * W) +
          r(sizeof(int32_t) * (size_t)BH * nqb) + r(sizeof(int32_t) * (size_t)BH * nkb);
 }

@@ -28,11 +28,15 @@ struct Blocks {
   int32_t block;     // uniform block size
   int32_t n_valid;   // uniform: blocks cover [0, n_valid)
 
+  // The descriptors are read-only while a kernel runs: reading them through
+  // the constant address space lets a wave-uniform lookup become a scalar
+  // load, which no wait on the vector loads in flight has to cover.
   __device__ __forceinline__ void get(int bh, int i, int& s, int& n) const {
     if (start) {
+      typedef __attribute__((address_space(4))) const int32_t c32;
       const size_t o = per_head ? (size_t)bh * nblocks + i : (size_t)i;
-      s = start[o];
-      n = len[o];
+      s = ((c32*)start)[o];
+      n = ((c32*)len)[o];
     } else {
       s = i * block;
       n = min(block, n_valid - s);

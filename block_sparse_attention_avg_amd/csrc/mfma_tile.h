@@ -33,12 +33,17 @@ __device__ __forceinline__ void tile_offsets(int wave, int lane, uint32_t* off) 
     off[i] = r * T::ROWB + (((lane % T::PPR) ^ swz_compact<D>(r & 15)) << 4);
   }
 }
-// Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros.
+// Rows [r0, r0 + n) of a head into `dst`; rows >= n read as zeros. r0 and n
+// are the same on every lane: taking them from the first lane keeps the
+// descriptor in scalar registers (one the compiler must treat as divergent
+// turns every load into a loop over the distinct descriptors).
 template <int D, int NW = 2>
 __device__ __forceinline__ void tile_load(const uint16_t* head, int r0, int n, lds_u8* dst, int wave,
                                           const uint32_t* off) {
   using T = Tile<D, NW>;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)max(n, 0) * T::ROWB);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  n = __builtin_amdgcn_readfirstlane(max(n, 0));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)n * T::ROWB);
 #pragma unroll
   for (int i = 0; i < T::NI; ++i) dma16(rs, dst + (wave * T::NI + i) * 1024, off[i]);
 }

@@ -282,7 +282,7 @@ int bsa_block_sparse_attn_fwd_lse(const void* q, const void* k, const void* v,
                                   hipStream_t stream);
 
 /* Workspace bytes needed by bsa_block_sparse_attn_bwd: fp32 row terms
- * [B,H,N] plus the transposed block lists (int32 [B,H,nkb] counts,
+ * [B,H,N,2] (lse in log2 units, rowsum(dO o O)) plus the transposed block lists (int32 [B,H,nkb] counts,
  * [B,H,nkb,nqb] ids, a [B,H,nkb,ceil(nqb/32)] bit matrix) and two
  * processing orders; nqb, nkb from the descriptors, ceil(N/64) for NULL. */
 size_t bsa_block_sparse_attn_bwd_workspace(int B, int H, int N,
