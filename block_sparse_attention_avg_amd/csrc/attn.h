@@ -23,8 +23,11 @@ struct AttnArgs {
   float* lse;                 // null, or [BH][N] natural-log row normaliser of the scaled scores
   // Split over key segments (uniform blocks, long rows): every non-empty
   // (query block I, key segment s) pair is an item; see split_plan_kernel.
-  const int32_t* items;       // [BH][max_items][4] {I, list offset, count, s}
-  const int32_t* item_base;   // [BH + 1] prefix of the item counts of the heads in head_order
+  const int32_t* items;       // [BH][max_items][4] {I, list offset, count, s}; per head the
+                              // items that are not their query block's last come first
+  const int32_t* item_base;   // [BH + 1] prefix of the launch's item counts of the heads in head_order
+  const int32_t* item_first;  // null: the launch runs every head's first items; else [BH]
+                              // their number, and the launch runs the last item of each query block
   const int32_t* head_order;  // [BH] head at each position of the item sequence
   const int32_t* nseg;        // [BH][nqb] non-empty segments of each query block
   const int32_t* slot_of;     // [BH][nqb][nsegs] item index of (I, s), or -1

@@ -67,11 +67,14 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, in
 
 // The tile walks the `cnt` list entries from `list` (a query block's whole
 // kept list, or one key segment of it). With `part` set it ends by storing
-// its unnormalised partial result there instead of output rows.
+// its unnormalised partial result there instead of output rows; with
+// `mslots` set (the slots of its query block's segments, its own being
+// `s_own`) it combines the other segments' partial results with its own
+// before writing the rows.
 template <int D, int KMODE>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int qs, int ql,
-                                          const int32_t* list, int cnt, float* part,
-                                          lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
+                                          const int32_t* list, int cnt, float* part, const cint* mslots,
+                                          int s_own, lds_u8* Kp, lds_u8* Vp, int* tok, int* chunk_rows) {
   constexpr int ROWB = D * 2;                  // bytes per K/V row
   constexpr int TILE = 64 * ROWB;              // bytes per K or V tile
   constexpr int NI = TILE / 1024 / 2;          // direct-to-LDS loads per wave per tile
@@ -472,7 +475,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   if (part) {
     // partial result of one key segment: the registers as they are (rows of
     // both waves, [wave][dg][r/4][lane][4]), then the reference max and row
-    // sum of each lane; combined by split_merge_kernel
+    // sum of each lane; combined by the query block's last item
     if constexpr (D == 128) {
       const int w64 = wave * 64 + lane;
 #pragma unroll
@@ -483,6 +486,49 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
               (f32x4){oacc[dg][4 * r4], oacc[dg][4 * r4 + 1], oacc[dg][4 * r4 + 2], oacc[dg][4 * r4 + 3]};
       part[2 * (D / 32) * 16 * 64 + w64] = m_run;
       part[2 * (D / 32) * 16 * 64 + 128 + w64] = l_run;
+    }
+    return;
+  }
+  if (mslots) {
+    // the query block's last item: every segment's partial (its own from
+    // the registers) rescaled to the largest reference max and summed in
+    // segment order, so the rows do not depend on which item ran last
+    if constexpr (D == 128) {
+      constexpr int MOFF = 2 * (D / 32) * 16 * 64;
+      const float* base = a.part + (size_t)bh * a.max_items * kSplitSlotFloats;
+      const int w64 = wave * 64 + lane;
+      float m = -1e30f;
+      for (int s = 0; s < a.nsegs; ++s) {
+        const int k = mslots[s];
+        if (s == s_own)
+          m = fmaxf(m, m_run);
+        else if (k >= 0)
+          m = fmaxf(m, base[(size_t)k * kSplitSlotFloats + MOFF + w64]);
+      }
+      // the own segment is the block's highest: its term starts the sum
+      const float w0 = __builtin_amdgcn_exp2f(m_run - m);
+      float l = l_run * w0;
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dg][r] *= w0;
+      for (int s = 0; s < s_own; ++s) {
+        const int k = mslots[s];
+        if (k < 0) continue;
+        const float* p = base + (size_t)k * kSplitSlotFloats;
+        const float w = __builtin_amdgcn_exp2f(p[MOFF + w64] - m);
+        l += p[MOFF + 128 + w64] * w;
+#pragma unroll
+        for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 x =
+                *reinterpret_cast<const f32x4*>(p + (((wave * (D / 32) + dg) * 4 + r4) * 64 + lane) * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oacc[dg][4 * r4 + j] += x[j] * w;
+          }
+      }
+      store_rows<D>(a, bh, qs, ql, oacc, m, l, Kp);
     }
     return;
   }
@@ -546,9 +592,10 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
 
   if constexpr (SPLIT) {
     // One item (query block, key segment) per workgroup. The grid is an upper
-    // bound; the items of all heads are dealt to the XCDs as contiguous
-    // ranges of their order (head, then segment, then longest first), so the
-    // tiles running together on an XCD read the same key segment of a head.
+    // bound; the launch's items of all heads are dealt to the XCDs as
+    // contiguous ranges of their order (head, then segment, then longest
+    // first), so the tiles running together on an XCD read the same key
+    // segment of a head.
     const int total = ((const cint*)a.item_base)[a.bh];
     const int L = blockIdx.x, x = L & 7, i = L >> 3;
     const int per = total >> 3, rem = total & 7;
@@ -560,18 +607,21 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
       if (((const cint*)a.item_base)[mid] <= flat) lo = mid; else hi = mid - 1;
     }
     const int bh = ((const cint*)a.head_order)[lo];
-    const int k = flat - ((const cint*)a.item_base)[lo];
+    const int k = flat - ((const cint*)a.item_base)[lo] + (a.item_first ? ((const cint*)a.item_first)[bh] : 0);
     const cint* it = (const cint*)a.items + ((size_t)bh * a.max_items + k) * 4;
-    const int I = it[0], off = it[1], cnt = it[2];
+    const int I = it[0], off = it[1], cnt = it[2], s_own = it[3];
     int qs, ql;
     a.qb.get(bh, I, qs, ql);
     ql = min(ql, 64);
     if (ql <= 0) return;
     const size_t qrow = (size_t)bh * a.nqb + I;
-    float* part = ((const cint*)a.nseg)[qrow] > 1 ? a.part + ((size_t)bh * a.max_items + k) * kSplitSlotFloats
-                                                    : nullptr;
-    attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride + off, cnt, part, (lds_u8*)Ks,
-                        (lds_u8*)Vs, tok, chunk_rows);
+    // first items store their partial result; a last item merges when its
+    // query block has more than one, else writes its rows
+    const bool many = ((const cint*)a.nseg)[qrow] > 1;
+    float* part = !a.item_first && many ? a.part + ((size_t)bh * a.max_items + k) * kSplitSlotFloats : nullptr;
+    const cint* mslots = a.item_first && many ? (const cint*)a.slot_of + qrow * a.nsegs : nullptr;
+    attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride + off, cnt, part, mslots, s_own,
+                        (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
     return;
   }
 
@@ -615,8 +665,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   const size_t qrow = (size_t)bh * a.nqb + I;
   // counts outside [0, kv_stride] (a caller's contract) stay inside the row
   const int cnt = min(max(((const cint*)a.kv_count)[qrow], 0), a.kv_stride);
-  attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride, cnt, nullptr, (lds_u8*)Ks, (lds_u8*)Vs,
-                      tok, chunk_rows);
+  attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride, cnt, nullptr, nullptr, 0, (lds_u8*)Ks,
+                      (lds_u8*)Vs, tok, chunk_rows);
 }
 
 // ---- split over key segments (uniform blocks, long rows)
@@ -624,20 +674,25 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
 // Per head, the kept list of every query block is cut where the key block id
 // crosses a multiple of `sg` into at most `nsegs` segments; every non-empty
 // (query block, segment) pair is an item, computed by one workgroup of the
-// forward above and, when its query block has more than one item, stored as
-// a partial result that split_merge_kernel combines. The items are ordered
-// segment-major (longest first inside a segment): tiles that run together on
-// an XCD then read the K/V blocks of one key segment, which its L2 holds
+// forward above. Two launches: the first runs every item but the last
+// (highest segment) of each query block and stores their partial results;
+// the second runs the last items, which combine the block's partials with
+// their own and write its rows. The items of a launch are ordered
+// segment-major (longest first inside a segment): tiles that run together
+// on an XCD then read the K/V blocks of one key segment, which its L2 holds
 // while they are reused. Scheduling only: every partial is the exact online
 // softmax of its segment's keys, merged in segment order.
 // Where each key segment starts in every query block's (ascending) list, one
 // wave per query block: segoff[row][s] = number of entries below s * sg;
-// nseg[row] = number of non-empty segments; slot_of[row][*] = -1.
+// nseg[row] = number of non-empty segments; slot_of[row][*] = -1. A query
+// block with no kept key block (no item) gets its zero rows and lse -inf
+// here.
 __global__ __launch_bounds__(1024) void split_rows_kernel(const int32_t* __restrict__ kv_count,
                                                           const int32_t* __restrict__ kv_index, int kv_stride,
                                                           int nqb, int nsegs, int sg, int32_t* __restrict__ segoff,
                                                           int32_t* __restrict__ slot_of,
-                                                          int32_t* __restrict__ nseg) {
+                                                          int32_t* __restrict__ nseg, uint4* __restrict__ o,
+                                                          float* __restrict__ lse, int N, int n_valid) {
   const int lane = threadIdx.x & 63;
   const int I = blockIdx.x * 16 + (threadIdx.x >> 6);
   if (I >= nqb) return;
@@ -661,21 +716,31 @@ __global__ __launch_bounds__(1024) void split_rows_kernel(const int32_t* __restr
   }
   const int ns = __popcll(__ballot(c_s > 0));
   if (lane == 0) nseg[row] = ns;
+  if (ns == 0) {                        // uniform 64-token query blocks, d = 128: 16 pieces per row
+    const int qs = 64 * I, ql = min(64, n_valid - qs);
+    const size_t r0 = (size_t)blockIdx.y * N + qs;
+    for (int u = lane; u < 16 * ql; u += 64) o[r0 * 16 + u] = make_uint4(0, 0, 0, 0);
+    if (lse && lane < ql) lse[r0 + lane] = -INFINITY;
+  }
 }
 
 // Item order of one head (one workgroup): a counting sort of the non-empty
-// (query block, segment) pairs by segment, then by descending count.
+// (query block, segment) pairs by last-of-their-block (the other items
+// first), then by segment, then by descending count. n_first[bh] = number of
+// items that are not the last of their query block.
 __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ kv_count, int kv_stride,
                                                           int nqb, int nsegs, int sg, int max_items,
                                                           const int32_t* __restrict__ segoff,
                                                           int32_t* __restrict__ items, int32_t* __restrict__ slot_of,
-                                                          int32_t* __restrict__ n_items, int32_t* __restrict__ head_work) {
-  extern __shared__ int hist[];          // [nsegs * (sg + 1)] bucket counts, then cursors
+                                                          int32_t* __restrict__ n_items, int32_t* __restrict__ n_first,
+                                                          int32_t* __restrict__ head_work) {
+  extern __shared__ int hist[];          // [2 * nsegs * (sg + 1)] bucket counts, then cursors
   __shared__ int part[1025];
   __shared__ int work;
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nbk = nsegs * (sg + 1);
+  const int half = nsegs * (sg + 1);     // buckets of the first items; the last items' follow
+  const int nbk = 2 * half;
   const int npairs = nqb * nsegs;
   for (int b = tid; b < nbk; b += 1024) hist[b] = 0;
   if (tid == 0) work = 0;
@@ -687,19 +752,24 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
     for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
     if ((tid & 63) == 0) atomicAdd(&work, w);
   }
-  // count of pair p = (I, s): the next segment's start (or the list end) minus its own
-  auto pair = [&](int p, int& I, int& s, int& off) -> int {
+  // count of pair p = (I, s): the next segment's start (or the list end)
+  // minus its own; its bucket in the counting sort (a pair is its block's
+  // last item when nothing of the list lies past its segment)
+  auto pair = [&](int p, int& I, int& s, int& off, int& bucket) -> int {
     I = p / nsegs;
     s = p - I * nsegs;
     const size_t row = (size_t)bh * nqb + I;
     off = segoff[row * nsegs + s];
-    const int end = s + 1 < nsegs ? segoff[row * nsegs + s + 1] : min(max(kv_count[row], 0), kv_stride);
-    return end - off;
+    const int total = min(max(kv_count[row], 0), kv_stride);
+    const int end = s + 1 < nsegs ? segoff[row * nsegs + s + 1] : total;
+    const int c = end - off;
+    bucket = (end == total ? half : 0) + s * (sg + 1) + (sg - min(c, sg));
+    return c;
   };
   for (int p = tid; p < npairs; p += 1024) {
-    int I, s, off;
-    const int c = pair(p, I, s, off);
-    if (c > 0) atomicAdd(&hist[s * (sg + 1) + (sg - min(c, sg))], 1);
+    int I, s, off, b;
+    const int c = pair(p, I, s, off, b);
+    if (c > 0) atomicAdd(&hist[b], 1);
   }
   __syncthreads();
   // exclusive scan of the buckets
@@ -737,17 +807,19 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
     hist[b] = run;
     run += v;
   }
+  __syncthreads();
   if (tid == 0) {
     n_items[bh] = part[1024];
+    n_first[bh] = hist[half];
     head_work[bh] = work;
   }
   __syncthreads();
   // scatter the items
   for (int p = tid; p < npairs; p += 1024) {
-    int I, s, off;
-    const int c = pair(p, I, s, off);
+    int I, s, off, b;
+    const int c = pair(p, I, s, off, b);
     if (c > 0) {
-      const int k = atomicAdd(&hist[s * (sg + 1) + (sg - min(c, sg))], 1);
+      const int k = atomicAdd(&hist[b], 1);
       int32_t* it = items + ((size_t)bh * max_items + k) * 4;
       it[0] = I;
       it[1] = off;
@@ -758,20 +830,22 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
   }
 }
 
-// Order of the heads in the item sequence, and its prefix: the sequence is
-// dealt to the 8 XCDs as contiguous ranges of equal item counts, so each XCD
-// runs about BH / 8 consecutive heads. Heads differ in kept tiles (up to 2.3x
-// at the 720p layer), so the heads are first grouped by XCD greedily --
-// heaviest first, each to the least-loaded XCD that has fewer than
-// ceil(BH / 8) -- and the groups laid out one after the other.
+// Order of the heads in the item sequences, and their prefixes: a launch's
+// sequence is dealt to the 8 XCDs as contiguous ranges of equal item counts,
+// so each XCD runs about BH / 8 consecutive heads. Heads differ in kept tiles
+// (up to 2.3x at the 720p layer), so the heads are first grouped by XCD
+// greedily -- heaviest first, each to the least-loaded XCD that has fewer
+// than ceil(BH / 8) -- and the groups laid out one after the other.
 // head_order[p] = head at position p (identity for BH > kBalanceHeads);
-// item_base[p] = items of the heads at positions before p; item_base[BH] =
-// total.
+// base_first[p] / base_last[p] = first / last items of the heads at
+// positions before p; [BH] = totals.
 constexpr int kBalanceHeads = 2048;
 __global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __restrict__ n_items,
+                                                           const int32_t* __restrict__ n_first,
                                                            const int32_t* __restrict__ head_work, int BH,
                                                            int32_t* __restrict__ head_order,
-                                                           int32_t* __restrict__ item_base) {
+                                                           int32_t* __restrict__ base_first,
+                                                           int32_t* __restrict__ base_last) {
   __shared__ int part[257];
   __shared__ int sorted[kBalanceHeads];
   __shared__ int order[kBalanceHeads];
@@ -813,79 +887,36 @@ __global__ __launch_bounds__(256) void split_prefix_kernel(const int32_t* __rest
   __syncthreads();
   const int per = (BH + 255) / 256;
   const int b0 = tid * per, b1 = min(BH, b0 + per);
-  auto items_at = [&](int p) { return n_items[BH <= kBalanceHeads ? sorted[p] : p]; };
-  int loc = 0;
-  for (int p = b0; p < b1; ++p) loc += items_at(p);
-  part[tid] = loc;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    part[256] = run;
-  }
-  __syncthreads();
-  int run = part[tid];
-  for (int p = b0; p < b1; ++p) {
-    item_base[p] = run;
-    run += items_at(p);
-  }
-  if (tid == 0) item_base[BH] = part[256];
-}
-
-// Combines the partial results of query blocks with more than one item (in
-// segment order, online: each partial is rescaled to the running maximum of
-// the reference maxima) and writes their rows; query blocks with no kept key
-// block get zero rows (and lse -inf). Blocks with one item were written by
-// the forward itself.
-__global__ __launch_bounds__(128) void split_merge_kernel(AttnArgs a) {
-  constexpr int D = 128;
-  __shared__ __align__(16) unsigned char stage[64 * D * 2];
-  const int bh = blockIdx.x / a.nqb, I = blockIdx.x - bh * a.nqb;
-  const size_t qrow = (size_t)bh * a.nqb + I;
-  const int ns = ((const cint*)a.nseg)[qrow];
-  if (ns == 1) return;
-  int qs, ql;
-  a.qb.get(bh, I, qs, ql);
-  ql = min(ql, 64);
-  if (ql <= 0) return;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dg][r] = 0.f;
-  // the largest reference max over the partials, then their sum rescaled to it
-  constexpr int MOFF = 2 * (D / 32) * 16 * 64;
-  const float* base = a.part + (size_t)bh * a.max_items * kSplitSlotFloats;
-  const cint* slots = (const cint*)a.slot_of + qrow * a.nsegs;
-  float m = -1e30f;
-  for (int s = 0; s < a.nsegs; ++s) {
-    const int k = slots[s];
-    if (k >= 0) m = fmaxf(m, base[(size_t)k * kSplitSlotFloats + MOFF + wave * 64 + lane]);
-  }
-  float l = 0.f;
-  for (int s = 0; s < a.nsegs; ++s) {
-    const int k = slots[s];
-    if (k < 0) continue;
-    const float* p = base + (size_t)k * kSplitSlotFloats;
-    const float w = __builtin_amdgcn_exp2f(p[MOFF + wave * 64 + lane] - m);
-    l += p[MOFF + 128 + wave * 64 + lane] * w;
-#pragma unroll
-    for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(p + (((wave * (D / 32) + dg) * 4 + r4) * 64 + lane) * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[dg][4 * r4 + j] += x[j] * w;
+  auto head_at = [&](int p) { return BH <= kBalanceHeads ? sorted[p] : p; };
+  auto prefix = [&](bool last, int32_t* base) {
+    auto items_at = [&](int p) {
+      const int h = head_at(p);
+      return last ? n_items[h] - n_first[h] : n_first[h];
+    };
+    int loc = 0;
+    for (int p = b0; p < b1; ++p) loc += items_at(p);
+    part[tid] = loc;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int t = 0; t < 256; ++t) {
+        const int v = part[t];
+        part[t] = run;
+        run += v;
       }
-  }
-  store_rows<D>(a, bh, qs, ql, oacc, m, l, (lds_u8*)stage);
+      part[256] = run;
+    }
+    __syncthreads();
+    int run = part[tid];
+    for (int p = b0; p < b1; ++p) {
+      base[p] = run;
+      run += items_at(p);
+    }
+    if (tid == 0) base[BH] = part[256];
+    __syncthreads();
+  };
+  prefix(false, base_first);
+  prefix(true, base_last);
 }
 
 // Processing order of uniform query blocks: longest first. The query blocks
@@ -1013,8 +1044,8 @@ constexpr int kSplitSegBlocks = 384;
 namespace {
 struct SplitLayout {
   int nsegs = 0, sg = 0, max_items = 0;
-  size_t segoff = 0, slot_of = 0, nseg = 0, n_items = 0, head_work = 0, head_order = 0, item_base = 0, items = 0,
-         part = 0, end = 0;
+  size_t segoff = 0, slot_of = 0, nseg = 0, n_items = 0, n_first = 0, head_work = 0, head_order = 0,
+         base_first = 0, base_last = 0, items = 0, part = 0, end = 0;
 };
 size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace layout of the split path after the order table; nsegs = 0 when
@@ -1025,7 +1056,7 @@ SplitLayout split_layout(int BH, int nqb, int nkb, int d) {
   if (d != 128 || nkb < kSplitMinKeyBlocks || nqb <= 0) return L;
   const int S = (nkb + kSplitSegBlocks - 1) / kSplitSegBlocks;
   const int sg = (nkb + S - 1) / S;
-  if (S < 2 || S > 63 || sizeof(int) * (size_t)S * (sg + 1) > 64 * 1024) return L;
+  if (S < 2 || S > 63 || 2 * sizeof(int) * (size_t)S * (sg + 1) > 64 * 1024) return L;
   const size_t pairs = (size_t)BH * nqb * S;
   if ((size_t)nqb * S > 0x7fffffff / 8) return L;
   L.nsegs = S;
@@ -1036,9 +1067,11 @@ SplitLayout split_layout(int BH, int nqb, int nkb, int d) {
   L.slot_of = o; o += r256(4 * pairs);
   L.nseg = o; o += r256(4 * (size_t)BH * nqb);
   L.n_items = o; o += r256(4 * (size_t)BH);
+  L.n_first = o; o += r256(4 * (size_t)BH);
   L.head_work = o; o += r256(4 * (size_t)BH);
   L.head_order = o; o += r256(4 * (size_t)BH);
-  L.item_base = o; o += r256(4 * ((size_t)BH + 1));
+  L.base_first = o; o += r256(4 * ((size_t)BH + 1));
+  L.base_last = o; o += r256(4 * ((size_t)BH + 1));
   L.items = o; o += r256(16 * pairs);
   L.part = o; o += r256(sizeof(float) * (size_t)kSplitSlotFloats * pairs);
   L.end = o;
@@ -1085,7 +1118,8 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int kmode = kvar ? 2 : kshort ? 1 : 0;
   a.tile_base = tile_ws;
   a.order = nullptr;
-  a.items = nullptr; a.item_base = nullptr; a.head_order = nullptr; a.nseg = nullptr; a.slot_of = nullptr;
+  a.items = nullptr; a.item_base = nullptr; a.item_first = nullptr; a.head_order = nullptr; a.nseg = nullptr;
+  a.slot_of = nullptr;
   a.part = nullptr;
   a.max_items = 0; a.nsegs = 0;
   // Long uniform rows with a workspace of the full size: split over key
@@ -1098,9 +1132,11 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
       a.slot_of = reinterpret_cast<int32_t*>(w + L.slot_of);
       a.nseg = reinterpret_cast<int32_t*>(w + L.nseg);
       int32_t* n_items = reinterpret_cast<int32_t*>(w + L.n_items);
+      int32_t* n_first = reinterpret_cast<int32_t*>(w + L.n_first);
       int32_t* head_work = reinterpret_cast<int32_t*>(w + L.head_work);
+      int32_t* base_first = reinterpret_cast<int32_t*>(w + L.base_first);
+      int32_t* base_last = reinterpret_cast<int32_t*>(w + L.base_last);
       a.head_order = reinterpret_cast<int32_t*>(w + L.head_order);
-      a.item_base = reinterpret_cast<int32_t*>(w + L.item_base);
       a.items = reinterpret_cast<int32_t*>(w + L.items);
       a.part = reinterpret_cast<float*>(w + L.part);
       a.max_items = L.max_items;
@@ -1108,19 +1144,26 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
       a.tiles = 0;
       a.bh = BH;
       if (!pad_done) zero_pad();
-      const size_t lds = sizeof(int) * (size_t)L.nsegs * (L.sg + 1);
+      const size_t lds = 2 * sizeof(int) * (size_t)L.nsegs * (L.sg + 1);
       split_rows_kernel<<<dim3((qb.nblocks + 15) / 16, BH), 1024, 0, s>>>(
           kv_count, kv_index, kv_stride, qb.nblocks, L.nsegs, L.sg, segoff, const_cast<int32_t*>(a.slot_of),
-          const_cast<int32_t*>(a.nseg));
+          const_cast<int32_t*>(a.nseg), reinterpret_cast<uint4*>(o), lse, N, n_valid);
       split_plan_kernel<<<BH, 1024, lds, s>>>(kv_count, kv_stride, qb.nblocks, L.nsegs, L.sg, L.max_items, segoff,
                                               const_cast<int32_t*>(a.items), const_cast<int32_t*>(a.slot_of),
-                                              n_items, head_work);
-      split_prefix_kernel<<<1, 256, 0, s>>>(n_items, head_work, BH, const_cast<int32_t*>(a.head_order),
-                                            const_cast<int32_t*>(a.item_base));
-      const long long grid = 8LL * (((long long)BH * L.max_items + 7) / 8);
-      if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-      attn_fwd_kernel<128, false, 0, true><<<(int)grid, 128, 0, s>>>(a);
-      split_merge_kernel<<<BH * qb.nblocks, 128, 0, s>>>(a);
+                                              n_items, n_first, head_work);
+      split_prefix_kernel<<<1, 256, 0, s>>>(n_items, n_first, head_work, BH, const_cast<int32_t*>(a.head_order),
+                                            base_first, base_last);
+      // every item but the last of its query block (at most all pairs but
+      // one per block), then the last items (at most one per block)
+      const long long grid1 = 8LL * (((long long)BH * (L.max_items - qb.nblocks) + 7) / 8);
+      const long long grid2 = 8LL * (((long long)BH * qb.nblocks + 7) / 8);
+      if (grid1 > 0x7fffffffLL || grid2 > 0x7fffffffLL) return hipErrorInvalidValue;
+      a.item_base = base_first;
+      a.item_first = nullptr;
+      attn_fwd_kernel<128, false, 0, true><<<(int)grid1, 128, 0, s>>>(a);
+      a.item_base = base_last;
+      a.item_first = n_first;
+      attn_fwd_kernel<128, false, 0, true><<<(int)grid2, 128, 0, s>>>(a);
       return hipGetLastError();
     }
   }
