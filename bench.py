@@ -446,11 +446,12 @@ def mfma_probe():
 
 def attn_kernel_name(w) -> str:
     # with the full workspace the library splits uniform d = 128 rows over at
-    # least 1024 key blocks into key segments (plan, items, merge); two waves
-    # per 64-row tile otherwise
+    # least 1024 key blocks into key segments (plan, then two item launches,
+    # the second merging each query block's partials); two waves per 64-row
+    # tile otherwise
     nb = -(-w.n_valid // w.block)
     if w.d == 128 and nb >= 1024:
-        return "attn_fwd_kernel (items over key segments) + split_rows/plan/prefix/merge kernels"
+        return "attn_fwd_kernel (items over key segments, two launches) + split_rows/plan/prefix kernels"
     return "attn_fwd_kernel"
 
 
@@ -622,16 +623,22 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
                 st = rocprof_stats(dirs[0])
                 att = [x for x in st if x[0].startswith("bsa::attn_fwd")]
                 call = [x for x in st if x[0].startswith(ATTN_CALL_KERNELS)]
-                lines.append(f"bench (same run): attention stage {b['stages_ms']['attention'] * 1e3:.1f} us per "
-                             f"call (HIP events around the C-ABI call), roofline.achieved "
-                             f"{b['roofline']['achieved']} TFLOP/s")
+                ev = b['stages_ms']['attention'] * 1e3
+                lines.append(f"bench (same run): attention stage {ev:.1f} us per call (HIP events around the "
+                             f"C-ABI call), roofline.achieved {b['roofline']['achieved']} TFLOP/s")
+                # calls = launches of the kernels run once per call (the split
+                # path launches the attention kernel twice per call)
+                once = [x[1] for x in call if not x[0].startswith("bsa::attn_fwd")]
+                n_calls = min(once) if once else (att[0][1] if att else 1)
                 if att:
-                    lines.append(f"rocprof {att[0][0]} average {att[0][2]:.1f} us "
-                                 f"(ratio events / kernel {b['stages_ms']['attention'] * 1e3 / att[0][2]:.3f})")
+                    a_us = att[0][1] * att[0][2] / n_calls
+                    lines.append(f"rocprof {att[0][0]}: {att[0][1] / n_calls:g} launch(es) per call, "
+                                 f"average {att[0][2]:.1f} us, {a_us:.1f} us per call "
+                                 f"(ratio events / kernel {ev / a_us:.3f})")
                 if len(call) > 1:
-                    tot = sum(x[2] for x in call)
+                    tot = sum(x[1] * x[2] for x in call) / n_calls
                     lines.append(f"rocprof kernels of one attention call ({', '.join(x[0] for x in call)}): "
-                                 f"{tot:.1f} us (ratio events / kernels {b['stages_ms']['attention'] * 1e3 / tot:.3f})")
+                                 f"{tot:.1f} us over {n_calls} calls (ratio events / kernels {ev / tot:.3f})")
                 if "backward" in b:
                     bw = [x for x in rocprof_stats(dirs[0]) if x[0].startswith("bsa::bwd_") or
                           x[0].startswith("bsa::csc_")]
@@ -657,10 +664,15 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
         prefixes = tuple(p for p in kernel.split(",") if p)
 
         def summed(d, counter):
+            # per attention call: every matching dispatch summed, over the
+            # dispatch count of the kernels launched once per call (the split
+            # path launches the attention kernel twice per call)
             names = sorted({_short(r["Kernel_Name"]) for r in _csv_rows(os.path.join(d, "run_counter_collection.csv"))
                             if _short(r["Kernel_Name"]).startswith(prefixes)})
-            vals = [rocprof_counter(d, counter, nm) for nm in names]
-            return sum(v for v, _ in vals), min((n for _, n in vals), default=0), names
+            vals = {nm: rocprof_counter(d, counter, nm) for nm in names}
+            once = [n for nm, (_, n) in vals.items() if not nm.startswith("bsa::attn_fwd")]
+            n_calls = min(once) if once else min((n for _, n in vals.values()), default=1)
+            return sum(v * n for v, n in vals.values()) / n_calls, n_calls, names
         kern = kernel
         copy = "bsa::permute_kernel<16>"
         f_att, n1, names = summed(fetch_dir, "FETCH_SIZE")
@@ -676,8 +688,8 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
         lines += [
             f"command: {command}",
             f"kernel: {kern} ({workload} workload)",
-            f"FETCH_SIZE per dispatch: {f_att:.1f} KiB over {n1} dispatches",
-            f"WRITE_SIZE per dispatch: {w_att:.1f} KiB over {n2} dispatches",
+            f"FETCH_SIZE per call: {f_att:.1f} KiB over {n1} calls",
+            f"WRITE_SIZE per call: {w_att:.1f} KiB over {n2} calls",
             f"copy calibration ({copy}, identity permutation reading and writing 1 GiB): "
             f"FETCH_SIZE {f_cp:.1f} KiB (x{f_scale:.3f}), WRITE_SIZE {w_cp:.1f} KiB (x{w_scale:.3f}) over {n3}/{n4}",
             f"fetch_bytes_per_launch: {fetch_b:.6g}",

@@ -379,8 +379,9 @@ def test_hunyuan720_sampled(gpu_lib, part):
 @pytest.mark.parametrize("path", ["split", "one_wave"])
 def test_attn_long_rows(gpu_lib, path):
     # >= 1024 uniform key blocks at d = 128: with the full workspace the rows
-    # run split over key segments (plan, items, partials, merge); with only
-    # the order table the one-wave kernel runs them whole. Random kept lists
+    # run split over key segments (plan, items, partials merged by each query
+    # block's last item); with only the order table the one-wave kernel runs
+    # them whole. Random kept lists
     # (a dense row, rows inside one segment, a row keeping nothing, the
     # ragged last block) on a ragged length, sampled query blocks (and their
     # log-normalisers) against the oracle, then repeat runs and poisoned
