@@ -56,6 +56,67 @@ constexpr float kMassScale = 0x1p31f; // block masses in 2^-31 fixed point
 template <int W>
 constexpr int hist_words() { return W >= 16 ? 256 : 512; }
 constexpr int kDigit0 = 192;          // first-digit value of p = 2^-31 (bits(p) >> 22)
+
+// Wave-wide scans and reductions on DPP lane moves (GFX9 controls): four
+// shifts inside each row of 16 lanes, then the row broadcasts of lanes 15
+// and 31 into the following rows. A step costs a VALU move with no trip
+// through the LDS crossbar, which is what the shuffles of a radix pass
+// chain on. Source lanes outside a row, and rows the mask leaves out, read
+// the identity `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t id, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long id, unsigned long long x) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)id, (uint32_t)x);
+  const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(id >> 32), (uint32_t)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ unsigned long long scan_u64(unsigned long long x) {
+  x += dpp_u64<kRowShr1, 0xf>(0, x);
+  x += dpp_u64<kRowShr2, 0xf>(0, x);
+  x += dpp_u64<kRowShr4, 0xf>(0, x);
+  x += dpp_u64<kRowShr8, 0xf>(0, x);
+  x += dpp_u64<kRowBcast15, 0xa>(0, x);
+  x += dpp_u64<kRowBcast31, 0xc>(0, x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long x, int l) {   // l wave-uniform
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long sum_u64(unsigned long long x) { return lane_u64(scan_u64(x), 63); }
+__device__ __forceinline__ float max_f32(float x) {
+  const uint32_t id = __float_as_uint(-INFINITY);
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowShr1, 0xf>(id, __float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowShr2, 0xf>(id, __float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowShr4, 0xf>(id, __float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowShr8, 0xf>(id, __float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowBcast15, 0xa>(id, __float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp_u32<kRowBcast31, 0xc>(id, __float_as_uint(x))));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
+}
+__device__ __forceinline__ unsigned long long min_u64(unsigned long long x) {
+  const unsigned long long id = ~0ull;
+  unsigned long long t;
+  t = dpp_u64<kRowShr1, 0xf>(id, x); x = t < x ? t : x;
+  t = dpp_u64<kRowShr2, 0xf>(id, x); x = t < x ? t : x;
+  t = dpp_u64<kRowShr4, 0xf>(id, x); x = t < x ? t : x;
+  t = dpp_u64<kRowShr8, 0xf>(id, x); x = t < x ? t : x;
+  t = dpp_u64<kRowBcast15, 0xa>(id, x); x = t < x ? t : x;
+  t = dpp_u64<kRowBcast31, 0xc>(id, x); x = t < x ? t : x;
+  return lane_u64(x, 63);
+}
+// first lane whose predicate holds (64 when none)
+__device__ __forceinline__ int first_lane(bool p) {
+  const unsigned long long m = __ballot(p);
+  return m ? __builtin_ctzll(m) : kWave;
+}
 }  // namespace
 
 // Selection of one row with its elements held in registers (E per lane,
@@ -78,7 +139,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
     pb[t] = __float_as_uint(sj);
     mx = fmaxf(mx, sj);
   }
-  mx = wave_max(mx);
+  mx = max_f32(mx);
   unsigned long long z = 0;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
@@ -92,7 +153,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   auto key_of = [&](int t) -> unsigned long long {
     return ((unsigned long long)pb[t] << kIdxBits) | (unsigned)((1 << kIdxBits) - 1 - (lane + kWave * t));
   };
-  z = wave_sum_u64(z);
+  z = sum_u64(z);
   const double tt = ceil((double)thr * (double)z);
   const unsigned long long tint = tt >= (double)z ? z : (unsigned long long)tt;
 
@@ -145,13 +206,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
         const bool ok = lane < ncand && through >= tint;
         // smallest qualifying key; some candidate always qualifies since
         // below + all candidate mass >= the threshold
-        unsigned long long best = ok ? ck : ~0ull;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const unsigned long long other = __shfl_xor(best, o);
-          best = other < best ? other : best;
-        }
-        kstar = best;
+        kstar = min_u64(ok ? ck : ~0ull);
         done = true;
         wave_lds_sync();
         break;
@@ -174,9 +229,12 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
       unsigned long long v = 0;
 #pragma unroll
       for (int q = 0; q < COPIES; ++q) v += h0[q * kWave + lane];
-      const unsigned long long through = wave_incl_scan_u64(v, lane);
-      const int b0 = wave_min_i32(through >= tint ? lane : 1 << 30);
-      below = __shfl(through - v, b0);
+      // the cumulative mass grows with the lane: the first lane reaching the
+      // threshold holds the digit
+      const unsigned long long through = scan_u64(v);
+      const int f0 = first_lane(through >= tint);
+      const int b0 = f0 < kWave ? f0 : 1 << 30;   // none: unreachable for finite inputs
+      below = lane_u64(through - v, f0 & (kWave - 1));
       prefix = (unsigned)(kDigit0 + b0);
       wave_lds_sync();
       continue;
@@ -213,7 +271,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
       hv[q] = h[lane * (kBins / kWave) + q];
       loc += hv[q];
     }
-    const unsigned long long incl = wave_incl_scan_u64(loc, lane);
+    const unsigned long long incl = scan_u64(loc);
     const unsigned long long run = incl - loc;
     const unsigned long long need = tint > below ? tint - below : 0ull;
     int cand = 1 << 30;
@@ -228,9 +286,13 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
         before = through - hv[q];
       }
     }
-    int b = wave_min_i32(cand);
-    if (b >= kBins) b = kBins - 1;   // unreachable for finite inputs
-    before = __shfl(before, b / (kBins / kWave));
+    // the first lane whose bins reach the need holds the digit (the
+    // cumulative mass grows with the lane); none: unreachable for finite
+    // inputs, the last bin
+    const int fl = first_lane(incl >= need) & (kWave - 1);
+    int b = __builtin_amdgcn_readlane(cand, fl);
+    if (b >= kBins) b = kBins - 1;
+    before = lane_u64(before, fl);
     below += before;
     prefix = (prefix << width) | (unsigned)b;
     wave_lds_sync();
@@ -243,7 +305,11 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   const bool none = (kstar >> kIdxBits) > 0xffffffffull;   // k* past every key: keep nothing by the CDF
 #pragma unroll
   for (int t = 0; t < E; ++t) {
-    const int j = lane + kWave * t;
+    // j through an empty asm: the window coordinates of the lane's E blocks
+    // are the same for every row, and hoisted out of the row loop they
+    // would hold 3 E registers (spilled)
+    int j = lane + kWave * t;
+    asm volatile("" : "+v"(j));
     const uint32_t lo = (uint32_t)((1 << kIdxBits) - 1 - j);
     bool keep = j < nkb && !none && (pb[t] > ks_hi || (pb[t] == ks_hi && lo >= ks_lo));
     if (keep && ksz && ksz[j] <= 0) keep = false;
