@@ -60,7 +60,9 @@ namespace bsa {
 // Key blocks: KMODE 0 = uniform 64-token blocks, 1 = descriptor blocks of at
 // most 64 tokens (each one chunk, loaded like a uniform block from its own
 // start), 2 = descriptor blocks of any length (keys gathered row by row into
-// 64-key chunks).
+// 64-key chunks), 3 = descriptor blocks of any length as contiguous runs
+// (each kept block cut into 64-key chunks from its own start, the last one
+// partial: no gathering, at the price of the partial chunks).
 template <int D>
 __device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, int ql, const f32x16* oacc,
                                            float m_run, float l_run, lds_u8* Kp);
@@ -83,6 +85,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   constexpr float TAU = 8.f;                   // rescale O only when a row max grows by > 2^TAU
   constexpr uint32_t OOB = 0xFFFFFFF0u;        // lane offset past every descriptor: loads zeros
   constexpr bool KVAR = KMODE == 2;            // gathered keys
+  constexpr bool KRUN = KMODE == 3;            // runs
   // A chunk's length doubles as "the chunk exists" (> 0). A kept short block
   // with no tokens is still a chunk: its length is coded as kEmpty (no rows
   // loaded, every key masked).
@@ -182,8 +185,33 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
   };
 
   // ---- chunk descriptors
+  // Runs: a cursor (entry, piece) over the kept blocks, advanced once per
+  // chunk in chunk order (scalar loads; blocks without tokens and invalid
+  // ids give no chunk).
+  int r_e = 0, r_p = 0;
+  auto next_run = [&](int& ks, int& kl) {
+    ks = 0;
+    kl = 0;
+    while (r_e < cnt) {
+      const int J = slist[r_e];
+      int st = 0, n = 0;
+      if ((unsigned)J < (unsigned)a.nkb) a.kb.get(bh, J, st, n);
+      if (64 * r_p < n) {
+        ks = st + 64 * r_p;
+        kl = min(64, n - 64 * r_p);
+        ++r_p;
+        return;
+      }
+      ++r_e;
+      r_p = 0;
+    }
+  };
   // Uniform blocks: chunk c is key block list[c] (scalar loads).
   auto chunk_uniform = [&](int c, int& ks, int& kl) {
+    if constexpr (KRUN) {
+      next_run(ks, kl);                // chunks are asked for in order
+      return;
+    }
     if (c >= cnt) { ks = 0; kl = 0; return; }
     int J = slist[c];
     J = (unsigned)J < (unsigned)a.nkb ? J : a.nkb - 1;   // invalid ids stay in bounds
@@ -582,6 +610,33 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, in
   }
 }
 
+// Blocks of any length: runs when cutting each kept block into its own
+// 64-key chunks costs at most a quarter more chunks than packing the keys
+// densely (then no token lists are built per chunk); else gathering. Every
+// wave computes the same answer.
+__device__ __forceinline__ bool runs_pay(const AttnArgs& a, int bh, const int32_t* list, int cnt) {
+  const int lane = threadIdx.x & 63;
+  int padded = 0, keys = 0;
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
+    const int e = e0 + lane;
+    int n = 0;
+    if (e < cnt) {
+      const int J = list[e];
+      int st = 0;
+      if ((unsigned)J < (unsigned)a.nkb) a.kb.get(bh, J, st, n);
+      n = max(n, 0);
+    }
+    padded += (n + 63) >> 6;
+    keys += n;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    padded += __shfl_xor(padded, o);
+    keys += __shfl_xor(keys, o);
+  }
+  return 4 * padded <= 5 * ((keys + 63) >> 6);
+}
+
 template <int D, bool QVAR, int KMODE, bool SPLIT>
 __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = 64 * D * 2;
@@ -665,8 +720,14 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(AttnArgs a) {
   const size_t qrow = (size_t)bh * a.nqb + I;
   // counts outside [0, kv_stride] (a caller's contract) stay inside the row
   const int cnt = min(max(((const cint*)a.kv_count)[qrow], 0), a.kv_stride);
-  attn_tile<D, KMODE>(a, bh, I, qs, ql, a.kv_index + qrow * a.kv_stride, cnt, nullptr, nullptr, 0, (lds_u8*)Ks,
-                      (lds_u8*)Vs, tok, chunk_rows);
+  const int32_t* list = a.kv_index + qrow * a.kv_stride;
+  if constexpr (KMODE == 2) {
+    if (runs_pay(a, bh, list, cnt)) {
+      attn_tile<D, 3>(a, bh, I, qs, ql, list, cnt, nullptr, nullptr, 0, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
+      return;
+    }
+  }
+  attn_tile<D, KMODE>(a, bh, I, qs, ql, list, cnt, nullptr, nullptr, 0, (lds_u8*)Ks, (lds_u8*)Vs, tok, chunk_rows);
 }
 
 // ---- split over key segments (uniform blocks, long rows)
