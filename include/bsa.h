@@ -196,9 +196,13 @@ int bsa_build_centroid_mask(const float* cq, const int32_t* q_sizes,
  * Block-sparse attention
  * ------------------------------------------------------------------------ */
 
-/* Workspace bytes needed by bsa_block_sparse_attn_fwd: int32 scratch of
- * B*H*(nqb+1) entries (the processing order of the query blocks, or the tile
- * table of variable-size query blocks). */
+/* Workspace bytes of bsa_block_sparse_attn_fwd with every path available.
+ * The call needs at least int32 B*H*(nqb+1) entries (the processing order
+ * of uniform query blocks, or the tile table of variable-size query
+ * blocks); with the bytes returned here it also runs, for uniform blocks
+ * over rows of at least 1024 key blocks at d = 128, the split over key
+ * segments (its tables and fp32 partial results). nqb: number of query
+ * blocks (uniform: ceil(N / 64)). */
 size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
                                            const bsa_blocks* qb);
 
@@ -217,13 +221,17 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
  *   o         bf16 [B,H,N,d] (device); every row of every query block is
  *             written, rows n_valid..N-1 are zeroed, other rows untouched
  *   qb, kb    block descriptors (NULL = uniform `block`-token blocks,
- *             block = 64). Query blocks of any length are tiled by 64 rows;
- *             key blocks of any length are gathered into 64-key tiles.
+ *             block = 64). Query blocks of any length are tiled by 64 rows.
+ *             Key blocks of any length are cut into 64-key chunks from
+ *             their starts where that takes at most a quarter more chunks
+ *             than packing the keys densely, else gathered row by row into
+ *             packed 64-key chunks (decided per query block).
  *   kv_count, kv_index, kv_stride   as produced by the mask stage; ids must
  *             be valid key blocks (the caller's contract)
  *   scale     > 0, or <= 0 for 1/sqrt(d)
- *   ws        workspace of bsa_block_sparse_attn_fwd_workspace(...) bytes
- *             (device, 4-byte aligned; contents are overwritten)
+ *   ws        workspace of bsa_block_sparse_attn_fwd_workspace(...) bytes,
+ *             or at least 4*B*H*(nqb+1) bytes (then without the split);
+ *             device, 16-byte aligned, contents overwritten
  * Limits: one head of K or V (N*d*2 bytes) must stay below 4 GiB
  * (BSA_EUNSUPPORTED otherwise).
  * Uniform query blocks are scheduled longest first (most kept key blocks

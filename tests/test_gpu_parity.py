@@ -464,7 +464,7 @@ def _random_partition(rng, n, lens=(0, 1, 7, 17, 33, 64, 65, 100, 150, 230)):
                                              (128, True, "qshort")])
 def test_attn_variable_blocks_random(gpu_lib, d, per_head, mode):
     # "any": query blocks of any length (tiled by 64 rows) and key blocks of
-    # any length (gathered into 64-row chunks), shared or per head; "short":
+    # any length (runs or gathered 64-row chunks), shared or per head; "short":
     # blocks of at most 64 tokens declared as such (one tile / chunk each);
     # "qshort": short query blocks with gathered key blocks
     bsa = gpu_lib
@@ -513,6 +513,16 @@ def test_attn_variable_blocks_random(gpu_lib, d, per_head, mode):
     o = bsa.block_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(cnt[None]).cuda(),
                                   torch.from_numpy(idx[None]).cuda(), n_valid=nv, qb=qb, kb=kb)
     o = _np(o)
+    if mode == "any":
+        # the list of a query block runs as contiguous key runs when they take
+        # at most a quarter more 64-key chunks than packing, else gathered:
+        # the case holds both kinds
+        kinds = set()
+        for h in range(H):
+            for i in range(nqb):
+                lens = kln[h if per_head else 0][keep[h, i]]
+                kinds.add(4 * int(((lens + 63) // 64).sum()) <= 5 * ((int(lens.sum()) + 63) // 64))
+        assert kinds == {True, False}
     assert (o[:, :, nv:] == 0).all()
     for h in range(H):
         hi = h if per_head else 0
