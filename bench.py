@@ -626,10 +626,10 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
                 ev = b['stages_ms']['attention'] * 1e3
                 lines.append(f"bench (same run): attention stage {ev:.1f} us per call (HIP events around the "
                              f"C-ABI call), roofline.achieved {b['roofline']['achieved']} TFLOP/s")
-                # calls = launches of the kernels run once per call (the split
-                # path launches the attention kernel twice per call)
-                once = [x[1] for x in call if not x[0].startswith("bsa::attn_fwd")]
-                n_calls = min(once) if once else (att[0][1] if att else 1)
+                # calls = the fewest launches of any kernel of the call (the
+                # split path launches the attention kernel twice per call; the
+                # backward launches the order kernel too)
+                n_calls = min((x[1] for x in call), default=1)
                 if att:
                     a_us = att[0][1] * att[0][2] / n_calls
                     lines.append(f"rocprof {att[0][0]}: {att[0][1] / n_calls:g} launch(es) per call, "
