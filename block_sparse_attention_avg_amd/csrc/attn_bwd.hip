@@ -222,6 +222,9 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
     tile_load<D, 4>(vh, ks1, kl1, Vn, wave, off);
     wait_vm<2 * T::NI>();                          // this wave's share of chunk c landed
     wg_barrier();                                  // and the other waves'
+    // the score products and the exp/pack that follow go first among the
+    // waves sharing this SIMD; the other workgroup's loads fill the gaps
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -240,6 +243,7 @@ __device__ __forceinline__ void bwd_dq_tile(const BwdArgs& a, int L, int BH, uns
       }
       pw[r >> 3][(r & 7) >> 1] = pack2(d2[0], d2[1]);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const bf16x8 ds = __builtin_bit_cast(bf16x8, (u32x4){pw[hh][0], pw[hh][1], pw[hh][2], pw[hh][3]});
@@ -367,6 +371,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
     issue(c + 1, Qn, Gn);
     wait_vm<2 * T::NI + 1>();                      // this wave's share of chunk c landed
     wg_barrier();                                  // and the other waves'
+    __builtin_amdgcn_s_setprio(1);                 // as in the query-tile step
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -395,6 +400,7 @@ __device__ __forceinline__ void bwd_dkdv_tile(const BwdArgs& a, int L, int BH, u
       pd[r4 >> 1][2 * (r4 & 1) + 0] = pack2(d[0], d[1]);
       pd[r4 >> 1][2 * (r4 & 1) + 1] = pack2(d[2], d[3]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // the dV wave keeps its P and hands over its dS, the dK wave the reverse
     u32x4 own[2];
 #pragma unroll
