@@ -8,9 +8,11 @@
 //
 // Phase 1 -- scores. s[r][J] = scale * qbar_r . kbar_J (+ log n_J) for all
 // key blocks, on fp32 MFMA 16x16x4 (A = 16 pooled query rows, B = 16 pooled
-// key rows, the 4-wide k slot of the MFMA split over the four 16-lane groups
-// so each lane streams a contiguous quarter of the channel vector). The R x nkb
-// fp32 score rows stay in LDS; the reduced map never touches HBM.
+// key rows, the 4-wide k slot of the MFMA split over the four 16-lane
+// groups). Lane group g takes the 16-byte pieces 4s + g of a row, so one
+// load instruction reads 64 contiguous bytes of each of its 16 rows rather
+// than 16 bytes of 64 separate lines. The R x nkb fp32 score rows stay in
+// LDS; the reduced map never touches HBM.
 //
 // Phase 2 -- selection, one wave per row (rows of up to 2048 key blocks are
 // held in registers, longer rows are streamed from LDS). p_J = exp(s_J - max)
@@ -342,40 +344,29 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
   {
     const int row = row0 + i16;
     const bool ok = i16 < R && row < nqb;
-    const float4* src =
-        reinterpret_cast<const float4*>(qbar + ((size_t)bh * nqb + (ok ? row : 0)) * D + g * KQ);
+    const float4* src = reinterpret_cast<const float4*>(qbar + ((size_t)bh * nqb + (ok ? row : 0)) * D);
 #pragma unroll
     for (int s = 0; s < KQ / 4; ++s) {
-      const float4 v = ok ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = ok ? src[4 * s + g] : make_float4(0.f, 0.f, 0.f, 0.f);
       a[4 * s + 0] = v.x; a[4 * s + 1] = v.y; a[4 * s + 2] = v.z; a[4 * s + 3] = v.w;
     }
   }
   const float* kbh = kbar + (size_t)bh * nkb * D;
   const int ntiles = (nkb + 15) >> 4;
-  // key rows of tile t for this lane (B operand), loaded one tile ahead
+  // key rows of tile t for this lane (B operand). Rows past nkb read the
+  // last row (their scores are never stored), so every load is
+  // unconditional and the compiler can count them.
   auto load_b = [&](int t, float* b) {
-    const int key = t * 16 + i16;
-    const bool kok = key < nkb;
-    const float4* src = reinterpret_cast<const float4*>(kbh + (size_t)(kok ? key : 0) * D + g * KQ);
+    const int key = min(t * 16 + i16, nkb - 1);
+    const float4* src = reinterpret_cast<const float4*>(kbh + (size_t)key * D);
 #pragma unroll
     for (int s4 = 0; s4 < KQ / 4; ++s4) {
-      const float4 v = kok ? src[s4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = src[4 * s4 + g];
       b[4 * s4 + 0] = v.x; b[4 * s4 + 1] = v.y; b[4 * s4 + 2] = v.z; b[4 * s4 + 3] = v.w;
     }
   };
-  // the next tile's key rows are prefetched into registers when few waves
-  // share the CU; with more waves the others hide the load latency
-  constexpr bool PF = W <= 4;
-  float b[KQ], bn[PF ? KQ : 1] = {};
-  if (PF && wave < ntiles) load_b(wave, b);
-  for (int t = wave; t < ntiles; t += W) {
+  auto score_tile = [&](int t, const float* b) {
     const int key = t * 16 + i16;
-    const bool kok = key < nkb;
-    if constexpr (PF) {
-      if (t + W < ntiles) load_b(t + W, bn);
-    } else {
-      load_b(t, b);
-    }
     // four independent accumulation chains, summed at the end
     f32x4 acc4[4];
 #pragma unroll
@@ -383,7 +374,7 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
 #pragma unroll
     for (int s = 0; s < KQ; ++s) acc4[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc4[s & 3], 0, 0, 0);
     const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    if (kok) {
+    if (key < nkb) {
       float bias = 0.f;
       bool excluded = false;
       if (const int32_t* ks = sz.krow(bh, nkb)) {
@@ -397,10 +388,20 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
         if (rr < R) sc[rr * nkb_pad + key] = excluded ? -INFINITY : acc[v] * scale + bias;
       }
     }
-    if constexpr (PF) {
-#pragma unroll
-      for (int s4 = 0; s4 < KQ; ++s4) b[s4] = bn[s4];
-    }
+  };
+  // Two register buffers in turn: the loads of a wave's next tile are
+  // issued before the MFMAs of the current one (the scheduling barrier
+  // keeps them there), so they land while the products run.
+  float b0[KQ], b1[KQ];
+  if (wave < ntiles) load_b(wave, b0);
+  for (int t = wave; t < ntiles; t += 2 * W) {
+    load_b(min(t + W, ntiles - 1), b1);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile(t, b0);
+    if (t + W >= ntiles) break;
+    load_b(min(t + 2 * W, ntiles - 1), b0);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile(t + W, b1);
   }
   __syncthreads();
 

@@ -251,6 +251,47 @@ def test_mask_long_rows(gpu_lib, nkb):
     assert (cnt >= 1).all()
 
 
+@pytest.mark.parametrize("nkb,d,H,nv_cut,win", [(1025, 128, 3, 0, None), (1500, 64, 2, 37, None),
+                                                   (2048, 128, 2, 0, None), (1200, 128, 2, 20, (3, 20, 20, 1, 2, 2))])
+def test_mask_rows_1025_to_2048(gpu_lib, nkb, d, H, nv_cut, win):
+    """Rows of 1025..2048 key blocks (the 720p layer's class; 8 waves share
+    16 score rows held in registers): both head dims, several heads, a
+    ragged last block, row counts that are not a multiple of 16, the
+    2048-block edge where the score rows and histograms fill the LDS, and
+    the window union."""
+    rng = np.random.default_rng(nkb + d)
+    nv = nkb * 64 - nv_cut
+    N = nkb * 64
+    ph = rng.normal(size=(N, 8)) @ rng.normal(size=(8, d)) * 0.7
+    x = (ph[None, None] + 0.3 * rng.normal(size=(2, H, N, d))).astype(np.float32)
+    x[:, :, nv:] = 0
+    q = torch.from_numpy(x[0][None]).to(torch.bfloat16)
+    k = torch.from_numpy(x[1][None]).to(torch.bfloat16)
+    say(f"mask rows nkb={nkb} d={d} H={H} n_valid={nv} window={win}")
+    cnt, idx = gpu_lib.build_block_mask(q.cuda(), k.cuda(), 0.2, window=win, n_valid=nv)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    st, ln = ol.raster_blocks(nv)
+    assert len(st) == nkb
+    W = None
+    if win is not None:
+        nt, ny, nx = win[:3]
+        J = np.arange(nkb)
+        coords = np.stack([J // (nx * ny), (J // nx) % ny, J % nx], axis=1)
+        W = ol.window_blocks(coords, coords, *win[3:])
+    total = 0
+    for h in range(H):
+        keep = keep_from_lists(cnt[0, h], idx[0, h], nkb)
+        rows = np.unique(np.concatenate([np.arange(h, nkb, 23), np.arange(nkb - 9, nkb)]))
+        _, P = om.block_mask(_np(q[0, h]), _np(k[0, h]), st, ln, st, ln, 0.2)
+        bad = mask_mismatches(P[rows], 0.2, keep[rows], window=None if W is None else W[rows])
+        if W is not None:
+            assert (keep >= W).all(), "window bits must be set"
+        say(f"  head {h}: kept {keep[rows].sum()} of {keep[rows].size}, mismatches {bad}")
+        total += bad
+    assert total == 0
+    assert (cnt >= 1).all()
+
+
 # ------------------------------------------------------------------- attention
 
 def _attn_case(bsa, w, q, k, v, heads, nsample, seed=0, thr=None):
