@@ -611,8 +611,10 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int bh, int qs, in
 }
 
 // Blocks of any length: runs when cutting each kept block into its own
-// 64-key chunks costs at most a quarter more chunks than packing the keys
-// densely (then no token lists are built per chunk); else gathering. Every
+// 64-key chunks costs at most twice the chunks of packing the keys densely
+// (then no token lists are built per chunk); else gathering. A gathered
+// chunk costs more than 1.5 run chunks (one wave builds its token list
+// while the others wait), so runs win up to about twice the chunks. Every
 // wave computes the same answer.
 __device__ __forceinline__ bool runs_pay(const AttnArgs& a, int bh, const int32_t* list, int cnt) {
   const int lane = threadIdx.x & 63;
@@ -634,7 +636,7 @@ __device__ __forceinline__ bool runs_pay(const AttnArgs& a, int bh, const int32_
     padded += __shfl_xor(padded, o);
     keys += __shfl_xor(keys, o);
   }
-  return 4 * padded <= 5 * ((keys + 63) >> 6);
+  return padded <= 2 * ((keys + 63) >> 6);
 }
 
 template <int D, bool QVAR, int KMODE, bool SPLIT>

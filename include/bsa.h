@@ -223,8 +223,8 @@ size_t bsa_block_sparse_attn_fwd_workspace(int B, int H, int nqb,
  *   qb, kb    block descriptors (NULL = uniform `block`-token blocks,
  *             block = 64). Query blocks of any length are tiled by 64 rows.
  *             Key blocks of any length are cut into 64-key chunks from
- *             their starts where that takes at most a quarter more chunks
- *             than packing the keys densely, else gathered row by row into
+ *             their starts where that takes at most twice the chunks of
+ *             packing the keys densely, else gathered row by row into
  *             packed 64-key chunks (decided per query block).
  *   kv_count, kv_index, kv_stride   as produced by the mask stage; ids must
  *             be valid key blocks (the caller's contract)
