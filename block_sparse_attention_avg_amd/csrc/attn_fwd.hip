@@ -47,12 +47,15 @@ namespace bsa {
 //              instruction with exp2 / row sum / bf16 pack of S(c) on the
 //              VALU (independent work, so the two pipes overlap in one wave);
 //   region B:  O^T += V(c)^T P(c)^T on MFMA.
-// Loads: K(c+2) is issued once every wave has finished region A, V(c+1) once
-// every wave has finished region B. Each iteration issues exactly one K and
-// one V tile load (after the last chunk they re-load rows of a chunk that
-// exists into the free buffer, and the extra S is discarded), so the number
-// of loads in flight is the same on every path. The loop body is unrolled
-// twice so S(c) and S(c+1) swap registers instead of being copied.
+// Loads and barriers, two per iteration: at the top every wave waits for its
+// share of K(c+1), and the barrier then also tells that every wave is done
+// with region B of c-1, so V(c) goes out into the free V buffer (it lands
+// during region A). After region A every wave waits for its share of V(c);
+// the second barrier also tells that K(c+1) has been read, so K(c+2) goes
+// out (it lands during region B). One tile is in flight at each wait. After
+// the last chunk no K is loaded and the extra S (from the stale buffer) is
+// discarded. The loop body is unrolled twice so S(c) and S(c+1) swap
+// registers instead of being copied.
 //
 // Loads go through buffer descriptors that end at the chunk's last row:
 // rows past it (a partial last block, gathered rows past the chunk) read as
@@ -365,11 +368,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     } else {
       chunk_uniform(c + 2, ks_2, kl_2);         // scalar load, lands by the barrier
     }
-    // outstanding loads, oldest first: [K(c+1)] [V(c)]
-    wait_vm<NI>();                     // K(c+1) landed
+    // outstanding: K(c+1) only
+    wait_vm<0>();                      // this wave's share of K(c+1) landed
     wait_lgkm0();
-    wg_barrier();
+    wg_barrier();                      // every share landed; every wave is done with V(c-1)
     if constexpr (KVAR) chunk_info(c + 2, ks_2, kl_2);
+    issue_tile(true, ks_c, kl, tok + (c & 3) * 64);   // V(c), lands during region A
 
     // Region A runs at raised wave priority: when the two waves of a SIMD are
     // in different regions, the one interleaving S MFMAs with the softmax
@@ -422,20 +426,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
         pf[kb][hh] = __builtin_bit_cast(bf16x8, (u32x4){pw[kb][hh][0], pw[kb][hh][1], pw[kb][hh][2], pw[kb][hh][3]});
 
     __builtin_amdgcn_s_setprio(0);
-    wg_barrier();                      // every wave is done reading K(c+1)
-    {
-      // K(c+2); without a chunk c+2 a re-load of a chunk that has rows
-      // (c+1 if it exists, else c itself) into the free buffer
-      const int kc = kl_2 > 0 ? c + 2 : (kl_n > 0 ? c + 1 : c);
-      const int ks_k = kl_2 > 0 ? ks_2 : (kl_n > 0 ? ks_n : ks_c);
-      const int kl_k = kl_2 > 0 ? kl_2 : (kl_n > 0 ? kl_n : kl);
-      issue_tile(false, ks_k, kl_k, tok + (kc & 3) * 64);
-    }
+    wait_vm<0>();                      // this wave's share of V(c) landed
+    wg_barrier();                      // every share landed; every wave is done reading K(c+1)
+    if (kl_2 > 0) issue_tile(false, ks_2, kl_2, tok + ((c + 2) & 3) * 64);   // K(c+2), lands during region B
 
     // ---- region B: O^T += V(c)^T P(c)^T on MFMA || row max of S(c+1)
-    // outstanding loads, oldest first: [V(c)] [K(c+2)]
-    wait_vm<NI>();                     // V(c) landed
-    wg_barrier();
     mask_tail(sn, kl_n);
     float mx = -INFINITY;
     {
@@ -456,13 +451,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wg_barrier();                      // every wave is done reading V(c)
-    {
-      // V(c+1), or a re-load of chunk c's rows when there is no chunk c+1
-      const bool more = kl_n > 0;
-      const int vc = more ? c + 1 : c;
-      issue_tile(true, more ? ks_n : ks_c, more ? kl_n : kl, tok + (vc & 3) * 64);
-    }
     settle_max(mx);                    // reference max for S(c+1)
     // advance: chunk c+1 becomes current
     ks_c = ks_n; kl = kl_n;
@@ -477,13 +465,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, int bh, int I, int 
     wg_barrier();
     compute_s(sA);
     wg_barrier();
-    {
-      const bool more = kl1 > 0;
-      issue_tile(false, more ? ks1 : ks0, more ? kl1 : kl0, tok + (more ? 1 : 0) * 64);
-    }
-    // V0 after K1: an iteration starts with loads outstanding in the order
-    // [K(c+1)] [V(c)]
-    issue_tile(true, ks0, kl0, tok);
+    if (kl1 > 0) issue_tile(false, ks1, kl1, tok + 64);   // K1; V0 goes out in the first iteration
     mask_tail(sA, kl0);
     {
       float mx = -INFINITY;
