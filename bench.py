@@ -630,6 +630,15 @@ def rocprof_summary(kind: str, dirs, bench_log=None, command="", kernel="", work
                 # split path launches the attention kernel twice per call; the
                 # backward launches the order kernel too)
                 n_calls = min((x[1] for x in call), default=1)
+                paths = bool(b.get("paths")) or any(isinstance(v, dict) and v.get("paths")
+                                                     for v in b.get("also", {}).values())
+                if paths:
+                    # the variant paths launch the same kernels: no per-call
+                    # comparison with the attention stage's events
+                    att, call = [], []
+                    lines.append("rocprof: the variant paths of this run launch the attention kernels too, so "
+                                 "launch counts are not per attention call; see the paths' own timings in the "
+                                 "bench line")
                 if att:
                     a_us = att[0][1] * att[0][2] / n_calls
                     lines.append(f"rocprof {att[0][0]}: {att[0][1] / n_calls:g} launch(es) per call, "
