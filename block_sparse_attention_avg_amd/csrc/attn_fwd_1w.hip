@@ -115,22 +115,7 @@ __device__ __forceinline__ void attn_tile_1w(const AttnArgs& a, int bh, int I, i
   const cint* slist = (const cint*)list;
 
   // ---- per-lane LDS offsets (loop invariant)
-  // K operand of S^T: row 32kb + l32, piece 2c + half.
-  const int fk = swz<D>(l32 & 15);
-  // V^T operand via the transpose read: lane (16-lane group g, slot 4j+q)
-  // addresses key row 32kb + 16hh + 8t + 4*half + j, channels
-  // 32dg + 16(g&1) + 4q .. +3, so the lane receives channel 32dg + l32 of
-  // keys 32kb + 16hh + 8t + 4*half + 0..3 -- the P^T slot order.
-  const int g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
-  int voff[D / 32][2];
-#pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = 8 * t + 4 * half + sj;
-      const int piece = 4 * dg + 2 * g16 + (sq >> 1);
-      voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
-    }
+  const KvOperands<D> kvo(lane);
   uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -162,18 +147,8 @@ __device__ __forceinline__ void attn_tile_1w(const AttnArgs& a, int bh, int I, i
   };
 
   // ---- LDS operand reads
-  auto k_read = [&](int j) -> bf16x8 {
-    const int cc = j >> 1, kb = j & 1;
-    const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
-  };
-  auto v_read = [&](int j) -> bf16x8 {
-    const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
-    const int base = (32 * kb + 16 * hh) * ROWB;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][0]));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  auto k_read = [&](int j) -> bf16x8 { return kvo.k(Kp, j); };
+  auto v_read = [&](int j) -> bf16x8 { return kvo.v(Vp, j); };
   // S[kb][qh] (s has 4 accumulators, index 2*kb + qh)
   auto compute_s = [&](f32x16* s) {
 #pragma unroll

@@ -97,5 +97,47 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Per-lane operand reads of the forward's 64-row K and V tiles (row-major,
+// 16-byte pieces permuted by swz<D>), shared by its two- and one-wave
+// kernels. K operand of S^T = K Q^T: row 32 kb + l32, piece 2 cc + half.
+// V^T operand through the transpose read: lane (16-lane group g, slot
+// 4 j + q) addresses key row 32 kb + 16 hh + 8 t + 4 half + j, channels
+// 32 dg + 16 (g & 1) + 4 q .. +3, so it receives channel 32 dg + l32 of keys
+// 32 kb + 16 hh + 8 t + 4 half + 0..3: the P^T slot order.
+template <int D>
+struct KvOperands {
+  static constexpr int ROWB = D * 2;
+  int l32, half, fk;
+  int voff[D / 32][2];
+  __device__ __forceinline__ explicit KvOperands(int lane) {
+    l32 = lane & 31;
+    half = lane >> 5;
+    fk = swz<D>(l32 & 15);
+    const int g16 = (lane >> 4) & 1, sj = (lane & 15) >> 2, sq = lane & 3;
+#pragma unroll
+    for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 8 * t + 4 * half + sj;   // + 32 kb + 16 hh (a multiple of 16)
+        const int piece = 4 * dg + 2 * g16 + (sq >> 1);
+        voff[dg][t] = row * ROWB + ((piece ^ swz<D>(row & 15)) << 4) + ((sq & 1) << 3);
+      }
+  }
+  // K operand of S^T step j (k-step cc = j / 2, key half kb = j % 2)
+  __device__ __forceinline__ bf16x8 k(const lds_u8* Kp, int j) const {
+    const int cc = j >> 1, kb = j & 1;
+    const int off = (32 * kb + l32) * ROWB + (((2 * cc + half) ^ fk) << 4);
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(Kp + off);
+  }
+  // V^T operand of PV step j (key half kb, 16-key group hh, channel group dg)
+  __device__ __forceinline__ bf16x8 v(const lds_u8* Vp, int j) const {
+    const int kb = j / (2 * (D / 32)), hh = (j / (D / 32)) & 1, dg = j % (D / 32);
+    const int base = (32 * kb + 16 * hh) * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vp + base + voff[dg][1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
 }  // namespace
 }  // namespace bsa
