@@ -3,16 +3,18 @@
 // window union; Sparse VideoGen2 summary, Metodologia B for the
 // size-weighted centroid variant).
 //
-// One workgroup (4 waves, 8 for rows of 1025..2048 key blocks) owns R
-// consecutive rows of one head's reduced map.
+// One workgroup of 4 waves owns R consecutive rows of one head's reduced map;
+// rows of 1025..2048 key blocks at d = 128 go to a pipelined kernel in which
+// some waves score the next 16 rows while the others select the previous 16.
 //
 // Phase 1 -- scores. s[r][J] = scale * qbar_r . kbar_J (+ log n_J) for all
 // key blocks, on fp32 MFMA 16x16x4 (A = 16 pooled query rows, B = 16 pooled
 // key rows, the 4-wide k slot of the MFMA split over the four 16-lane
-// groups). Lane group g takes the 16-byte pieces 4s + g of a row, so one
-// load instruction reads 64 contiguous bytes of each of its 16 rows rather
-// than 16 bytes of 64 separate lines. The R x nkb fp32 score rows stay in
-// LDS; the reduced map never touches HBM.
+// groups), or in the pipelined kernel on bf16 MFMA over exact three-way
+// bf16 splits of both fp32 operands. Lane group g takes the 16-byte pieces
+// 4s + g of a row, so one load instruction reads 64 contiguous bytes of each
+// of its 16 rows rather than 16 bytes of 64 separate lines. The R x nkb fp32
+// score rows stay in LDS; the reduced map never touches HBM.
 //
 // Phase 2 -- selection, one wave per row (rows of up to 2048 key blocks are
 // held in registers, longer rows are streamed from LDS). p_J = exp(s_J - max)
@@ -32,19 +34,20 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace bsa {
 
-// Rows of 1025..2048 key blocks (the 118,800-token layer): 8 waves share
-// the 16 score rows, two per SIMD, so one wave's LDS atomics and scans wait
-// while the other issues (measured: mask stage 1.22 -> 0.99 ms at 1857 key
-// blocks; 16 waves, or the rows streamed from LDS instead of registers, were
-// slower).
-#ifndef BSA_SEL_W2048
-#define BSA_SEL_W2048 8
-#endif
-#ifndef BSA_SEL_E2048
-#define BSA_SEL_E2048 32
-#endif
+// Rows of 1025..2048 key blocks at d = 128 (the 118,800-token layer) take the
+// pipelined kernel below: 4 scoring waves and 8 selecting waves per
+// workgroup, each selecting wave holding two rows in registers (168 VGPRs at
+// three waves per SIMD). Measured at 1857 key blocks, mask stage (pool +
+// select) in the bench loop: 0.94 ms with one 8-wave workgroup per 16 rows
+// (scoring, then selecting), 0.86 pipelined with fp32 MFMA scores (those
+// hold the SIMD's VALU, so the two roles took turns), 0.73 with the scores
+// on bf16 MFMA over exact three-way splits.
+constexpr int kSelPW = 4, kSelSW = 8;
 
 namespace {
 constexpr int kIdxBits = 13;          // supports nkb <= 8192
@@ -124,23 +127,18 @@ __device__ __forceinline__ int first_lane(bool p) {
 // Selection of one row with its elements held in registers (E per lane,
 // element j = lane + 64 t): the same exact radix select as the LDS path
 // below, but every pass streams registers instead of re-reading and
-// re-converting the scores. Writes the kept ids in ascending order and
-// returns their count (lane-uniform).
+// re-converting the scores. On entry pb holds the bits of the row's scores
+// (-inf past nkb); it is overwritten. Writes the kept ids in ascending order
+// and returns their count (lane-uniform).
 template <int E, int COPIES>
-__device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float thr, int row,
+__device__ __forceinline__ int select_row_core(uint32_t (&pb)[E], int nkb, float thr, int row,
                                                const int32_t* ksz, const Window& win,
                                                unsigned long long* h, int32_t* out, int lane) {
   // per element: pb = bits of p (the key is pb << 13 | 8191 - j); its
   // fixed-point mass floor(p * 2^31) is recomputed where needed (mass_of)
-  uint32_t pb[E];
   float mx = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < E; ++t) {
-    const int j = lane + kWave * t;
-    const float sj = j < nkb ? sr[j] : -INFINITY;
-    pb[t] = __float_as_uint(sj);
-    mx = fmaxf(mx, sj);
-  }
+  for (int t = 0; t < E; ++t) mx = fmaxf(mx, __uint_as_float(pb[t]));
   mx = max_f32(mx);
   unsigned long long z = 0;
 #pragma unroll
@@ -172,6 +170,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
     // of them alive across passes (register pressure)
 #pragma unroll
     for (int t = 0; t < E; ++t) asm volatile("" : "+v"(pb[t]));
+    asm volatile("" : "+v"(lane));
     if (pass == 2) {
       // The cut lies among the keys that share the 16-bit prefix (bits 42..27). When there
       // are at most 64 of them, finish exactly with one candidate per lane:
@@ -302,6 +301,7 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   if (!done) kstar = prefix;
 
   int base = 0;
+  asm volatile("" : "+v"(lane));
   // key >= k*  <=>  pb > k*_hi, or pb == k*_hi and 8191 - j >= k*_lo
   const uint32_t ks_hi = (uint32_t)(kstar >> kIdxBits), ks_lo = (uint32_t)(kstar & ((1u << kIdxBits) - 1));
   const bool none = (kstar >> kIdxBits) > 0xffffffffull;   // k* past every key: keep nothing by the CDF
@@ -323,23 +323,59 @@ __device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float t
   return base;
 }
 
-template <int D, int R, int E, int W>
-__global__ __launch_bounds__(64 * W) void select_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
-    Sizes sz, float thr, float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
-    int kv_stride) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
-  unsigned long long* hist =
-      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [W][kHist]
+// The row's scores from LDS into registers, then the selection above.
+template <int E, int COPIES>
+__device__ __forceinline__ int select_row_regs(const float* sr, int nkb, float thr, int row,
+                                               const int32_t* ksz, const Window& win,
+                                               unsigned long long* h, int32_t* out, int lane) {
+  uint32_t pb[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int j = lane + kWave * t;
+    pb[t] = __float_as_uint(j < nkb ? sr[j] : -INFINITY);
+  }
+  return select_row_core<E, COPIES>(pb, nkb, thr, row, ksz, win, h, out, lane);
+}
 
+// Exact three-way split of eight fp32 values into bf16 planes, x = x1 + x2 +
+// x3: x1 keeps the top 8 significant bits of x (truncation), x2 the top 8 of
+// the remainder, and the last remainder has at most 8 significant bits, so
+// it is a bf16 exactly. Both subtractions are exact (same sign, same
+// exponent). Element e of each plane is x[e].
+__device__ __forceinline__ void split3_bf16(const float* x, bf16x8& p1, bf16x8& p2, bf16x8& p3) {
+  uint32_t w1[4], w2[4], w3[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a0 = __float_as_uint(x[2 * i]), a1 = __float_as_uint(x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(a0 & 0xffff0000u);
+    const float r1 = x[2 * i + 1] - __uint_as_float(a1 & 0xffff0000u);
+    const uint32_t b0 = __float_as_uint(r0), b1 = __float_as_uint(r1);
+    const float s0 = r0 - __uint_as_float(b0 & 0xffff0000u);
+    const float s1 = r1 - __uint_as_float(b1 & 0xffff0000u);
+    // high halves of two words -> one word (element 2i low, 2i+1 high)
+    w1[i] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    w2[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+    w3[i] = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), 0x07060302u);
+  }
+  __builtin_memcpy(&p1, w1, 16);
+  __builtin_memcpy(&p2, w2, 16);
+  __builtin_memcpy(&p3, w3, 16);
+}
+
+// Phase 1: the scores of rows row0..row0+R-1 of head bh against every key
+// block, into sc ([R][nkb_pad]), by NW waves of which this is number wv.
+// Products on fp32 MFMA 16x16x4, or with SPLIT on bf16 MFMA 16x16x32 over
+// the three-way splits of both operands: every cross product but x3 y3
+// (below 2^-28 of |x||y|), each exact in fp32 and summed in fp32. A lane's
+// 32 values of a row (the pieces 4s + g) form chunk c from a[8c..8c+7], on
+// both sides, so the d order matches. The bf16 products run beside other
+// waves' VALU work; the fp32 ones hold the SIMD's VALU while they run.
+template <int D, int R, int NW, bool SPLIT = false>
+__device__ __forceinline__ void score_rows(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                           int bh, int row0, int nqb, int nkb, int nkb_pad, const Sizes& sz,
+                                           float scale, float* sc, int wv, int lane) {
   constexpr int KQ = D / 4;
-  const int bh = blockIdx.y;
-  const int row0 = blockIdx.x * R;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, i16 = lane & 15;
-
-  // ---------------- phase 1: score rows into LDS
   float a[KQ];
   {
     const int row = row0 + i16;
@@ -350,6 +386,12 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
       const float4 v = ok ? src[4 * s + g] : make_float4(0.f, 0.f, 0.f, 0.f);
       a[4 * s + 0] = v.x; a[4 * s + 1] = v.y; a[4 * s + 2] = v.z; a[4 * s + 3] = v.w;
     }
+  }
+  constexpr int NC = D / 32;
+  bf16x8 qa[SPLIT ? 3 : 1][SPLIT ? NC : 1];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) split3_bf16(&a[8 * c], qa[0][c], qa[1][c], qa[2][c]);
   }
   const float* kbh = kbar + (size_t)bh * nkb * D;
   const int ntiles = (nkb + 15) >> 4;
@@ -371,8 +413,21 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
     f32x4 acc4[4];
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) acc4[c4] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int s = 0; s < KQ; ++s) acc4[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc4[s & 3], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 kb[3];
+        split3_bf16(&b[8 * c], kb[0], kb[1], kb[2]);
+        // (q plane, k plane): every pair but (3, 3)
+        constexpr int PQ[8] = {0, 0, 1, 0, 1, 2, 1, 2}, PK[8] = {0, 1, 0, 2, 1, 0, 2, 1};
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          acc4[p & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[PQ[p]][c], kb[PK[p]], acc4[p & 3], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KQ; ++s) acc4[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc4[s & 3], 0, 0, 0);
+    }
     const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     if (key < nkb) {
       float bias = 0.f;
@@ -393,16 +448,34 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
   // issued before the MFMAs of the current one (the scheduling barrier
   // keeps them there), so they land while the products run.
   float b0[KQ], b1[KQ];
-  if (wave < ntiles) load_b(wave, b0);
-  for (int t = wave; t < ntiles; t += 2 * W) {
-    load_b(min(t + W, ntiles - 1), b1);
+  if (wv < ntiles) load_b(wv, b0);
+  for (int t = wv; t < ntiles; t += 2 * NW) {
+    load_b(min(t + NW, ntiles - 1), b1);
     __builtin_amdgcn_sched_barrier(0);
     score_tile(t, b0);
-    if (t + W >= ntiles) break;
-    load_b(min(t + 2 * W, ntiles - 1), b0);
+    if (t + NW >= ntiles) break;
+    load_b(min(t + 2 * NW, ntiles - 1), b0);
     __builtin_amdgcn_sched_barrier(0);
-    score_tile(t + W, b1);
+    score_tile(t + NW, b1);
   }
+}
+
+template <int D, int R, int E, int W>
+__global__ __launch_bounds__(64 * W) void select_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad,
+    Sizes sz, float thr, float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+    int kv_stride) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
+  unsigned long long* hist =
+      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [W][kHist]
+
+  const int bh = blockIdx.y;
+  const int row0 = blockIdx.x * R;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // ---------------- phase 1: score rows into LDS
+  score_rows<D, R, W>(qbar, kbar, bh, row0, nqb, nkb, nkb_pad, sz, scale, sc, wave, lane);
   __syncthreads();
 
   // ---------------- phase 2: per-row CDF selection
@@ -506,6 +579,90 @@ __global__ __launch_bounds__(64 * W) void select_kernel(
   }
 }
 
+// Rows of 1025..2048 key blocks, pipelined over groups of 16 rows. Each
+// workgroup takes a contiguous range of (head, 16-row group) pairs; PW
+// scoring waves write the scores of group k into LDS while SW selecting
+// waves select the rows of group k - 1, each holding 16 / SW rows in
+// registers, so the fp32 MFMA and key-stream work of one group runs beside
+// the VALU and LDS-atomic work of the previous one (with one group per
+// workgroup the two phases take turns on the CU). Two workgroup barriers per
+// group: after the first, the scores of group k are complete and the
+// selecting waves copy their rows into registers; after the second the
+// score rows are free for group k + 1. Both roles pass the same number of
+// barriers. The ranges are laid out XCD by XCD (workgroup i runs on XCD
+// i mod 8), so the groups running together on one XCD share a few heads'
+// pooled keys in its L2.
+template <int D, int E, int PW, int SW>
+__global__ __launch_bounds__(64 * (PW + SW)) void select_pipe_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nkb_pad, int BH,
+    Sizes sz, float thr, float scale, Window win, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_index,
+    int kv_stride) {
+  constexpr int R = 16, RPW = R / SW;
+  static_assert(R % SW == 0 && RPW <= 4, "each selecting wave holds the same number of rows, at most 4");
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sc = reinterpret_cast<float*>(smem);                                  // [R][nkb_pad]
+  unsigned long long* hist =
+      reinterpret_cast<unsigned long long*>(smem + (size_t)R * nkb_pad * sizeof(float));  // [SW][512]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ngr = (nqb + R - 1) / R;
+  const long long total = (long long)BH * ngr;
+  const int nwg = gridDim.x, i = blockIdx.x;
+  const int L = (nwg & 7) == 0 ? (i & 7) * (nwg >> 3) + (i >> 3) : i;
+  const int g0 = (int)(L * total / nwg);
+  const int ng = (int)((L + 1) * total / nwg) - g0;
+  if (wave < PW) {
+    for (int k = 0; k <= ng; ++k) {
+      if (k < ng) {
+        const int g = g0 + k;
+        score_rows<D, R, PW, true>(qbar, kbar, g / ngr, (g % ngr) * R, nqb, nkb, nkb_pad, sz, scale, sc, wave, lane);
+      }
+      __syncthreads();
+      __syncthreads();
+    }
+  } else {
+    const int sw = wave - PW;
+    unsigned long long* h = hist + sw * 512;
+    uint32_t rows[RPW][E];
+    // One call site per held row (constant indices keep the rows in
+    // registers). The lane index passes through an empty asm at each call so
+    // that the per-lane values derived from it (element ids, bounds masks,
+    // addresses) are formed where they are used, not hoisted out of the
+    // group loop, where they would not fit beside the held rows.
+    auto select_one = [&](uint32_t (&pb)[E], int bh, int row) __attribute__((always_inline)) {
+      if (row >= nqb) return;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const size_t orow = (size_t)bh * nqb + row;
+      int n = 0;
+      if (!sz.q_empty(bh, nqb, row))
+        n = select_row_core<E, 8>(pb, nkb, thr, row, sz.krow(bh, nkb), win, h, kv_index + orow * kv_stride, ln);
+      if (ln == 0) kv_count[orow] = n;
+    };
+    for (int k = 0; k <= ng; ++k) {
+      if (k > 0) {
+        const int g = g0 + k - 1, bh = g / ngr, row0 = (g % ngr) * R + sw;
+        select_one(rows[0], bh, row0);
+        if constexpr (RPW > 1) select_one(rows[1], bh, row0 + SW);
+        if constexpr (RPW > 2) select_one(rows[2], bh, row0 + 2 * SW);
+        if constexpr (RPW > 3) select_one(rows[3], bh, row0 + 3 * SW);
+      }
+      __syncthreads();
+      if (k < ng) {
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+          const float* sr = sc + (sw + SW * q) * nkb_pad;
+#pragma unroll
+          for (int t = 0; t < E; ++t) {
+            const int j = lane + kWave * t;
+            rows[q][t] = __float_as_uint(j < nkb ? sr[j] : -INFINITY);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 template <int D, int R, int E, int W = 4>
 static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
                                   const Sizes& sz, float thr, float scale, const Window& win, int32_t* kv_count,
@@ -522,6 +679,38 @@ static hipError_t launch_select_t(const float* qbar, const float* kbar, int BH, 
   return hipGetLastError();
 }
 
+// CU count of the current device, cached per device.
+static int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int D, int E, int PW, int SW>
+static hipError_t launch_select_pipe(const float* qbar, const float* kbar, int BH, int nqb, int nkb,
+                                     const Sizes& sz, float thr, float scale, const Window& win,
+                                     int32_t* kv_count, int32_t* kv_index, int kv_stride, hipStream_t s) {
+  const int nkb_pad = (nkb + 3) & ~3;
+  const size_t lds = (size_t)16 * nkb_pad * sizeof(float) + (size_t)SW * 512 * sizeof(unsigned long long);
+  auto kern = select_pipe_kernel<D, E, PW, SW>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  // the score rows take most of the LDS: one workgroup per CU, each over a
+  // range of whole groups
+  const long long groups = (long long)BH * ((nqb + 15) / 16);
+  const int nwg = (int)std::min<long long>(groups, device_cus());
+  kern<<<nwg, 64 * (PW + SW), lds, s>>>(qbar, kbar, nqb, nkb, nkb_pad, BH, sz, thr, scale, win,
+                                        kv_count, kv_index, kv_stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, int nkb, int d,
                          const Sizes& sz, float thr, float scale,
                          const Window& win, int32_t* kv_count, int32_t* kv_index, int kv_stride,
@@ -529,13 +718,18 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
   if (BH == 0 || nqb == 0) return hipSuccess;
 #define BSA_SEL(DD, RR, EE) \
   launch_select_t<DD, RR, EE>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win, kv_count, kv_index, kv_stride, s)
-#define BSA_SELW(DD, RR, EE, WW) \
-  launch_select_t<DD, RR, EE, WW>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win, kv_count, kv_index, kv_stride, s)
   // rows of up to 2048 key blocks are selected from registers (E per lane)
   if (d == 128) {
     if (nkb <= 512) return BSA_SEL(128, 16, 8);
     if (nkb <= 1024) return BSA_SEL(128, 16, 16);
-    if (nkb <= 2048) return BSA_SELW(128, 16, BSA_SEL_E2048, BSA_SEL_W2048);
+    // E = 30 registers per row up to 1920 key blocks: no spills at the
+    // 168-register bound of three waves per SIMD
+    if (nkb <= 1920)
+      return launch_select_pipe<128, 30, kSelPW, kSelSW>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win,
+                                                         kv_count, kv_index, kv_stride, s);
+    if (nkb <= 2048)
+      return launch_select_pipe<128, 32, kSelPW, kSelSW>(qbar, kbar, BH, nqb, nkb, sz, thr, scale, win,
+                                                         kv_count, kv_index, kv_stride, s);
     if (nkb <= 4096) return BSA_SEL(128, 8, 0);
     return BSA_SEL(128, 4, 0);
   }
@@ -544,7 +738,6 @@ hipError_t launch_select(const float* qbar, const float* kbar, int BH, int nqb, 
   if (nkb <= 2048) return BSA_SEL(64, 16, 32);
   if (nkb <= 4096) return BSA_SEL(64, 8, 0);
   return BSA_SEL(64, 4, 0);
-#undef BSA_SELW
 #undef BSA_SEL
 }
 

@@ -131,8 +131,10 @@ int bsa_pool_blocks(const void* x, int B, int H, int N, int d, int n_valid,
  * "Attenzione Ridotta" and "CDF Thresholding"; section 3 window union;
  * Sparse VideoGen2 summary, Metodologia B, for the size-weighted variant).
  *
- * For every row (b,h,I): s_J = scale * qbar_I . kbar_J in fp32 (+ log n_J
- * when k_sizes is given), p_J = exp(s_J - max s), and the kept set is
+ * For every row (b,h,I): s_J = scale * qbar_I . kbar_J with fp32 sums (+ log
+ * n_J when k_sizes is given; rows of 1025..2048 key blocks at d = 128 form
+ * the products from exact three-way bf16 splits of the fp32 operands, every
+ * cross term but the smallest), p_J = exp(s_J - max s), and the kept set is
  * computed exactly on the fp32 values p_J: order the blocks lightest first
  * (equal p: higher J lighter), drop J exactly when the inclusive cumulative
  * mass up to J is below thr times the row total. Masses are summed in
