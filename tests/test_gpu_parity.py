@@ -254,11 +254,12 @@ def test_mask_long_rows(gpu_lib, nkb):
 @pytest.mark.parametrize("nkb,d,H,nv_cut,win", [(1025, 128, 3, 0, None), (1500, 64, 2, 37, None),
                                                    (2048, 128, 2, 0, None), (1200, 128, 2, 20, (3, 20, 20, 1, 2, 2))])
 def test_mask_rows_1025_to_2048(gpu_lib, nkb, d, H, nv_cut, win):
-    """Rows of 1025..2048 key blocks (the 720p layer's class; 8 waves share
-    16 score rows held in registers): both head dims, several heads, a
-    ragged last block, row counts that are not a multiple of 16, the
-    2048-block edge where the score rows and histograms fill the LDS, and
-    the window union."""
+    """Rows of 1025..2048 key blocks (the 720p layer's class; at d = 128 the
+    pipelined kernel with split bf16 scores): both head dims, several heads,
+    a ragged last block, row counts that are not a multiple of 16, the
+    2048-block edge where the score rows and histograms fill the LDS, the
+    window union, and the fused call against pooling and selecting in two
+    calls."""
     rng = np.random.default_rng(nkb + d)
     nv = nkb * 64 - nv_cut
     N = nkb * 64
@@ -270,6 +271,14 @@ def test_mask_rows_1025_to_2048(gpu_lib, nkb, d, H, nv_cut, win):
     say(f"mask rows nkb={nkb} d={d} H={H} n_valid={nv} window={win}")
     cnt, idx = gpu_lib.build_block_mask(q.cuda(), k.cuda(), 0.2, window=win, n_valid=nv)
     cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    # pooling and selecting in two calls gives the same lists as the fused call
+    qbar = gpu_lib.pool_blocks(q.cuda(), n_valid=nv)
+    kbar = gpu_lib.pool_blocks(k.cuda(), n_valid=nv)
+    cnt2, idx2 = gpu_lib.select_blocks(qbar, kbar, 0.2, window=win)
+    cnt2, idx2 = cnt2.cpu().numpy(), idx2.cpu().numpy()
+    assert np.array_equal(cnt2, cnt)
+    for h in range(H):
+        assert np.array_equal(keep_from_lists(cnt2[0, h], idx2[0, h], nkb), keep_from_lists(cnt[0, h], idx[0, h], nkb))
     st, ln = ol.raster_blocks(nv)
     assert len(st) == nkb
     W = None
