@@ -110,7 +110,8 @@ __device__ __forceinline__ void attn_tile_1w(const AttnArgs& a, int bh, int I, i
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   const size_t qrow = (size_t)bh * a.nqb + I;
-  const int cnt = ((const cint*)a.kv_count)[qrow];
+  // counts outside [0, kv_stride] (a caller's contract) stay inside the row
+  const int cnt = min(max(((const cint*)a.kv_count)[qrow], 0), a.kv_stride);
   const int32_t* list = a.kv_index + qrow * a.kv_stride;
   const cint* slist = (const cint*)list;
 
