@@ -301,6 +301,44 @@ def test_mask_rows_1025_to_2048(gpu_lib, nkb, d, H, nv_cut, win):
     assert (cnt >= 1).all()
 
 
+
+@pytest.mark.parametrize("nkb,d", [(3000, 128), (8192, 64), (8192, 128)])
+def test_mask_max_key_blocks(gpu_lib, nkb, d):
+    """Rows past 2048 key blocks, where the scores are streamed from LDS:
+    2049..4096 at d = 128 (eight rows per workgroup) and the supported
+    maximum of 8192 key blocks (four rows per workgroup; the block index of
+    the radix key reaches its last 13-bit value), with a ragged last block.
+    Inputs are smooth within each 64-token block (a per-block latent plus
+    token noise), which keeps ~8-24 % of the blocks at thr = 0.2. Sampled
+    rows against the reference's block probabilities (pooling, scores and
+    row softmax for those rows only: rows are independent)."""
+    rng = np.random.default_rng(nkb + d)
+    N = nkb * 64
+    nv = N - 29
+    zb = rng.normal(size=(nkb, 8)).astype(np.float32)
+    W = rng.normal(size=(8, d)).astype(np.float32) * 0.25
+    qb_ = np.repeat(zb @ W, 64, axis=0)
+    kb_ = np.repeat((zb + 0.5 * rng.normal(size=(nkb, 8)).astype(np.float32)) @ W, 64, axis=0)
+    q = torch.from_numpy((qb_ + 0.3 * rng.normal(size=(N, d)).astype(np.float32))[None, None]).to(torch.bfloat16)
+    k = torch.from_numpy((kb_ + 0.3 * rng.normal(size=(N, d)).astype(np.float32))[None, None]).to(torch.bfloat16)
+    del qb_, kb_
+    q[:, :, nv:] = 0
+    k[:, :, nv:] = 0
+    say(f"mask max key blocks nkb={nkb} d={d} n_valid={nv}")
+    cnt, idx = gpu_lib.build_block_mask(q.cuda(), k.cuda(), 0.2, n_valid=nv)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    st, ln = ol.raster_blocks(nv)
+    assert len(st) == nkb and ln[-1] == 64 - 29
+    rows = np.unique(np.concatenate([np.arange(0, nkb, 61), np.arange(nkb - 5, nkb)]))
+    keep = keep_from_lists(cnt[0, 0][rows], idx[0, 0][rows], nkb)
+    qbar = om.pool(_np(q[0, 0]), st, ln)
+    kbar = om.pool(_np(k[0, 0]), st, ln)
+    P = om.softmax_rows(om.reduced_scores(qbar[rows], kbar, 1.0 / np.sqrt(d)))
+    bad = mask_mismatches(P, 0.2, keep)
+    say(f"  kept {keep.sum()} of {keep.size} over {len(rows)} rows, mismatches {bad}")
+    assert bad == 0
+    assert (cnt >= 1).all() and (cnt <= nkb).all()
+
 # ------------------------------------------------------------------- attention
 
 def _attn_case(bsa, w, q, k, v, heads, nsample, seed=0, thr=None):
@@ -496,6 +534,62 @@ def test_attn_long_rows(gpu_lib, path):
     for t in (qd, kd, vd):
         t[:, :, nv:] = float("nan")
     o3 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv, workspace=ws)
+    assert torch.equal(o1, o3)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attn_max_key_blocks(gpu_lib, d):
+    """The supported maximum of 8192 query and key blocks. At d = 128 the
+    split plan's bucket counts do not fit its LDS there, and at either head
+    dim the longest-first order table is one word past its 64 KiB, so the
+    rows run whole on the two-wave kernel in block order, with the pad rows
+    zeroed by a launch of their own. Random lists with a dense row (8192
+    chunks), a single-block row, a row keeping nothing and the ragged last
+    block; sampled query blocks against the reference, then a repeat run
+    and poisoned padding must give the same bits."""
+    bsa = gpu_lib
+    nkb = 8192
+    N = nkb * 64
+    nv = N - 37
+    rng = np.random.default_rng(8192 + d)
+    say(f"attention max key blocks d={d} N={N} n_valid={nv}")
+    x = [rng.normal(size=(N, d)).astype(np.float32) for _ in range(3)]
+    for t in x:
+        t[nv:] = 0
+    q, k, v = (torch.from_numpy(t[None, None] * (2.0 if i < 2 else 1.0)).to(torch.bfloat16)
+               for i, t in enumerate(x))
+    del x
+    st, ln = ol.raster_blocks(nv)
+    assert len(st) == nkb
+    keep = rng.random((nkb, nkb), dtype=np.float32) < 0.01
+    keep[:, nkb - 1] |= rng.random(nkb, dtype=np.float32) < 0.2     # ragged last key block
+    keep[:, 0] |= ~keep.any(1)
+    keep[5, :] = True                                                # a dense row
+    keep[9, :] = False
+    keep[9, 4097] = True                                             # a single-block row
+    keep[11, :] = False                                              # a row keeping nothing
+    keep[nkb - 1, :] = False
+    keep[nkb - 1, [0, 383, 384, 4095, 4096, nkb - 1]] = True          # ragged last query block
+    cnt = keep.sum(1).astype(np.int32)
+    idx = np.full((nkb, nkb), -1, np.int32)
+    for i in range(nkb):
+        ids = np.flatnonzero(keep[i])
+        idx[i, :len(ids)] = ids
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cd, id_ = torch.from_numpy(cnt[None, None]).cuda(), torch.from_numpy(idx[None, None]).cuda()
+    del idx
+    o1 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    o = _np(o1[0, 0])
+    blocks = sorted({0, 5, 9, 11, nkb - 1} | set(rng.choice(nkb, 8, replace=False).tolist()))
+    ref = oa.masked_attention(_np(q[0, 0]), _np(k[0, 0]), _np(v[0, 0]), st, ln, st, ln, keep, blocks=blocks)
+    _check_out(o, ref, _rows_of(st, ln, blocks), f"{len(blocks)} query blocks")
+    assert (o[st[11]:st[11] + 64] == 0).all()                       # no kept block: zero rows
+    assert (o[nv:] == 0).all()
+    o2 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
+    assert torch.equal(o1, o2)
+    for t in (qd, kd, vd):
+        t[:, :, nv:] = float("nan")
+    o3 = bsa.block_sparse_attn_fwd(qd, kd, vd, cd, id_, n_valid=nv)
     assert torch.equal(o1, o3)
 
 
