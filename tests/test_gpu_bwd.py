@@ -307,3 +307,59 @@ def test_bwd_fractal_patches_wan480_sampled(gpu_lib):
         krows = np.arange(st[J], st[J] + ln[J])
         _check_grad(dk[h], rk, krows, f"head {h} dk (patch {J} of {ln[J]} tokens, {len(users)} query patches)")
         _check_grad(dv[h], rv, krows, f"head {h} dv (patch {J})")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_max_key_blocks(gpu_lib, d):
+    # the supported maximum of 8192 query and key blocks: neither
+    # longest-first order (query tiles by kept count, key tiles by user
+    # count) fits its 64 KiB of LDS, so both tile kinds run in block order;
+    # the transposed lists span 256 bit-words per key block. Random 1 %
+    # lists with a dense row, a row keeping nothing, a key block kept by
+    # every 16th query block and the ragged last block; dQ of sampled query
+    # blocks and dK, dV of sampled key blocks (every query block that keeps
+    # them, whole) against the reference, then a repeat run
+    bsa = gpu_lib
+    nkb = 8192
+    N = nkb * 64
+    nv = N - 37
+    rng = np.random.default_rng(9000 + d)
+    say(f"backward, max key blocks d={d} N={N} n_valid={nv}")
+    x = [rng.normal(size=(N, d)).astype(np.float32) for _ in range(4)]
+    for t in x:
+        t[nv:] = 0
+    q, k, v, do = (torch.from_numpy(t[None, None] * (1.5 if i < 2 else 1.0)).to(torch.bfloat16)
+                   for i, t in enumerate(x))
+    del x
+    st, ln = ol.raster_blocks(nv)
+    assert len(st) == nkb
+    keep = rng.random((nkb, nkb), dtype=np.float32) < 0.01
+    keep[:, 0] |= ~keep.any(1)
+    keep[5, :] = True                                  # a dense row
+    keep[11, :] = False                                # a row keeping nothing
+    keep[::16, 777] = True                             # a key block 512 query blocks keep
+    keep[11, 777] = False
+    cnt, idx = _lists(keep[None])
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    cd, id_ = torch.from_numpy(cnt[None]).cuda(), torch.from_numpy(idx[None]).cuda()
+    del idx
+    o, lse = bsa.block_sparse_attn_fwd_lse(qd, kd, vd, cd, id_, n_valid=nv)
+    g1 = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv)
+    torch.cuda.synchronize()
+    g2 = bsa.block_sparse_attn_bwd(qd, kd, vd, o, gd, lse, cd, id_, n_valid=nv)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))            # deterministic
+    dq, dk, dv = (_np(t[0, 0]) for t in g1)
+    del g1, g2
+    assert (dq[nv:] == 0).all() and (dk[nv:] == 0).all() and (dv[nv:] == 0).all()
+    assert (dq[st[11]:st[11] + 64] == 0).all()
+    args = [_np(t[0, 0]) for t in (q, k, v, do)]
+    qi = sorted({5, 11, nkb - 1} | set(rng.choice(nkb, 4, replace=False).tolist()))
+    rq, _, _ = oa.masked_attention_bwd(*args, st[qi], ln[qi], st, ln, keep[qi])
+    rows = np.concatenate([np.arange(st[i], st[i] + ln[i]) for i in qi])
+    _check_grad(dq, rq, rows, f"dq (query blocks {qi})")
+    for J in (777, nkb - 1, int(rng.integers(1, nkb - 1))):
+        users = np.nonzero(keep[:, J])[0]
+        _, rk, rv = oa.masked_attention_bwd(*args, st[users], ln[users], st, ln, keep[users])
+        krows = np.arange(st[J], st[J] + ln[J])
+        _check_grad(dk, rk, krows, f"dk (key block {J}, {len(users)} query blocks)")
+        _check_grad(dv, rv, krows, f"dv (key block {J})")
