@@ -255,11 +255,15 @@ def test_kmeans_seeding_rule(gpu_lib, which):
 
 
 @pytest.mark.parametrize("d,C,n,N,H", [(64, 5, 650, 704, 2), (64, 40, 650, 704, 2), (128, 100, 1000, 1024, 1),
-                                       (128, 1, 300, 320, 1), (64, 33, 2100, 2112, 3), (128, 37, 64, 64, 1)])
+                                       (128, 1, 300, 320, 1), (64, 33, 2100, 2112, 3), (128, 37, 64, 64, 1),
+                                       (64, 1024, 140000, 140032, 1)])
 def test_kmeans_small_shapes(gpu_lib, d, C, n, N, H):
     """Head dims 64 and 128, cluster counts off the 32-centroid chunk of the
-    assignment kernel, ragged token tails and a single cluster: the seeding
-    rule, then four Lloyd rounds checked against the third's centroids."""
+    assignment kernel, ragged token tails and a single cluster, and the
+    supported maximum of 1024 clusters over 547 chunks of 256 tokens (the
+    seeding draw holds 512 chunk sums in registers and reads the rest):
+    the seeding rule, then four Lloyd rounds checked against the third's
+    centroids."""
     bsa = gpu_lib
     g = torch.Generator().manual_seed(1000 + d + C + n)
     centres = torch.randn((H, 8, d), generator=g) * 3.0
