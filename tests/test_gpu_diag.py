@@ -123,3 +123,35 @@ def test_tile_stats_wan480_full_layer_sampled(gpu_lib):
             np.testing.assert_allclose(grec[h, I], rrec[0], rtol=0, atol=1e-6)
             np.testing.assert_allclose(gmass[h, I], rmass[0], rtol=1e-5, atol=1e-7)
             say(f"  head {h} row {I}: oracle recall {grec[h, I]:.3f} mass recall {gmass[h, I]:.3f}")
+
+
+def test_mask_recall_max_key_blocks(gpu_lib):
+    """The recall at the supported maximum of 8192 key blocks (the rows'
+    maxima take 128 KiB of LDS per workgroup), on given tile maps: maxima
+    with many exact ties (1000 distinct values, so the lower index decides),
+    rows keeping nothing, one block, every block and random sets."""
+    bsa = gpu_lib
+    nq, nk = 40, 8192
+    rng = np.random.default_rng(8192)
+    tmax = (np.round(rng.random((nq, nk)) * 1000) / 1000).astype(np.float32)
+    tsum = (rng.random((nq, nk)) * tmax).astype(np.float32)
+    keep = rng.random((nq, nk)) < rng.choice([0.001, 0.01, 0.2, 0.5], size=(nq, 1))
+    keep[0] = False
+    keep[1] = True
+    keep[2] = False
+    keep[2, nk - 1] = True
+    tsum[3] = 0.0                                    # a row with no attention mass
+    cnt = keep.sum(1).astype(np.int32)
+    idx = np.full((nq, nk), -1, np.int32)
+    for i in range(nq):
+        ids = np.flatnonzero(keep[i])
+        idx[i, :len(ids)] = ids
+    dev = lambda a: torch.from_numpy(a[None, None]).cuda()
+    say(f"mask recall nqb={nq} nkb={nk}")
+    rec, mass = bsa.mask_recall(dev(tmax), dev(tsum), dev(cnt), dev(idx))
+    rec, mass = _np(rec)[0, 0], _np(mass)[0, 0]
+    rrec, rmass = od.mask_recall(keep, tmax.astype(np.float64), tsum.astype(np.float64))
+    say(f"  oracle recall {rrec.mean():.4f}, mass recall {rmass.mean():.4f}")
+    np.testing.assert_allclose(rec, rrec, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(mass, rmass, rtol=1e-5, atol=1e-7)
+    assert rec[0] == 0 and rec[1] == 1 and mass[1] == pytest.approx(1.0, abs=1e-6) and mass[3] == 0
