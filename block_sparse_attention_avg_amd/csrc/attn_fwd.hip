@@ -1055,11 +1055,13 @@ bool launch_qorder(const int32_t* counts, int BH, int n, int cap, int32_t* order
 constexpr int kOneWaveKeyBlocks = 1024;
 
 // Split over key segments: rows over at least kSplitMinKeyBlocks uniform key
-// blocks at d = 128, segments of kSplitSegBlocks key blocks (8 MiB of K and V,
-// twice an XCD's L2: at the 720p layer a concurrently running XCD still finds
-// most blocks in L2).
+// blocks at d = 128 are cut into S = ceil(nkb / kSplitSegBlocks) equal key
+// segments (at the 720p layer 4 segments of 465 blocks, 14.5 MiB of K and V
+// each: the tiles running together on an XCD read one segment, and ~2/3 of
+// their requests hit its L2). Fewer, longer segments lose L2 hits; more,
+// shorter ones add items and partial results.
 constexpr int kSplitMinKeyBlocks = 1024;
-constexpr int kSplitSegBlocks = 384;
+constexpr int kSplitSegBlocks = 512;
 
 namespace {
 struct SplitLayout {
